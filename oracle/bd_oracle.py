@@ -1,0 +1,332 @@
+"""Float64 CPU oracle for block-diffusion attention over a KV cache.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py``
+import this module.  The HIP library never calls it and shares no code
+with it.
+
+Every function is the plain definition written out in NumPy float64, one
+(row, KV head) at a time, with no blocking, fusion or reordering beyond
+what the definition states.  Inputs given in bf16 or fp32 convert to f64
+exactly.  Sources (the pages the method is described on):
+
+* HERALD: High-Throughput Block Diffusion LLM Serving via CPU-GPU
+  Cooperative KV Cache Retrieval ("HERALD" below).
+* FlowBlock: Wavefront-Parallel Decoding for Self-Correcting Diffusion
+  Language Models, blog review ("FlowBlock review" below).  The review
+  numbers its equations (1)-(7); the paper's own numbers are one lower
+  from (3) on.  Both are given.
+
+Readings taken where the pages leave a step open (each is repeated in the
+design notes):
+
+* softmax scale ``sm_scale`` is an explicit argument (1/sqrt(d) in every
+  workload); the same value is used for selection and attention.
+* GQA head map: query head ``hq`` reads KV head ``hq // G``.
+* the representative query is either the mean of the block's queries or
+  one given query row; ``center_row`` implements HERALD Eq. (2).
+* selection scans prefix positions ``s < S_b`` only; top-k ties go to the
+  lower position and the kept positions are returned in ascending order.
+
+Parity pins: every function here is pinned by ``tests/test_oracle_*.py``
+against closed forms, brute force, a library routine (torch SDPA, scipy)
+or the worked example printed on the FlowBlock review.  No function is
+unpinned.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "eq6_mask",
+    "window_visible",
+    "block_attention",
+    "cache_attention_eq6",
+    "rep_query",
+    "center_row",
+    "selection_scores",
+    "topk_select",
+    "gather",
+    "kv_scatter",
+]
+
+
+def _f64(x):
+    """Exact conversion of a NumPy or torch (CPU) array to float64."""
+    if hasattr(x, "detach"):
+        x = x.detach().cpu().double().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _i64(x):
+    if hasattr(x, "detach"):
+        x = x.detach().cpu().numpy()
+    return np.asarray(x, dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------
+# Mask
+# ---------------------------------------------------------------------------
+
+def eq6_mask(C: int, q: int, bl: int, o) -> np.ndarray:
+    """Per-row block-diagonal mask over a cache of capacity ``C``.
+
+    FlowBlock review, Eq. (6) (paper Eq. 5): query ``i`` of row ``b`` sees
+    key ``j`` when ``j < o_b`` (the row's own frozen prefix) or when
+    ``t <= j < t + (s+1)*bl`` with ``t = C - q`` the shared physical tail
+    where the window's present KV lives and ``s = floor(i / bl)`` the
+    query's window slot.
+
+    Returns a bool array ``[B, q, C]``.
+    """
+    o = _i64(o)
+    t = C - q
+    i = np.arange(q)[:, None]
+    j = np.arange(C)[None, :]
+    s = i // bl
+    own_tail = (j >= t) & (j < t + (s + 1) * bl)          # [q, C]
+    own_prefix = j[None, :, :] < o[:, None, None]          # [B, 1, C]
+    return own_prefix | own_tail[None, :, :]
+
+
+def window_visible(q: int, bl: int) -> np.ndarray:
+    """Window part of Eq. (6) in window coordinates ``w = j - t``.
+
+    Query ``i`` sees window key ``w`` when ``w < (floor(i/bl) + 1) * bl``:
+    bidirectional inside its own block and causal over earlier window
+    blocks (FlowBlock review, W-shaped block-causal mask).  ``[q, q]`` bool.
+    """
+    i = np.arange(q)[:, None]
+    w = np.arange(q)[None, :]
+    return w < (i // bl + 1) * bl
+
+
+# ---------------------------------------------------------------------------
+# Attention
+# ---------------------------------------------------------------------------
+
+def _softmax_attend(logits: np.ndarray, vals: np.ndarray):
+    """Softmax over the last axis of ``logits`` then weighted sum of ``vals``.
+
+    ``logits`` holds -inf where a key is not visible.  Returns (out, lse)
+    with ``lse = m + log(sum exp(logits - m))`` (FlashAttention statistics,
+    HERALD Sec. IV-B4).
+    """
+    m = logits.max(axis=-1, keepdims=True)
+    p = np.exp(logits - m)
+    z = p.sum(axis=-1, keepdims=True)
+    out = (p @ vals) / z
+    lse = (m + np.log(z))[..., 0]
+    return out, lse
+
+
+def block_attention(Q, PK, PV, p_len, WK, WV, bl: int, sm_scale: float,
+                    rows=None):
+    """Block-diffusion attention in prefix/window form.
+
+    For row ``b``, query ``i`` and query head ``hq`` (KV head ``h = hq//G``)
+    the visible keys are every prefix entry ``PK[b, 0:p_len[b], h]`` and the
+    window entries ``WK[b, w, h]`` with ``w < (floor(i/bl)+1)*bl``.  With
+    ``PK`` the cache and ``p_len = o`` this is FlowBlock review Eq. (6)
+    (the window is the cache tail ``[t, C)``); with ``PK`` a compact pool of
+    selected entries and ``p_len = k_b`` it is HERALD's denoising attention
+    over the critical KV cache (Sec. III-C, IV-B1), where the block attends
+    bidirectionally in-block and to the cached prefix (Sec. II-A).
+
+    Q: [B, q, Hq, d]; PK, PV: [B, P, Hkv, d]; WK, WV: [B, q, Hkv, d].
+    Returns ``O [B, q, Hq, d]`` and ``LSE [B, Hq, q]`` in float64; rows not
+    in ``rows`` are NaN.
+    """
+    Q, PK, PV, WK, WV = (_f64(x) for x in (Q, PK, PV, WK, WV))
+    p_len = _i64(p_len)
+    B, q, Hq, d = Q.shape
+    Hkv = PK.shape[2]
+    G = Hq // Hkv
+    assert G * Hkv == Hq
+    rows = range(B) if rows is None else [int(r) for r in _i64(rows)]
+    wvis = window_visible(q, bl)                             # [q, q]
+    O = np.full((B, q, Hq, d), np.nan)
+    LSE = np.full((B, Hq, q), np.nan)
+    for b in rows:
+        P = int(p_len[b])
+        for h in range(Hkv):
+            keys = np.concatenate([PK[b, :P, h], WK[b, :, h]], axis=0)
+            vals = np.concatenate([PV[b, :P, h], WV[b, :, h]], axis=0)
+            vis = np.concatenate([np.ones((q, P), bool), wvis], axis=1)
+            for g in range(G):
+                hq = h * G + g
+                logits = sm_scale * (Q[b, :, hq] @ keys.T)   # [q, P+q]
+                logits = np.where(vis, logits, -np.inf)
+                O[b, :, hq], LSE[b, hq] = _softmax_attend(logits, vals)
+    return O, LSE
+
+
+def cache_attention_eq6(Q, Kc, Vc, o, bl: int, sm_scale: float):
+    """Attention over the whole pre-allocated cache under the Eq. (6) mask.
+
+    FlowBlock review Eq. (6): the keys are the cache positions ``j`` of
+    ``[0, C)`` that ``eq6_mask`` marks visible; all other positions are
+    never read (they may hold anything, NaN included).  Kc, Vc:
+    ``[B, C, Hkv, d]``.  Returns ``O [B, q, Hq, d]``, ``LSE [B, Hq, q]``.
+    """
+    Q, Kc, Vc = _f64(Q), _f64(Kc), _f64(Vc)
+    B, q, Hq, d = Q.shape
+    C, Hkv = Kc.shape[1], Kc.shape[2]
+    G = Hq // Hkv
+    M = eq6_mask(C, q, bl, o)
+    O = np.empty((B, q, Hq, d))
+    LSE = np.empty((B, Hq, q))
+    for b in range(B):
+        cols = np.nonzero(M[b].any(axis=0))[0]             # keys read at all
+        vis = M[b][:, cols]
+        for h in range(Hkv):
+            keys, vals = Kc[b, cols, h], Vc[b, cols, h]
+            for g in range(G):
+                hq = h * G + g
+                logits = sm_scale * (Q[b, :, hq] @ keys.T)
+                logits = np.where(vis, logits, -np.inf)
+                O[b, :, hq], LSE[b, hq] = _softmax_attend(logits, vals)
+    return O, LSE
+
+
+# ---------------------------------------------------------------------------
+# Representative query and selection scores
+# ---------------------------------------------------------------------------
+
+def center_row(bl: int, S: int) -> int:
+    """Block position HERALD Eq. (2) picks as the representative query.
+
+    Eq. (2): the position ``p_i`` of the block minimising
+    ``sum_s (p_i - s - mean_offset)^2`` over prefix positions ``s``.  For an
+    even block the two middle positions tie exactly; the page speaks of the
+    block centre with offsets of at most ``B/2`` from it, and the later of
+    the two (``bl // 2``) is taken.
+    """
+    o = S  # block starts right after the prefix; the result is shift-free
+    pos = o + np.arange(bl, dtype=np.float64)
+    s = np.arange(S, dtype=np.float64)
+    mean_off = (pos[:, None] - s[None, :]).mean()
+    obj = ((pos[:, None] - s[None, :] - mean_off) ** 2).sum(axis=1)
+    best = obj.min()
+    ties = np.nonzero(np.isclose(obj, best, rtol=1e-12, atol=0.0))[0]
+    return int(ties.max())
+
+
+def rep_query(Q, mode: str = "mean", row: int | None = None):
+    """Representative query per (row, query head), float64 ``[B, Hq, d]``.
+
+    HERALD Sec. IV-A2 replaces the block's queries by one representative.
+    ``mode='row'`` takes query ``row`` of the block (HERALD's choice is the
+    centre, see ``center_row``); ``mode='mean'`` averages the ``nq`` queries
+    given (the sparse workloads use the mean of the block's queries).
+    Q: ``[B, nq, Hq, d]``.
+    """
+    Q = _f64(Q)
+    if mode == "mean":
+        return Q.mean(axis=1)
+    if mode == "row":
+        return Q[:, int(row)].copy()
+    raise ValueError(mode)
+
+
+def selection_scores(q_rep, K, s_len, sm_scale: float):
+    """GQA importance of every prefix position, HERALD Sec. IV-B4.
+
+    For row ``b`` and KV head ``h`` with query heads ``g < G``:
+    ``z[g, s] = sm_scale * <q_rep[b, h*G+g], K[b, s, h]>`` for ``s < S_b``,
+    ``m_g = max_s z[g, s]``, ``l_g = sum_s exp(z[g, s] - m_g)`` and
+    ``s_hat[s] = sum_g exp(z[g, s] - m_g) / l_g``.
+
+    q_rep: ``[B, Hq, d]``; K: ``[B, C, Hkv, d]``; s_len: ``[B]``.
+    Returns ``s_hat [B, Hkv, max(s_len)]`` (0 past ``S_b``), ``m`` and ``l``
+    ``[B, Hq]`` (NaN for rows with ``S_b = 0``).
+    """
+    q_rep, K = _f64(q_rep), _f64(K)
+    s_len = _i64(s_len)
+    B, Hq, d = q_rep.shape
+    Hkv = K.shape[2]
+    G = Hq // Hkv
+    s_max = int(s_len.max()) if len(s_len) else 0
+    s_hat = np.zeros((B, Hkv, s_max))
+    m = np.full((B, Hq), np.nan)
+    l = np.full((B, Hq), np.nan)
+    for b in range(B):
+        S = int(s_len[b])
+        if S == 0:
+            continue
+        for h in range(Hkv):
+            qg = q_rep[b, h * G:(h + 1) * G]               # [G, d]
+            z = sm_scale * (qg @ K[b, :S, h].T)            # [G, S]
+            mg = z.max(axis=1, keepdims=True)
+            e = np.exp(z - mg)
+            lg = e.sum(axis=1, keepdims=True)
+            s_hat[b, h, :S] = (e / lg).sum(axis=0)
+            m[b, h * G:(h + 1) * G] = mg[:, 0]
+            l[b, h * G:(h + 1) * G] = lg[:, 0]
+    return s_hat, m, l
+
+
+def topk_select(scores, s_len, k_sel, k_max: int) -> np.ndarray:
+    """Per-(row, KV head) top-k critical set, HERALD Sec. IV-B4.
+
+    Keeps the ``min(k_b, S_b)`` positions with the largest score; equal
+    scores go to the lower position.  The kept positions are written in
+    ascending order and the rest of the ``k_max`` slots hold -1.
+    scores: ``[B, Hkv, >= S_b]``.  Returns int64 ``[B, Hkv, k_max]``.
+    """
+    scores = _f64(scores)
+    s_len, k_sel = _i64(s_len), _i64(k_sel)
+    B, Hkv = scores.shape[:2]
+    out = np.full((B, Hkv, k_max), -1, dtype=np.int64)
+    for b in range(B):
+        S = int(s_len[b])
+        k = min(int(k_sel[b]), S)
+        if k <= 0:
+            continue
+        for h in range(Hkv):
+            sc = scores[b, h, :S]
+            order = np.lexsort((np.arange(S), -sc))        # score desc, pos asc
+            out[b, h, :k] = np.sort(order[:k])
+    return out
+
+
+# ---------------------------------------------------------------------------
+# KV movement
+# ---------------------------------------------------------------------------
+
+def gather(src, idx, k_cnt, pool):
+    """Copy selected entries into the compact pool, HERALD Sec. IV-B3.
+
+    ``pool[b, j, h] = src[b, idx[b, h, j], h]`` for ``j < k_cnt[b]``; every
+    other pool slot keeps its value.  Works on any dtype (bit copy).
+    """
+    src = np.asarray(src)
+    pool = np.array(pool, copy=True)
+    idx, k_cnt = _i64(idx), _i64(k_cnt)
+    B, Hkv = idx.shape[:2]
+    for b in range(B):
+        for h in range(Hkv):
+            for j in range(int(k_cnt[b])):
+                pool[b, j, h] = src[b, idx[b, h, j], h]
+    return pool
+
+
+def kv_scatter(present, data, o, t: int, q: int, rows=None):
+    """KV write-back, FlowBlock review Eq. (7) (paper Eq. 6).
+
+    ``data[l, b, o_b + delta] <- present[l, b, t + delta]`` for
+    ``delta < q`` and every layer ``l``; everything else in ``data`` keeps
+    its value.  present, data: ``[L, B, P, Hkv, d]`` (any dtype, bit copy).
+    ``present`` may be the same array as ``data``; the source rows are read
+    before any write.
+    """
+    present = np.asarray(present)
+    src = present[:, :, t:t + q].copy()
+    data = np.array(data, copy=True)
+    o = _i64(o)
+    B = data.shape[1]
+    rows = range(B) if rows is None else [int(r) for r in _i64(rows)]
+    for b in rows:
+        ob = int(o[b])
+        data[:, b, ob:ob + q] = src[:, b]
+    return data
