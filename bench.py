@@ -1,0 +1,246 @@
+"""Benchmark of the block-diffusion hot path on one MI355X.
+
+One step = one pass of every operation of the path over one batch of the
+64-row serving mix (log-uniform prefixes 1K-16K, W = 4 windows of 32-token
+blocks, 32/8 heads, d = 128, bf16): selection + gather for the rows whose
+prefix exceeds 8K (5 % budget), W-shaped attention of the dense rows over
+their own cache and of the sparse rows over their pools, and the KV
+write-back scatter of every row.  Inputs are resident in HBM before the
+timed region.
+
+Prints one JSON line.  ``value`` is the whole-step throughput in attention
+TFLOP/s: the algorithmic attention FLOPs of the step (4*d per visible
+(query, key) pair per query head) divided by the step time, select, gather
+and scatter included.  ``breakdown`` gives each operation's own rate
+(TFLOP/s or GB/s of algorithmic bytes) and fraction of the MI355X peak.
+``roofline`` reports the dominant kernel (dense-row attention), timed with
+HIP events on the stream it runs on.  ``cpu_baseline`` times the float64
+oracle on a bounded sample of the same step on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+METRIC = "block-diffusion attn TFLOP/s + select GB/s, as % of MI355X roofline"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_mfma_serving_mix_traffic.json")
+ATTN_SOURCE = os.path.join(ROOT, "sparse_kv_cache_bd_amd", "csrc", "bd_attn.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def attention_flops(p_len, rows, q, bl, Hq, d):
+    """4*d FLOPs per visible (query, key) pair per query head."""
+    win = sum(min(q, (i // bl + 1) * bl) for i in range(q))
+    return sum(4 * d * Hq * (q * int(p_len[b]) + win) for b in rows)
+
+
+def step_work(wl):
+    """Algorithmic FLOPs / bytes of one step, per operation."""
+    q, bl, Hq, Hkv, d = wl.q, wl.bl, wl.Hq, wl.Hkv, wl.d
+    es = 2
+    dense = wl.dense_rows.tolist()
+    sparse = wl.sparse_rows.tolist()
+    tok = Hkv * d * es                      # bytes of one (pos) row of K or V
+    w = {}
+    w["attn_dense_flop"] = attention_flops(wl.o, dense, q, bl, Hq, d)
+    w["attn_sparse_flop"] = attention_flops(wl.k_sel, sparse, q, bl, Hq, d)
+    w["select_bytes"] = sum(int(wl.s_len[b]) * tok for b in sparse) + len(sparse) * Hkv * wl.k_max * 4
+    w["gather_bytes"] = sum(int(wl.k_sel[b]) * tok * 2 * 2 for b in sparse)
+    w["scatter_bytes"] = wl.B * q * tok * 2 * 2
+    # bytes the dense attention must move at least once: Q, O, prefix + window K/V
+    w["attn_dense_bytes"] = sum(q * Hq * d * es * 2 + (int(wl.o[b]) + q) * tok * 2 for b in dense)
+    return w
+
+
+def traffic_for_attention():
+    """HBM bytes per dense-attention launch from the committed rocprofv3
+    counter summary, or None when the kernel source changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        with open(ATTN_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        if rec.get("source_sha256") != sha:
+            return None
+        return rec.get("bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, budget_s: float = 12.0):
+    """The float64 oracle timed on the host cores over a bounded sample of
+    the same step: whole rows (selection + gather + attention for sparse
+    rows, attention for dense rows, then the scatter), alternating dense and
+    sparse rows from the shortest up until about ``budget_s`` seconds."""
+    import numpy as np
+    import torch
+    from oracle import bd_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        cores = len(os.sched_getaffinity(0))
+    dense = sorted(wl.dense_rows.tolist(), key=lambda b: int(wl.o[b]))
+    sparse = sorted(wl.sparse_rows.tolist(), key=lambda b: int(wl.o[b]))
+    order = []
+    for i in range(max(len(dense), len(sparse))):
+        if i < len(dense):
+            order.append(("dense", dense[i]))
+        if i < len(sparse):
+            order.append(("sparse", sparse[i]))
+    t = wl.t
+    flops = 0
+    done = []
+    t0 = time.perf_counter()
+    for kind, b in order:
+        rows = [b]
+        if kind == "dense":
+            orc.block_attention(wl.Q[b:b + 1], wl.Kc[b:b + 1], wl.Vc[b:b + 1], wl.o[b:b + 1],
+                                wl.Kc[b:b + 1, t:], wl.Vc[b:b + 1, t:], wl.bl, wl.sm_scale)
+            flops += attention_flops(wl.o, rows, wl.q, wl.bl, wl.Hq, wl.d)
+        else:
+            qr = orc.rep_query(wl.Q[b:b + 1], "mean")
+            sh, _, _ = orc.selection_scores(qr, wl.Kc[b:b + 1], wl.s_len[b:b + 1], wl.sm_scale)
+            idx = orc.topk_select(sh, wl.s_len[b:b + 1], wl.k_sel[b:b + 1], int(wl.k_sel[b]))
+            kb = int(wl.k_sel[b])
+            z = np.zeros((1, kb, wl.Hkv, wl.d))
+            pk = orc.gather(wl.Kc[b:b + 1].double().numpy(), idx, wl.k_sel[b:b + 1], z)
+            pv = orc.gather(wl.Vc[b:b + 1].double().numpy(), idx, wl.k_sel[b:b + 1], z)
+            orc.block_attention(wl.Q[b:b + 1], pk, pv, wl.k_sel[b:b + 1], wl.Kc[b:b + 1, t:],
+                                wl.Vc[b:b + 1, t:], wl.bl, wl.sm_scale)
+            flops += attention_flops(wl.k_sel, rows, wl.q, wl.bl, wl.Hq, wl.d)
+        kv = wl.Kc[b:b + 1].view(torch.int16).numpy()[None]
+        orc.kv_scatter(kv, kv, wl.o[b:b + 1], t, wl.q)
+        done.append(f"{kind}:{b}(P={int(wl.o[b])})")
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{len(done)} of {wl.B} rows of the same step, whole rows "
+                      f"(dense: attention; sparse: select+gather+attention; all: scatter), "
+                      f"shortest first: {', '.join(done)}; {el:.1f} s float64 NumPy",
+            "seconds": round(el, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              "this build has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from sparse_kv_cache_bd_amd import bdattn as bd
+    from sparse_kv_cache_bd_amd.pipeline import BlockDiffusionStep
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    bd.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("generating the serving-mix workload")
+    wl = synth.serving_mix(seed=args.seed)
+    Kc, Vc, Q, o = (x.to(dev) for x in (wl.Kc, wl.Vc, wl.Q, wl.o))
+    dense_pmax = int(wl.o[wl.dense_rows.long()].max()) if len(wl.dense_rows) else 0
+    step = BlockDiffusionStep(Kc, Vc, Q, o, wl.bl, wl.sm_scale, sparse_rows=wl.sparse_rows,
+                              dense_rows=wl.dense_rows, s_len=wl.s_len, k_sel=wl.k_sel,
+                              p_max_dense=dense_pmax, k_max=wl.k_max, s_max=wl.s_max)
+    work = step_work(wl)
+    log(f"rows={wl.B} dense={step.n_dense} sparse={step.n_sparse} warmup={args.warmup} steps={args.steps}")
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+
+    ops = BlockDiffusionStep.OPS
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        e = ev[s]
+        e[0].record()
+        for i, name in enumerate(ops):
+            getattr(step, name)()
+            e[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    op_ms = {name: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
+             for i, name in enumerate(ops)}
+    ms_step = wall * 1e3 / args.steps
+    ev_step = sum(ev[s][0].elapsed_time(ev[s][-1]) for s in range(args.steps)) / args.steps
+    log(f"step {ms_step:.3f} ms (events {ev_step:.3f} ms): " +
+        ", ".join(f"{k} {v * 1e3:.1f} us" for k, v in op_ms.items()))
+
+    attn_flop = work["attn_dense_flop"] + work["attn_sparse_flop"]
+    value = attn_flop / (ms_step * 1e-3) / 1e12
+
+    def rate(num, ms, scale):
+        return num / (ms * 1e-3) / scale if ms > 0 else None
+
+    bd_ = {}
+    tf_d = rate(work["attn_dense_flop"], op_ms["attn_dense"], 1e12)
+    tf_s = rate(work["attn_sparse_flop"], op_ms["attn_sparse"], 1e12)
+    gb_sel = rate(work["select_bytes"], op_ms["select"], 1e9)
+    gb_gat = rate(work["gather_bytes"], op_ms["gather"], 1e9)
+    gb_sca = rate(work["scatter_bytes"], op_ms["scatter"], 1e9)
+    bd_["attn_dense"] = {"us": round(op_ms["attn_dense"] * 1e3, 2), "TFLOP/s": round(tf_d, 2),
+                         "frac_mfma_peak": round(tf_d / PEAK_BF16_TFLOPS, 4),
+                         "gflop": round(work["attn_dense_flop"] / 1e9, 3)}
+    bd_["attn_sparse"] = {"us": round(op_ms["attn_sparse"] * 1e3, 2), "TFLOP/s": round(tf_s, 2),
+                          "frac_mfma_peak": round(tf_s / PEAK_BF16_TFLOPS, 4),
+                          "gflop": round(work["attn_sparse_flop"] / 1e9, 3)}
+    bd_["select"] = {"us": round(op_ms["select"] * 1e3, 2), "GB/s": round(gb_sel, 1),
+                     "frac_hbm_peak": round(gb_sel / PEAK_HBM_GBS, 4),
+                     "mb": round(work["select_bytes"] / 1e6, 2)}
+    bd_["gather"] = {"us": round(op_ms["gather"] * 1e3, 2), "GB/s": round(gb_gat, 1),
+                     "frac_hbm_peak": round(gb_gat / PEAK_HBM_GBS, 4),
+                     "mb": round(work["gather_bytes"] / 1e6, 2)}
+    bd_["scatter"] = {"us": round(op_ms["scatter"] * 1e3, 2), "GB/s": round(gb_sca, 1),
+                      "frac_hbm_peak": round(gb_sca / PEAK_HBM_GBS, 4),
+                      "mb": round(work["scatter_bytes"] / 1e6, 2)}
+
+    traffic = traffic_for_attention()
+    roof = {"bound": "mfma", "kernel": "attn_mfma_kernel<4> (dense rows)",
+            "achieved": round(tf_d, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf_d / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+            "algorithmic_bytes": work["attn_dense_bytes"],
+            "intensity_flop_per_byte": round(work["attn_dense_flop"] / work["attn_dense_bytes"], 1)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the float64 oracle on a bounded sample (cpu_baseline)")
+        cpu = cpu_baseline(wl, args.cpu_budget)
+
+    res = {"metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic",
+           "config": {"workload": "serving_mix", "rows": wl.B, "dense_rows": step.n_dense,
+                      "sparse_rows": step.n_sparse, "prefix": "log-uniform 1K-16K",
+                      "bl": wl.bl, "W": wl.W, "q": wl.q, "Hq": wl.Hq, "Hkv": wl.Hkv, "d": wl.d,
+                      "C": wl.C, "budget": 0.05, "seed": args.seed},
+           "roofline": roof, "cpu_baseline": cpu, "breakdown": bd_}
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,219 @@
+/*
+ * libbdattn: block-diffusion attention over a KV cache on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Four operations make up the data-parallel hot path of block-diffusion
+ * decoding with a KV cache:
+ *
+ *   bd_select       representative-query scan of the K cache plus a
+ *                   per-KV-head top-k critical set
+ *                   (HERALD, Sec. IV-A2 and Sec. IV-B4).
+ *   bd_gather       copy of the selected entries into a compact pool
+ *                   (HERALD, Sec. IV-B3; pools of Sec. IV-B1).
+ *   bd_attn_packed  GQA attention of a packed window of W blocks over a
+ *                   prefix (the cache, or a pool) plus the window, under the
+ *                   per-row W-shaped mask with absolute offsets
+ *                   (FlowBlock review, Eq. (5)-(6) = paper Eq. 4-5).
+ *   bd_kv_scatter   write-back of the window's KV to its absolute positions
+ *                   (FlowBlock review, Eq. (7) = paper Eq. 6).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Memory: every tensor pointer is device memory owned by the caller.  The
+ *   library allocates nothing and keeps no state between calls; scratch
+ *   space comes from a caller workspace whose size the matching
+ *   *_workspace_size function returns.
+ * - Streams: every call is asynchronous on the given hipStream_t (passed as
+ *   void*; NULL is the default stream).  No call synchronises, reads device
+ *   memory from the host, or allocates, so calls can be captured in a HIP
+ *   graph.  Host integers (s_max, k_max, p_max, ...) size the grids; the
+ *   per-row values live in device int32 arrays.
+ * - Layout: tensors are token-major with the head dimension d contiguous.
+ *   Strides are in elements (int64) for the outer dimensions, e.g. a K cache
+ *   [B, C, Hkv, d] has strides {C*Hkv*d, Hkv*d, d}.  Base pointers must be
+ *   16-byte aligned and every stride times the element size a multiple of
+ *   16 bytes.
+ * - dtypes: BD_BF16 (bfloat16 storage, fp32 arithmetic) and BD_F32.
+ * - Errors: host-side validation runs before any HIP call; on failure the
+ *   call returns a nonzero bd_status, launches nothing and writes nothing.
+ *   bd_last_error() returns a thread-local message for the last failure.
+ * - Device-side values (offsets, lengths, indices) are range-checked in the
+ *   kernels: an out-of-range value never causes an out-of-bounds access;
+ *   the affected row, slot or entry is skipped (left unchanged) or clamped,
+ *   as each function states.
+ * - GQA: query head hq reads KV head hq / (Hq / Hkv).
+ */
+#ifndef BDATTN_H
+#define BDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BD_OK = 0,
+  BD_ERR_INVALID_ARG = 1, /* bad size, pointer, stride or alignment      */
+  BD_ERR_UNSUPPORTED = 2, /* valid but not built: dtype / head-dim combo */
+  BD_ERR_HIP = 3,         /* a HIP launch reported an error              */
+  BD_ERR_WORKSPACE = 4    /* workspace missing or too small              */
+} bd_status;
+
+typedef enum { BD_BF16 = 0, BD_F32 = 1 } bd_dtype;
+
+typedef enum {
+  BD_REP_MEAN = 0, /* mean of the nq given queries                       */
+  BD_REP_ROW = 1   /* one query row (HERALD's block-centre [MASK] query) */
+} bd_rep_mode;
+
+/* Library version string, e.g. "libbdattn 0.1.0 gfx950". */
+const char *bd_version(void);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *bd_last_error(void);
+
+/*
+ * bd_kv_scatter: FlowBlock review Eq. (7) (paper Eq. 6).
+ *
+ *   data[l, b, o_b + delta, h, :] <- present[l, b, t + delta, h, :]
+ *   for delta < q, every KV head h and every layer l < n_layers,
+ *
+ * for the rows b listed in row_ids (all B rows when row_ids is NULL; then
+ * n_rows must equal B).  Keys and values are both moved (data_v may be NULL
+ * together with present_v to move K only).  Bit-exact copy of any dtype.
+ *
+ *   present_k/v  [n_layers, B, present_cap, Hkv, d], strides present_strides
+ *                {layer, row, pos, head}; positions [t, t+q) are read.
+ *   data_k/v     [n_layers, B, data_cap, Hkv, d], strides data_strides.
+ *   o            device int32 [B]: per-row write offset o_b.
+ *
+ * present may alias data (the FlowBlock cache: window at the tail
+ * t = C - q).  Requires t + q <= present_cap.  A row whose o_b is negative
+ * or has o_b + q > data_cap is skipped; with aliasing, o_b must satisfy
+ * o_b + q <= t or o_b == t, otherwise the result is undefined.
+ */
+int bd_kv_scatter(int dtype, int B, int Hkv, int d, int q, int n_layers,
+                  const void *present_k, const void *present_v,
+                  const int64_t present_strides[4], int present_cap, int t,
+                  void *data_k, void *data_v, const int64_t data_strides[4],
+                  int data_cap, const int32_t *o, const int32_t *row_ids,
+                  int n_rows, void *stream);
+
+/*
+ * bd_gather: HERALD Sec. IV-B3 (CPU gather of the selected entries into a
+ * contiguous buffer), here device memory to device memory.
+ *
+ *   k_pool[b, j, h, :] = k_src[b, idx[b, h, j], h, :]   for j < k_cnt[b]
+ *   v_pool[b, j, h, :] = v_src[b, idx[b, h, j], h, :]
+ *
+ *   k_src/v_src  [B, src_cap, Hkv, d], strides src_strides {row, pos, head}.
+ *   idx          device int32 [B, Hkv, k_max], contiguous (bd_select output).
+ *   k_cnt        device int32 [B]; clamped to [0, k_max].
+ *   k_pool/v_pool [B, pool_cap, Hkv, d], strides pool_strides; pool_cap >= k_max.
+ *
+ * Pool slots j >= k_cnt[b] are left unchanged, as is any slot whose index is
+ * outside [0, src_cap).  v_src/v_pool may both be NULL to gather K only.
+ */
+int bd_gather(int dtype, int B, int Hkv, int d, const void *k_src,
+              const void *v_src, const int64_t src_strides[3], int src_cap,
+              const int32_t *idx, int k_max, const int32_t *k_cnt,
+              void *k_pool, void *v_pool, const int64_t pool_strides[3],
+              int pool_cap, void *stream);
+
+/*
+ * bd_select: HERALD Sec. IV-A2 (representative query) and Sec. IV-B4
+ * (fused selection: GQA importance and one top-k per KV head).
+ *
+ * For every row b with S_b = s_len[b] > 0 and k_b = k_sel[b] > 0:
+ *   q_rep[hq]   = mean_i q[b, i, hq, :] over i < nq     (BD_REP_MEAN)
+ *               = q[b, rep_row, hq, :]                  (BD_REP_ROW)
+ *   z[g, s]     = sm_scale * <q_rep[h*G+g], k[b, s, h, :]>   for s < S_b
+ *   m_g, l_g    = max_s z[g, s],  sum_s exp(z[g, s] - m_g)
+ *   score[h, s] = sum_g exp(z[g, s] - m_g) / l_g
+ *   idx_out[b, h, 0:min(k_b, S_b)] = the positions of the min(k_b, S_b)
+ *       largest scores, ties to the lower position, in ascending order;
+ *       the remaining slots up to k_max hold -1.
+ * Rows with S_b == 0 or k_b == 0 get idx_out all -1.
+ *
+ *   q         [B, nq, Hq, d] bf16, strides q_strides {row, query, head}.
+ *   k         [B, k_cap, Hkv, d] bf16, strides k_strides.
+ *   s_len     device int32 [B], clamped to [0, min(s_max, k_cap)].
+ *   k_sel     device int32 [B], clamped to [0, k_max].
+ *   idx_out   device int32 [B, Hkv, k_max], contiguous.
+ *   score_out optional device float [B, Hkv, s_max], contiguous: receives
+ *             the score vector exactly as ranked (positions >= S_b, and rows
+ *             with S_b == 0 or k_b == 0, are not written).  NULL keeps the
+ *             scores in the workspace.
+ *   workspace at least bd_select_workspace_size(...) bytes, 256-byte aligned.
+ *
+ * Built for dtype BD_BF16 with d == 128 and Hq / Hkv <= 8.
+ */
+size_t bd_select_workspace_size(int B, int Hq, int Hkv, int d, int s_max,
+                                int k_max);
+int bd_select(int dtype, int B, int Hq, int Hkv, int d, const void *q,
+              const int64_t q_strides[3], int nq, int rep_mode, int rep_row,
+              const void *k, const int64_t k_strides[3], int k_cap,
+              const int32_t *s_len, int s_max, const int32_t *k_sel, int k_max,
+              float sm_scale, int32_t *idx_out, float *score_out,
+              void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * bd_attn_packed: FlowBlock review Eq. (6) (paper Eq. 5) in prefix/window
+ * form; HERALD's denoising attention when the prefix is a pool.
+ *
+ * For each listed row b, query i < q, query head hq (KV head h):
+ *   visible keys = prefix entries pk/pv[b, j, h] for j < P_b = p_len[b]
+ *                  and window entries wk/wv[b, w, h] for
+ *                  w < (floor(i / bl) + 1) * bl      (capped at q)
+ *   out[b, i, hq, :] = sum_j softmax_j(sm_scale * <q[b,i,hq], key_j>) value_j
+ *   lse[b, hq, i]    = log sum_j exp(sm_scale * <q[b,i,hq], key_j>)
+ *
+ * FlowBlock call: pk = the cache [B, C, Hkv, d], p_len = o, wk = cache + t *
+ * pos_stride with t = C - q: key j < o_b is prefix j and key j in [t, C) is
+ * window j - t, exactly the Eq. (6) mask.  Sparse call: pk = a pool filled
+ * by bd_gather, p_len = k_b.  q = W * bl for a window of W blocks.
+ *
+ *   row_ids   device int32 [n_rows] or NULL (all B rows; n_rows == B).
+ *             Rows not listed are not written.  Entries outside [0, B) are
+ *             skipped.
+ *   q, out    [B, q, Hq, d], strides {row, query, head}.  out has q's dtype.
+ *   pk/pv     [B, p_cap, Hkv, d]; p_len device int32 [B], clamped to
+ *             [0, min(p_max, p_cap)].  Prefix rows at or past P_b are never
+ *             read, so they may hold anything (NaN included).
+ *   wk/wv     [B, q, Hkv, d] (any strides, e.g. a view of the cache tail).
+ *   lse       optional device float [B, Hq, q], contiguous.
+ *   workspace at least bd_attn_workspace_size(...) bytes, 256-byte aligned
+ *             (zero bytes are needed when the split plan keeps one chunk).
+ *
+ * Built for: BD_BF16 with d == 128 and Hq / Hkv in {1, 2, 4, 8} (MFMA path),
+ * BD_BF16 / BD_F32 with d in {64, 128} (general path).
+ */
+size_t bd_attn_workspace_size(int dtype, int B, int Hq, int Hkv, int d, int q,
+                              int n_rows, int p_max);
+int bd_attn_packed(int dtype, int B, int Hq, int Hkv, int d, int q, int bl,
+                   const int32_t *row_ids, int n_rows, const void *q_ptr,
+                   const int64_t q_strides[3], const void *pk, const void *pv,
+                   const int64_t p_strides[3], int p_cap,
+                   const int32_t *p_len, int p_max, const void *wk,
+                   const void *wv, const int64_t w_strides[3], float sm_scale,
+                   void *out, const int64_t out_strides[3], float *lse,
+                   void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * bd_mask_materialize: test hook for the attention mask.  Writes
+ * out[b, i, j] = 1 if query i of row b sees cache position j under
+ * FlowBlock review Eq. (6) (j < o_b, or t <= j < t + (floor(i/bl)+1)*bl
+ * with t = C - q), else 0, for j < C.  out is device uint8 [B, q, C],
+ * contiguous.  It evaluates the same device predicate the attention kernels
+ * use.  Rows with o_b outside [0, t] are written all 0xFF.
+ */
+int bd_mask_materialize(int B, int C, int q, int bl, const int32_t *o,
+                        uint8_t *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BDATTN_H */

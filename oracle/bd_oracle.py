@@ -52,7 +52,9 @@ __all__ = [
 
 
 def _f64(x):
-    """Exact conversion of a NumPy or torch (CPU) array to float64."""
+    """Exact conversion of a NumPy or torch (CPU) array to float64.  The
+    functions below convert one (row, KV head) slice at a time, so inputs
+    may be far larger than their float64 copy would be."""
     if hasattr(x, "detach"):
         x = x.detach().cpu().double().numpy()
     return np.asarray(x, dtype=np.float64)
@@ -137,7 +139,7 @@ def block_attention(Q, PK, PV, p_len, WK, WV, bl: int, sm_scale: float,
     Returns ``O [B, q, Hq, d]`` and ``LSE [B, Hq, q]`` in float64; rows not
     in ``rows`` are NaN.
     """
-    Q, PK, PV, WK, WV = (_f64(x) for x in (Q, PK, PV, WK, WV))
+    Q = _f64(Q)
     p_len = _i64(p_len)
     B, q, Hq, d = Q.shape
     Hkv = PK.shape[2]
@@ -150,8 +152,8 @@ def block_attention(Q, PK, PV, p_len, WK, WV, bl: int, sm_scale: float,
     for b in rows:
         P = int(p_len[b])
         for h in range(Hkv):
-            keys = np.concatenate([PK[b, :P, h], WK[b, :, h]], axis=0)
-            vals = np.concatenate([PV[b, :P, h], WV[b, :, h]], axis=0)
+            keys = np.concatenate([_f64(PK[b, :P, h]), _f64(WK[b, :, h])], axis=0)
+            vals = np.concatenate([_f64(PV[b, :P, h]), _f64(WV[b, :, h])], axis=0)
             vis = np.concatenate([np.ones((q, P), bool), wvis], axis=1)
             for g in range(G):
                 hq = h * G + g
@@ -169,7 +171,7 @@ def cache_attention_eq6(Q, Kc, Vc, o, bl: int, sm_scale: float):
     never read (they may hold anything, NaN included).  Kc, Vc:
     ``[B, C, Hkv, d]``.  Returns ``O [B, q, Hq, d]``, ``LSE [B, Hq, q]``.
     """
-    Q, Kc, Vc = _f64(Q), _f64(Kc), _f64(Vc)
+    Q = _f64(Q)
     B, q, Hq, d = Q.shape
     C, Hkv = Kc.shape[1], Kc.shape[2]
     G = Hq // Hkv
@@ -180,7 +182,7 @@ def cache_attention_eq6(Q, Kc, Vc, o, bl: int, sm_scale: float):
         cols = np.nonzero(M[b].any(axis=0))[0]             # keys read at all
         vis = M[b][:, cols]
         for h in range(Hkv):
-            keys, vals = Kc[b, cols, h], Vc[b, cols, h]
+            keys, vals = _f64(Kc[b, cols, h]), _f64(Vc[b, cols, h])
             for g in range(G):
                 hq = h * G + g
                 logits = sm_scale * (Q[b, :, hq] @ keys.T)
@@ -241,7 +243,7 @@ def selection_scores(q_rep, K, s_len, sm_scale: float):
     Returns ``s_hat [B, Hkv, max(s_len)]`` (0 past ``S_b``), ``m`` and ``l``
     ``[B, Hq]`` (NaN for rows with ``S_b = 0``).
     """
-    q_rep, K = _f64(q_rep), _f64(K)
+    q_rep = _f64(q_rep)
     s_len = _i64(s_len)
     B, Hq, d = q_rep.shape
     Hkv = K.shape[2]
@@ -256,7 +258,7 @@ def selection_scores(q_rep, K, s_len, sm_scale: float):
             continue
         for h in range(Hkv):
             qg = q_rep[b, h * G:(h + 1) * G]               # [G, d]
-            z = sm_scale * (qg @ K[b, :S, h].T)            # [G, S]
+            z = sm_scale * (qg @ _f64(K[b, :S, h]).T)      # [G, S]
             mg = z.max(axis=1, keepdims=True)
             e = np.exp(z - mg)
             lg = e.sum(axis=1, keepdims=True)

@@ -1,0 +1,225 @@
+"""Thin ctypes binding of libbdattn (argument marshalling only).
+
+Every function takes torch tensors on the GPU, turns them into device
+pointers, element strides and the current HIP stream, and calls the C-ABI
+entry point of the same name.  All computation happens in the HIP kernels;
+there is no CPU path.  A missing library or a CPU tensor raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbdattn.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "bdattn.h")
+
+BD_OK, BD_ERR_INVALID_ARG, BD_ERR_UNSUPPORTED, BD_ERR_HIP, BD_ERR_WORKSPACE = 0, 1, 2, 3, 4
+BD_BF16, BD_F32 = 0, 1
+BD_REP_MEAN, BD_REP_ROW = 0, 1
+
+_DTYPE = {torch.bfloat16: BD_BF16, torch.float32: BD_F32}
+
+_c_i64_3 = ctypes.c_int64 * 3
+_c_i64_4 = ctypes.c_int64 * 4
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+
+_SIGS = {
+    "bd_version": (ctypes.c_char_p, []),
+    "bd_last_error": (ctypes.c_char_p, []),
+    "bd_kv_scatter": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp, _vp, _i,
+                           _vp, _vp, _i, _vp]),
+    "bd_gather": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _i, _vp]),
+    "bd_select_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "bd_select": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _i, _i, _i, _vp, _vp, _i, _vp, _i, _vp, _i,
+                       ctypes.c_float, _vp, _vp, _vp, _sz, _vp]),
+    "bd_attn_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "bd_attn_packed": (_i, [_i, _i, _i, _i, _i, _i, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp, _i,
+                            _vp, _i, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _sz,
+                            _vp]),
+    "bd_mask_materialize": (_i, [_i, _i, _i, _i, _vp, _vp, _vp]),
+}
+
+_lib = None
+
+
+class BdError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libbdattn error {code}: {msg}")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """Load libbdattn.so (built in-tree); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions the public header declares."""
+    with open(HEADER_PATH) as f:
+        txt = f.read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(bd_[a-z_0-9]+)\s*\(", txt)))
+
+
+def version() -> str:
+    return lib().bd_version().decode()
+
+
+def last_error() -> str:
+    return lib().bd_last_error().decode()
+
+
+def _check(code: int):
+    if code != BD_OK:
+        raise BdError(code, last_error())
+
+
+def _dev(t: torch.Tensor | None, name: str):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a tensor on the GPU")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _strides(t: torch.Tensor, n: int):
+    if t.stride(-1) != 1:
+        raise ValueError("the head dimension must be contiguous")
+    st = list(t.stride()[:-1])
+    assert len(st) == n, (t.shape, n)
+    return (_c_i64_3 if n == 3 else _c_i64_4)(*st)
+
+
+def _i32(t, name):
+    t = _dev(t, name)
+    if t.dtype != torch.int32 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 GPU tensor")
+    return t
+
+
+def workspace(nbytes: int, device=None) -> torch.Tensor | None:
+    """Caller-owned workspace (256-byte aligned: torch allocations are)."""
+    if nbytes <= 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device or "cuda")
+
+
+# ---------------------------------------------------------------------------
+
+def kv_scatter(present_k, present_v, data_k, data_v, o, t: int, q: int, row_ids=None):
+    """Eq. (7) write-back.  present_*/data_*: [L, B, P, Hkv, d] or [B, P, Hkv, d]."""
+    pk, dk = _dev(present_k, "present_k"), _dev(data_k, "data_k")
+    pv, dv = _dev(present_v, "present_v"), _dev(data_v, "data_v")
+    if pk.dim() == 4:
+        pk, dk = pk.unsqueeze(0), dk.unsqueeze(0)
+        pv = pv.unsqueeze(0) if pv is not None else None
+        dv = dv.unsqueeze(0) if dv is not None else None
+    if pv is not None and (pv.stride() != pk.stride() or dv.stride() != dk.stride()):
+        raise ValueError("K and V tensors must share strides")
+    L, B, Pcap, Hkv, d = pk.shape
+    o = _i32(o, "o")
+    rid = _i32(row_ids, "row_ids") if row_ids is not None else None
+    n_rows = B if rid is None else rid.numel()
+    _check(lib().bd_kv_scatter(_DTYPE[pk.dtype], B, Hkv, d, q, L, _ptr(pk), _ptr(pv),
+                               _strides(pk, 4), Pcap, t, _ptr(dk), _ptr(dv), _strides(dk, 4),
+                               dk.shape[2], _ptr(o), _ptr(rid), n_rows, _stream()))
+
+
+def gather(k_src, v_src, idx, k_cnt, k_pool, v_pool):
+    """Pool gather.  *_src: [B, S, Hkv, d]; idx [B, Hkv, k_max]; pools [B, >=k_max, Hkv, d]."""
+    ks, kp = _dev(k_src, "k_src"), _dev(k_pool, "k_pool")
+    vs, vp = _dev(v_src, "v_src"), _dev(v_pool, "v_pool")
+    if vs is not None and (vs.stride() != ks.stride() or vp.stride() != kp.stride()):
+        raise ValueError("K and V tensors must share strides")
+    idx = _i32(idx, "idx")
+    k_cnt = _i32(k_cnt, "k_cnt")
+    B, S, Hkv, d = ks.shape
+    k_max = idx.shape[2]
+    _check(lib().bd_gather(_DTYPE[ks.dtype], B, Hkv, d, _ptr(ks), _ptr(vs), _strides(ks, 3), S,
+                           _ptr(idx), k_max, _ptr(k_cnt), _ptr(kp), _ptr(vp), _strides(kp, 3),
+                           kp.shape[1], _stream()))
+
+
+def select_workspace_size(B, Hq, Hkv, d, s_max, k_max) -> int:
+    return int(lib().bd_select_workspace_size(B, Hq, Hkv, d, s_max, k_max))
+
+
+def select(q, k, s_len, s_max: int, k_sel, k_max: int, sm_scale: float, rep_mode: int = BD_REP_MEAN,
+           rep_row: int = 0, idx_out=None, score_out=None, ws=None):
+    """Representative-query top-k.  q [B, nq, Hq, d]; k [B, C, Hkv, d].  Returns idx [B, Hkv, k_max]."""
+    q, k = _dev(q, "q"), _dev(k, "k")
+    B, nq, Hq, d = q.shape
+    Hkv = k.shape[2]
+    s_len, k_sel = _i32(s_len, "s_len"), _i32(k_sel, "k_sel")
+    if idx_out is None:
+        idx_out = torch.empty((B, Hkv, k_max), dtype=torch.int32, device=q.device)
+    need = select_workspace_size(B, Hq, Hkv, d, s_max, k_max)
+    if ws is None:
+        ws = workspace(need, q.device)
+    _check(lib().bd_select(_DTYPE[q.dtype], B, Hq, Hkv, d, _ptr(q), _strides(q, 3), nq, rep_mode,
+                           rep_row, _ptr(k), _strides(k, 3), k.shape[1], _ptr(s_len), s_max,
+                           _ptr(k_sel), k_max, float(sm_scale), _ptr(idx_out), _ptr(score_out),
+                           _ptr(ws), 0 if ws is None else ws.numel(), _stream()))
+    return idx_out
+
+
+def attn_workspace_size(dtype, B, Hq, Hkv, d, q, n_rows, p_max) -> int:
+    return int(lib().bd_attn_workspace_size(_DTYPE.get(dtype, dtype), B, Hq, Hkv, d, q, n_rows, p_max))
+
+
+def attn_packed(q, pk, pv, p_len, p_max: int, wk, wv, bl: int, sm_scale: float, out=None,
+                lse=None, row_ids=None, ws=None):
+    """Packed block-diffusion attention; returns out [B, q, Hq, d]."""
+    q = _dev(q, "q")
+    pk, pv, wk, wv = (_dev(x, n) for x, n in ((pk, "pk"), (pv, "pv"), (wk, "wk"), (wv, "wv")))
+    if pv.stride() != pk.stride() or wv.stride() != wk.stride():
+        raise ValueError("K and V tensors must share strides")
+    B, nqry, Hq, d = q.shape
+    Hkv = pk.shape[2]
+    p_len = _i32(p_len, "p_len")
+    rid = _i32(row_ids, "row_ids") if row_ids is not None else None
+    n_rows = B if rid is None else rid.numel()
+    if out is None:
+        out = torch.empty_like(q)
+    need = attn_workspace_size(q.dtype, B, Hq, Hkv, d, nqry, n_rows, p_max)
+    if ws is None:
+        ws = workspace(need, q.device)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be contiguous float32 [B, Hq, q]")
+    _check(lib().bd_attn_packed(_DTYPE[q.dtype], B, Hq, Hkv, d, nqry, bl, _ptr(rid), n_rows,
+                                _ptr(q), _strides(q, 3), _ptr(pk), _ptr(pv), _strides(pk, 3),
+                                pk.shape[1], _ptr(p_len), p_max, _ptr(wk), _ptr(wv),
+                                _strides(wk, 3), float(sm_scale), _ptr(out), _strides(out, 3),
+                                _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(), _stream()))
+    return out
+
+
+def mask_materialize(B: int, C: int, q: int, bl: int, o):
+    o = _i32(o, "o")
+    out = torch.empty((B, q, C), dtype=torch.uint8, device=o.device)
+    _check(lib().bd_mask_materialize(B, C, q, bl, _ptr(o), _ptr(out), _stream()))
+    return out

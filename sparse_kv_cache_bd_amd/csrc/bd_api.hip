@@ -1,0 +1,243 @@
+// Public C-ABI of libbdattn: argument validation (before any HIP call) and
+// dispatch to the kernel launchers.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "bd_common.h"
+
+namespace bd {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+static int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+static int esize(int dtype) { return dtype == BD_BF16 ? 2 : (dtype == BD_F32 ? 4 : 0); }
+
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+static bool strides_ok(const int64_t *s, int n, int es) {
+  for (int i = 0; i < n; ++i)
+    if (s[i] < 0 || ((s[i] * es) & 15) != 0) return false;
+  return true;
+}
+
+static int hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return BD_OK;
+  return fail(BD_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace bd
+
+using namespace bd;
+
+extern "C" {
+
+const char *bd_version(void) { return "libbdattn 0.1.0 gfx950"; }
+
+const char *bd_last_error(void) { return g_err; }
+
+int bd_kv_scatter(int dtype, int B, int Hkv, int d, int q, int n_layers, const void *present_k,
+                  const void *present_v, const int64_t present_strides[4], int present_cap, int t,
+                  void *data_k, void *data_v, const int64_t data_strides[4], int data_cap,
+                  const int32_t *o, const int32_t *row_ids, int n_rows, void *stream) {
+  g_err[0] = 0;
+  const int es = esize(dtype);
+  if (!es) return fail(BD_ERR_UNSUPPORTED, "bd_kv_scatter: unknown dtype %d", dtype);
+  if (B < 0 || Hkv <= 0 || d <= 0 || q < 0 || n_layers < 0 || n_rows < 0)
+    return fail(BD_ERR_INVALID_ARG, "bd_kv_scatter: negative or zero size");
+  if (!row_ids && n_rows != B)
+    return fail(BD_ERR_INVALID_ARG, "bd_kv_scatter: n_rows must equal B when row_ids is NULL");
+  if (B == 0 || q == 0 || n_layers == 0 || n_rows == 0) return BD_OK;
+  if ((d * es) % 16 != 0)
+    return fail(BD_ERR_UNSUPPORTED, "bd_kv_scatter: d * element size must be a multiple of 16 bytes");
+  if (!present_strides || !data_strides || !o)
+    return fail(BD_ERR_INVALID_ARG, "bd_kv_scatter: null strides or offsets");
+  if (!present_k || !data_k) return fail(BD_ERR_INVALID_ARG, "bd_kv_scatter: null K pointers");
+  if ((present_v == nullptr) != (data_v == nullptr))
+    return fail(BD_ERR_INVALID_ARG, "bd_kv_scatter: present_v and data_v must both be set or both NULL");
+  if (t < 0 || (int64_t)t + q > present_cap)
+    return fail(BD_ERR_INVALID_ARG, "bd_kv_scatter: window [t, t+q) = [%d, %d) outside present (cap %d)",
+                t, t + q, present_cap);
+  if (data_cap < q) return fail(BD_ERR_INVALID_ARG, "bd_kv_scatter: data_cap %d < q %d", data_cap, q);
+  if (n_rows > 65535 || n_layers * 2 > 65535)
+    return fail(BD_ERR_INVALID_ARG, "bd_kv_scatter: too many rows or layers for one launch");
+  if (!strides_ok(present_strides, 4, es) || !strides_ok(data_strides, 4, es))
+    return fail(BD_ERR_INVALID_ARG, "bd_kv_scatter: strides must be >= 0 and 16-byte multiples");
+  if (!aligned16(present_k) || !aligned16(data_k) || (present_v && (!aligned16(present_v) || !aligned16(data_v))))
+    return fail(BD_ERR_INVALID_ARG, "bd_kv_scatter: base pointers must be 16-byte aligned");
+  ScatterArgs a;
+  a.es = es; a.B = B; a.Hkv = Hkv; a.d = d; a.q = q; a.n_layers = n_layers; a.n_rows = n_rows;
+  a.t = t; a.present_cap = present_cap; a.data_cap = data_cap;
+  a.pk = (const char *)present_k; a.pv = (const char *)present_v;
+  a.dk = (char *)data_k; a.dv = (char *)data_v;
+  memcpy(a.ps, present_strides, sizeof(a.ps));
+  memcpy(a.ds, data_strides, sizeof(a.ds));
+  a.o = o; a.row_ids = row_ids;
+  return hip_status(launch_scatter(a, (hipStream_t)stream), "bd_kv_scatter launch");
+}
+
+int bd_gather(int dtype, int B, int Hkv, int d, const void *k_src, const void *v_src,
+              const int64_t src_strides[3], int src_cap, const int32_t *idx, int k_max,
+              const int32_t *k_cnt, void *k_pool, void *v_pool, const int64_t pool_strides[3],
+              int pool_cap, void *stream) {
+  g_err[0] = 0;
+  const int es = esize(dtype);
+  if (!es) return fail(BD_ERR_UNSUPPORTED, "bd_gather: unknown dtype %d", dtype);
+  if (B < 0 || Hkv <= 0 || d <= 0 || k_max < 0 || src_cap < 0)
+    return fail(BD_ERR_INVALID_ARG, "bd_gather: negative or zero size");
+  if (B == 0 || k_max == 0) return BD_OK;
+  if ((d * es) % 16 != 0)
+    return fail(BD_ERR_UNSUPPORTED, "bd_gather: d * element size must be a multiple of 16 bytes");
+  if (!k_src || !k_pool || !idx || !k_cnt || !src_strides || !pool_strides)
+    return fail(BD_ERR_INVALID_ARG, "bd_gather: null pointer");
+  if ((v_src == nullptr) != (v_pool == nullptr))
+    return fail(BD_ERR_INVALID_ARG, "bd_gather: v_src and v_pool must both be set or both NULL");
+  if (pool_cap < k_max) return fail(BD_ERR_INVALID_ARG, "bd_gather: pool_cap %d < k_max %d", pool_cap, k_max);
+  if ((int64_t)B * Hkv > 65535) return fail(BD_ERR_INVALID_ARG, "bd_gather: B * Hkv too large");
+  if (!strides_ok(src_strides, 3, es) || !strides_ok(pool_strides, 3, es))
+    return fail(BD_ERR_INVALID_ARG, "bd_gather: strides must be >= 0 and 16-byte multiples");
+  if (!aligned16(k_src) || !aligned16(k_pool) || (v_src && (!aligned16(v_src) || !aligned16(v_pool))))
+    return fail(BD_ERR_INVALID_ARG, "bd_gather: base pointers must be 16-byte aligned");
+  GatherArgs a;
+  a.es = es; a.B = B; a.Hkv = Hkv; a.d = d; a.src_cap = src_cap; a.k_max = k_max; a.pool_cap = pool_cap;
+  a.ks = (const char *)k_src; a.vs = (const char *)v_src;
+  a.kp = (char *)k_pool; a.vp = (char *)v_pool;
+  memcpy(a.ss, src_strides, sizeof(a.ss));
+  memcpy(a.pls, pool_strides, sizeof(a.pls));
+  a.idx = idx; a.k_cnt = k_cnt;
+  return hip_status(launch_gather(a, (hipStream_t)stream), "bd_gather launch");
+}
+
+size_t bd_select_workspace_size(int B, int Hq, int Hkv, int d, int s_max, int k_max) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || s_max < 0 || k_max < 0) return 0;
+  return select_workspace(B, Hq, Hkv, d, s_max, k_max);
+}
+
+int bd_select(int dtype, int B, int Hq, int Hkv, int d, const void *q, const int64_t q_strides[3],
+              int nq, int rep_mode, int rep_row, const void *k, const int64_t k_strides[3], int k_cap,
+              const int32_t *s_len, int s_max, const int32_t *k_sel, int k_max, float sm_scale,
+              int32_t *idx_out, float *score_out, void *workspace, size_t ws_bytes, void *stream) {
+  g_err[0] = 0;
+  if (dtype != BD_BF16) return fail(BD_ERR_UNSUPPORTED, "bd_select: only BD_BF16 is built");
+  if (d != 128) return fail(BD_ERR_UNSUPPORTED, "bd_select: only d == 128 is built");
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || s_max < 0 || k_max < 0 || k_cap < 0)
+    return fail(BD_ERR_INVALID_ARG, "bd_select: negative or zero size");
+  if (Hq % Hkv != 0) return fail(BD_ERR_INVALID_ARG, "bd_select: Hq %% Hkv != 0");
+  if (Hq / Hkv > 8 || Hq > 64) return fail(BD_ERR_UNSUPPORTED, "bd_select: needs Hq/Hkv <= 8 and Hq <= 64");
+  if (B == 0 || k_max == 0) return BD_OK;
+  if (!idx_out || !s_len || !k_sel) return fail(BD_ERR_INVALID_ARG, "bd_select: null pointer");
+  if (s_max > 0 && (!q || !k || !q_strides || !k_strides))
+    return fail(BD_ERR_INVALID_ARG, "bd_select: null pointer");
+  if (rep_mode != BD_REP_MEAN && rep_mode != BD_REP_ROW)
+    return fail(BD_ERR_INVALID_ARG, "bd_select: unknown rep_mode %d", rep_mode);
+  if (nq <= 0) return fail(BD_ERR_INVALID_ARG, "bd_select: nq must be positive");
+  if (rep_mode == BD_REP_ROW && (rep_row < 0 || rep_row >= nq))
+    return fail(BD_ERR_INVALID_ARG, "bd_select: rep_row %d outside [0, %d)", rep_row, nq);
+  if (!(sm_scale > 0.f) || sm_scale > 1e30f) return fail(BD_ERR_INVALID_ARG, "bd_select: bad sm_scale");
+  if ((int64_t)B * Hkv > 65535 || (int64_t)B * Hq > 65535 || B > 65535)
+    return fail(BD_ERR_INVALID_ARG, "bd_select: too many rows for one launch");
+  if (s_max > 0 && (!strides_ok(q_strides, 3, 2) || !strides_ok(k_strides, 3, 2) || !aligned16(q) || !aligned16(k)))
+    return fail(BD_ERR_INVALID_ARG, "bd_select: q/k must be 16-byte aligned with 16-byte stride multiples");
+  const size_t need = select_workspace(B, Hq, Hkv, d, s_max, k_max);
+  if (!workspace || ws_bytes < need)
+    return fail(BD_ERR_WORKSPACE, "bd_select: workspace %zu bytes, need %zu", ws_bytes, need);
+  if (((uintptr_t)workspace & 255u) != 0)
+    return fail(BD_ERR_WORKSPACE, "bd_select: workspace must be 256-byte aligned");
+  SelectArgs a;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.d = d; a.nq = nq; a.rep_mode = rep_mode;
+  a.rep_row = rep_row; a.k_cap = k_cap; a.s_max = s_max; a.k_max = k_max;
+  a.q = (const bf16 *)q; a.k = (const bf16 *)k;
+  for (int i = 0; i < 3; ++i) { a.qs[i] = q_strides ? q_strides[i] : 0; a.ks[i] = k_strides ? k_strides[i] : 0; }
+  a.s_len = s_len; a.k_sel = k_sel; a.scale2 = sm_scale * kLog2e;
+  a.idx_out = idx_out; a.score_out = score_out; a.ws = (char *)workspace;
+  return hip_status(launch_select(a, (hipStream_t)stream), "bd_select launch");
+}
+
+size_t bd_attn_workspace_size(int dtype, int B, int Hq, int Hkv, int d, int q, int n_rows, int p_max) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || q <= 0 || n_rows <= 0 || p_max < 0) return 0;
+  int chunk, n_split, nqt;
+  size_t ws;
+  attn_plan(dtype, B, Hq, Hkv, d, q, n_rows, p_max, &chunk, &n_split, &nqt, &ws);
+  return ws;
+}
+
+int bd_attn_packed(int dtype, int B, int Hq, int Hkv, int d, int q, int bl, const int32_t *row_ids,
+                   int n_rows, const void *q_ptr, const int64_t q_strides[3], const void *pk,
+                   const void *pv, const int64_t p_strides[3], int p_cap, const int32_t *p_len,
+                   int p_max, const void *wk, const void *wv, const int64_t w_strides[3],
+                   float sm_scale, void *out, const int64_t out_strides[3], float *lse,
+                   void *workspace, size_t ws_bytes, void *stream) {
+  g_err[0] = 0;
+  const int es = esize(dtype);
+  if (!es) return fail(BD_ERR_UNSUPPORTED, "bd_attn_packed: unknown dtype %d", dtype);
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || q < 0 || bl <= 0 || n_rows < 0 || p_cap < 0 || p_max < 0)
+    return fail(BD_ERR_INVALID_ARG, "bd_attn_packed: negative or zero size");
+  if (Hq % Hkv != 0) return fail(BD_ERR_INVALID_ARG, "bd_attn_packed: Hq %% Hkv != 0");
+  if (!row_ids && n_rows != B)
+    return fail(BD_ERR_INVALID_ARG, "bd_attn_packed: n_rows must equal B when row_ids is NULL");
+  const int G = Hq / Hkv;
+  if (!attn_mfma_supported(dtype, d, G) && !attn_generic_supported(dtype, d))
+    return fail(BD_ERR_UNSUPPORTED, "bd_attn_packed: dtype %d with d %d is not built", dtype, d);
+  if (B == 0 || n_rows == 0 || q == 0) return BD_OK;
+  if (!q_ptr || !wk || !wv || !out || !p_len || !q_strides || !w_strides || !out_strides || !p_strides)
+    return fail(BD_ERR_INVALID_ARG, "bd_attn_packed: null pointer");
+  if (p_max > 0 && (!pk || !pv)) return fail(BD_ERR_INVALID_ARG, "bd_attn_packed: null prefix pointers");
+  if (!(sm_scale > 0.f) || sm_scale > 1e30f) return fail(BD_ERR_INVALID_ARG, "bd_attn_packed: bad sm_scale");
+  if (!strides_ok(q_strides, 3, es) || !strides_ok(p_strides, 3, es) || !strides_ok(w_strides, 3, es) ||
+      !strides_ok(out_strides, 3, es))
+    return fail(BD_ERR_INVALID_ARG, "bd_attn_packed: strides must be >= 0 and 16-byte multiples");
+  if (!aligned16(q_ptr) || !aligned16(wk) || !aligned16(wv) || !aligned16(out) ||
+      (p_max > 0 && (!aligned16(pk) || !aligned16(pv))))
+    return fail(BD_ERR_INVALID_ARG, "bd_attn_packed: base pointers must be 16-byte aligned");
+  AttnArgs a;
+  a.dtype = dtype; a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.d = d; a.q = q; a.bl = bl;
+  a.n_rows = n_rows; a.p_cap = p_cap; a.p_max = p_max;
+  a.Q = q_ptr; a.pk = pk; a.pv = pv; a.wk = wk; a.wv = wv; a.out = out; a.lse = lse;
+  memcpy(a.qs, q_strides, sizeof(a.qs));
+  memcpy(a.ps, p_strides, sizeof(a.ps));
+  memcpy(a.ws, w_strides, sizeof(a.ws));
+  memcpy(a.os, out_strides, sizeof(a.os));
+  a.row_ids = row_ids; a.p_len = p_len; a.scale2 = sm_scale * kLog2e;
+  size_t need;
+  attn_plan(dtype, B, Hq, Hkv, d, q, n_rows, p_max, &a.chunk, &a.n_split, &a.nqt, &need);
+  const int64_t grid_units = (int64_t)n_rows * Hkv * a.nqt * a.n_split;
+  if (grid_units + 8 * (int64_t)a.nqt * a.n_split > ((int64_t)1 << 31) - 1)
+    return fail(BD_ERR_INVALID_ARG, "bd_attn_packed: problem too large for one launch");
+  a.part_o = a.part_ml = nullptr;
+  if (need > 0) {
+    if (!workspace || ws_bytes < need)
+      return fail(BD_ERR_WORKSPACE, "bd_attn_packed: workspace %zu bytes, need %zu", ws_bytes, need);
+    if (((uintptr_t)workspace & 255u) != 0)
+      return fail(BD_ERR_WORKSPACE, "bd_attn_packed: workspace must be 256-byte aligned");
+    const int64_t prows = (int64_t)n_rows * Hkv * a.nqt * a.n_split * G * 32;
+    a.part_o = (float *)workspace;
+    a.part_ml = (float *)((char *)workspace + align256((size_t)prows * d * sizeof(float)));
+  }
+  return hip_status(launch_attn(a, (hipStream_t)stream), "bd_attn_packed launch");
+}
+
+int bd_mask_materialize(int B, int C, int q, int bl, const int32_t *o, uint8_t *out, void *stream) {
+  g_err[0] = 0;
+  if (B < 0 || C < 0 || q < 0 || bl <= 0 || q > C)
+    return fail(BD_ERR_INVALID_ARG, "bd_mask_materialize: bad sizes");
+  if (B == 0 || C == 0 || q == 0) return BD_OK;
+  if (!o || !out) return fail(BD_ERR_INVALID_ARG, "bd_mask_materialize: null pointer");
+  if (B > 65535 || q > 65535) return fail(BD_ERR_INVALID_ARG, "bd_mask_materialize: too large");
+  return hip_status(launch_mask(B, C, q, bl, o, out, (hipStream_t)stream), "bd_mask_materialize launch");
+}
+
+}  // extern "C"

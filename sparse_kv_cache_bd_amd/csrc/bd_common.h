@@ -1,0 +1,122 @@
+// Internal definitions shared by the libbdattn sources (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bdattn.h"
+
+namespace bd {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Error reporting (thread-local message, defined in bd_api.hip).
+void set_error(const char *fmt, ...);
+
+// log2(e): the kernels evaluate exp(x) as exp2(x * log2(e)).
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// Visibility predicate of the per-row block-diagonal mask (FlowBlock review
+// Eq. (6)).  In window coordinates a query i sees window keys w < lim(i),
+// lim(i) = min(q, (floor(i/bl) + 1) * bl); every prefix key j < P_b is
+// visible.  The attention kernels and the mask test hook both call these.
+// ---------------------------------------------------------------------------
+__host__ __device__ inline int window_limit(int i, int bl, int q) {
+  int lim = (i / bl + 1) * bl;
+  return lim < q ? lim : q;
+}
+
+__host__ __device__ inline bool cache_visible(int i, int j, int ob, int t, int bl, int q) {
+  if (j < ob) return true;
+  return j >= t && (j - t) < window_limit(i, bl, q);
+}
+
+__host__ __device__ inline int clampi(int v, int lo, int hi) {
+  return v < lo ? lo : (v > hi ? hi : v);
+}
+
+__host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Exchange with lane l ^ 32 (the other half of the wave).
+__device__ inline float xor32(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  // lanes < 32 receive the upper half in r[1]; lanes >= 32 the lower half in r[0]
+  return (__lane_id() < 32) ? __uint_as_float(r[1]) : __uint_as_float(r[0]);
+}
+
+// ---------------------------------------------------------------------------
+// Kernel launchers (host side), one per operation.  Arguments are validated
+// by the public entry points before these are called.
+// ---------------------------------------------------------------------------
+struct ScatterArgs {
+  int es;  // element size in bytes
+  int B, Hkv, d, q, n_layers, n_rows, t, present_cap, data_cap;
+  const char *pk, *pv;
+  char *dk, *dv;
+  int64_t ps[4], ds[4];  // element strides {layer, row, pos, head}
+  const int32_t *o, *row_ids;
+};
+hipError_t launch_scatter(const ScatterArgs &a, hipStream_t s);
+
+struct GatherArgs {
+  int es;
+  int B, Hkv, d, src_cap, k_max, pool_cap;
+  const char *ks, *vs;
+  char *kp, *vp;
+  int64_t ss[3], pls[3];
+  const int32_t *idx, *k_cnt;
+};
+hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
+
+hipError_t launch_mask(int B, int C, int q, int bl, const int32_t *o, uint8_t *out,
+                       hipStream_t s);
+
+struct AttnArgs {
+  int dtype;  // BD_BF16 / BD_F32
+  int B, Hq, Hkv, G, d, q, bl, n_rows, p_cap, p_max;
+  const void *Q;
+  int64_t qs[3];
+  const void *pk, *pv;
+  int64_t ps[3];
+  const void *wk, *wv;
+  int64_t ws[3];
+  void *out;
+  int64_t os[3];
+  float *lse;
+  const int32_t *row_ids, *p_len;
+  float scale2;  // sm_scale * log2(e)
+  // split plan
+  int nqt, chunk, n_split;
+  float *part_o, *part_ml;
+};
+// Split plan: number of key chunks per (row, KV head, query tile) unit.
+void attn_plan(int dtype, int B, int Hq, int Hkv, int d, int q, int n_rows, int p_max,
+               int *chunk, int *n_split, int *nqt, size_t *ws_bytes);
+hipError_t launch_attn(const AttnArgs &a, hipStream_t s);
+bool attn_mfma_supported(int dtype, int d, int G);
+bool attn_generic_supported(int dtype, int d);
+
+struct SelectArgs {
+  int B, Hq, Hkv, G, d, nq, rep_mode, rep_row, k_cap, s_max, k_max;
+  const bf16 *q;
+  int64_t qs[3];
+  const bf16 *k;
+  int64_t ks[3];
+  const int32_t *s_len, *k_sel;
+  float scale2;
+  int32_t *idx_out;
+  float *score_out;
+  char *ws;
+};
+size_t select_workspace(int B, int Hq, int Hkv, int d, int s_max, int k_max);
+hipError_t launch_select(const SelectArgs &a, hipStream_t s);
+
+}  // namespace bd

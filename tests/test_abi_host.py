@@ -1,0 +1,181 @@
+"""Host-side tests of the C-ABI (no GPU needed).
+
+The library loads, exports every function the header declares, and every
+argument-validation path returns its documented status before any HIP
+call (so none of these calls launches anything).
+"""
+import ctypes
+
+import pytest
+
+from sparse_kv_cache_bd_amd import bdattn as bd
+
+I3 = ctypes.c_int64 * 3
+I4 = ctypes.c_int64 * 4
+FAKE = ctypes.c_void_p(0x100000)       # 16-byte aligned, never dereferenced
+FAKE2 = ctypes.c_void_p(0x200000)
+MISALIGNED = ctypes.c_void_p(0x100008)
+
+
+@pytest.fixture(scope="module")
+def L():
+    return bd.lib()
+
+
+def test_exports_every_header_function(L):
+    names = bd.header_functions()
+    assert len(names) == 9
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version(L):
+    assert bd.version().startswith("libbdattn")
+    assert "gfx950" in bd.version()
+
+
+def _scatter(L, **kw):
+    a = dict(dtype=bd.BD_BF16, B=2, Hkv=8, d=128, q=64, n_layers=1, pk=FAKE, pv=FAKE2,
+             ps=I4(0, 4096 * 1024, 1024, 128), pcap=4096, t=4032, dk=FAKE, dv=FAKE2,
+             ds=I4(0, 4096 * 1024, 1024, 128), dcap=4096, o=FAKE, rid=None, n_rows=2)
+    a.update(kw)
+    return L.bd_kv_scatter(a["dtype"], a["B"], a["Hkv"], a["d"], a["q"], a["n_layers"], a["pk"],
+                           a["pv"], a["ps"], a["pcap"], a["t"], a["dk"], a["dv"], a["ds"],
+                           a["dcap"], a["o"], a["rid"], a["n_rows"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), bd.BD_ERR_UNSUPPORTED),
+    (dict(Hkv=0), bd.BD_ERR_INVALID_ARG),
+    (dict(n_rows=1), bd.BD_ERR_INVALID_ARG),            # row_ids NULL needs n_rows == B
+    (dict(d=4), bd.BD_ERR_UNSUPPORTED),                 # 8-byte rows
+    (dict(o=None), bd.BD_ERR_INVALID_ARG),
+    (dict(pk=None), bd.BD_ERR_INVALID_ARG),
+    (dict(dv=None), bd.BD_ERR_INVALID_ARG),             # V pointers must pair up
+    (dict(t=4040), bd.BD_ERR_INVALID_ARG),              # window past present_cap
+    (dict(ps=I4(0, 4096 * 1024, 1023, 128)), bd.BD_ERR_INVALID_ARG),   # stride not 16 B
+    (dict(pk=MISALIGNED), bd.BD_ERR_INVALID_ARG),
+])
+def test_scatter_validation(L, kw, code):
+    assert _scatter(L, **kw) == code
+    assert bd.last_error().startswith("bd_kv_scatter")
+
+
+def test_scatter_empty_is_ok(L):
+    assert _scatter(L, B=0, n_rows=0) == bd.BD_OK
+    assert _scatter(L, q=0) == bd.BD_OK
+
+
+def _gather(L, **kw):
+    a = dict(dtype=bd.BD_BF16, B=2, Hkv=8, d=128, ks=FAKE, vs=FAKE2, ss=I3(1 << 20, 1024, 128),
+             scap=1000, idx=FAKE, kmax=64, kcnt=FAKE, kp=FAKE, vp=FAKE2, pls=I3(65536, 1024, 128),
+             pcap=64)
+    a.update(kw)
+    return L.bd_gather(a["dtype"], a["B"], a["Hkv"], a["d"], a["ks"], a["vs"], a["ss"], a["scap"],
+                       a["idx"], a["kmax"], a["kcnt"], a["kp"], a["vp"], a["pls"], a["pcap"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=-1), bd.BD_ERR_UNSUPPORTED),
+    (dict(idx=None), bd.BD_ERR_INVALID_ARG),
+    (dict(vp=None), bd.BD_ERR_INVALID_ARG),
+    (dict(pcap=63), bd.BD_ERR_INVALID_ARG),
+    (dict(ss=I3(1 << 20, 1025, 128)), bd.BD_ERR_INVALID_ARG),
+    (dict(kp=MISALIGNED), bd.BD_ERR_INVALID_ARG),
+    (dict(B=70000), bd.BD_ERR_INVALID_ARG),
+])
+def test_gather_validation(L, kw, code):
+    assert _gather(L, **kw) == code
+
+
+def _select(L, ws_bytes=None, **kw):
+    a = dict(dtype=bd.BD_BF16, B=2, Hq=32, Hkv=8, d=128, q=FAKE, qs=I3(32 * 4096, 4096, 128),
+             nq=32, mode=bd.BD_REP_MEAN, row=0, k=FAKE2, ks=I3(1 << 22, 1024, 128), kcap=4000,
+             s_len=FAKE, s_max=4000, k_sel=FAKE, k_max=200, scale=0.088, idx=FAKE, score=None,
+             ws=FAKE)
+    a.update(kw)
+    need = bd.select_workspace_size(a["B"], a["Hq"], a["Hkv"], a["d"], a["s_max"], a["k_max"])
+    wsb = need if ws_bytes is None else ws_bytes
+    return L.bd_select(a["dtype"], a["B"], a["Hq"], a["Hkv"], a["d"], a["q"], a["qs"], a["nq"],
+                       a["mode"], a["row"], a["k"], a["ks"], a["kcap"], a["s_len"], a["s_max"],
+                       a["k_sel"], a["k_max"], a["scale"], a["idx"], a["score"], a["ws"], wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=bd.BD_F32), bd.BD_ERR_UNSUPPORTED),
+    (dict(d=64), bd.BD_ERR_UNSUPPORTED),
+    (dict(Hq=30), bd.BD_ERR_INVALID_ARG),
+    (dict(Hq=128, Hkv=8), bd.BD_ERR_UNSUPPORTED),
+    (dict(mode=5), bd.BD_ERR_INVALID_ARG),
+    (dict(mode=bd.BD_REP_ROW, row=32), bd.BD_ERR_INVALID_ARG),
+    (dict(nq=0), bd.BD_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), bd.BD_ERR_INVALID_ARG),
+    (dict(scale=-1.0), bd.BD_ERR_INVALID_ARG),
+    (dict(idx=None), bd.BD_ERR_INVALID_ARG),
+    (dict(k=MISALIGNED), bd.BD_ERR_INVALID_ARG),
+    (dict(ws=None), bd.BD_ERR_WORKSPACE),
+    (dict(ws=ctypes.c_void_p(0x100010)), bd.BD_ERR_WORKSPACE),   # not 256-byte aligned
+])
+def test_select_validation(L, kw, code):
+    assert _select(L, **kw) == code
+
+
+def test_select_workspace_too_small(L):
+    need = bd.select_workspace_size(2, 32, 8, 128, 4000, 200)
+    assert need > 0
+    assert _select(L, ws_bytes=need - 1) == bd.BD_ERR_WORKSPACE
+    assert "need" in bd.last_error()
+
+
+def test_workspace_sizes_monotone():
+    a = bd.select_workspace_size(4, 32, 8, 128, 32768, 1638)
+    b = bd.select_workspace_size(4, 32, 8, 128, 65536, 1638)
+    assert 0 < a < b
+    # few units: the attention splits its prefix and needs a workspace
+    assert bd.attn_workspace_size(bd.BD_BF16, 1, 32, 8, 128, 32, 1, 6554) > 0
+    # many units: one chunk per unit, no workspace
+    assert bd.attn_workspace_size(bd.BD_BF16, 64, 32, 8, 128, 128, 64, 16384) == 0
+
+
+def _attn(L, ws_bytes=None, **kw):
+    a = dict(dtype=bd.BD_BF16, B=2, Hq=32, Hkv=8, d=128, q=64, bl=32, rid=None, n_rows=2,
+             Q=FAKE, qs=I3(64 * 4096, 4096, 128), pk=FAKE, pv=FAKE2, ps=I3(1 << 22, 1024, 128),
+             pcap=4096, plen=FAKE, pmax=4000, wk=FAKE, wv=FAKE2, wsd=I3(1 << 22, 1024, 128),
+             scale=0.088, out=FAKE2, os=I3(64 * 4096, 4096, 128), lse=None, ws=FAKE)
+    a.update(kw)
+    need = bd.attn_workspace_size(a["dtype"], a["B"], a["Hq"], a["Hkv"], a["d"], a["q"],
+                                  a["n_rows"], a["pmax"])
+    wsb = need if ws_bytes is None else ws_bytes
+    return L.bd_attn_packed(a["dtype"], a["B"], a["Hq"], a["Hkv"], a["d"], a["q"], a["bl"],
+                            a["rid"], a["n_rows"], a["Q"], a["qs"], a["pk"], a["pv"], a["ps"],
+                            a["pcap"], a["plen"], a["pmax"], a["wk"], a["wv"], a["wsd"],
+                            a["scale"], a["out"], a["os"], a["lse"], a["ws"], wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=3), bd.BD_ERR_UNSUPPORTED),
+    (dict(d=96), bd.BD_ERR_UNSUPPORTED),
+    (dict(Hq=33), bd.BD_ERR_INVALID_ARG),
+    (dict(bl=0), bd.BD_ERR_INVALID_ARG),
+    (dict(n_rows=1), bd.BD_ERR_INVALID_ARG),
+    (dict(plen=None), bd.BD_ERR_INVALID_ARG),
+    (dict(pk=None), bd.BD_ERR_INVALID_ARG),
+    (dict(wv=MISALIGNED), bd.BD_ERR_INVALID_ARG),
+    (dict(os=I3(64 * 4096, 4096, 129)), bd.BD_ERR_INVALID_ARG),
+    (dict(scale=0.0), bd.BD_ERR_INVALID_ARG),
+    (dict(ws=None), bd.BD_ERR_WORKSPACE),
+])
+def test_attn_validation(L, kw, code):
+    assert _attn(L, **kw) == code
+
+
+def test_attn_empty_is_ok(L):
+    assert _attn(L, B=0, n_rows=0) == bd.BD_OK
+    assert _attn(L, q=0) == bd.BD_OK
+
+
+def test_mask_validation(L):
+    assert L.bd_mask_materialize(2, 100, 200, 32, FAKE, FAKE2, None) == bd.BD_ERR_INVALID_ARG
+    assert L.bd_mask_materialize(2, 100, 64, 0, FAKE, FAKE2, None) == bd.BD_ERR_INVALID_ARG
+    assert L.bd_mask_materialize(2, 100, 64, 32, None, FAKE2, None) == bd.BD_ERR_INVALID_ARG
+    assert L.bd_mask_materialize(0, 100, 64, 32, None, None, None) == bd.BD_OK
