@@ -3,6 +3,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
+#include <stdint.h>
 
 #include "bd_common.h"
 
@@ -169,10 +170,7 @@ int bd_select(int dtype, int B, int Hq, int Hkv, int d, const void *q, const int
 
 size_t bd_attn_workspace_size(int dtype, int B, int Hq, int Hkv, int d, int q, int n_rows, int p_max) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || q <= 0 || n_rows <= 0 || p_max < 0) return 0;
-  int chunk, n_split, nqt;
-  size_t ws;
-  attn_plan(dtype, B, Hq, Hkv, d, q, n_rows, p_max, &chunk, &n_split, &nqt, &ws);
-  return ws;
+  return attn_plan(dtype, B, Hq, Hkv, d, q, n_rows, p_max).ws_bytes;
 }
 
 int bd_attn_packed(int dtype, int B, int Hq, int Hkv, int d, int q, int bl, const int32_t *row_ids,
@@ -203,6 +201,8 @@ int bd_attn_packed(int dtype, int B, int Hq, int Hkv, int d, int q, int bl, cons
   if (!aligned16(q_ptr) || !aligned16(wk) || !aligned16(wv) || !aligned16(out) ||
       (p_max > 0 && (!aligned16(pk) || !aligned16(pv))))
     return fail(BD_ERR_INVALID_ARG, "bd_attn_packed: base pointers must be 16-byte aligned");
+  if (p_strides[1] * es * 64 > INT32_MAX || w_strides[1] * es * 64 > INT32_MAX)
+    return fail(BD_ERR_INVALID_ARG, "bd_attn_packed: key row strides above 32 MB are not supported");
   AttnArgs a;
   a.dtype = dtype; a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.d = d; a.q = q; a.bl = bl;
   a.n_rows = n_rows; a.p_cap = p_cap; a.p_max = p_max;
@@ -212,20 +212,24 @@ int bd_attn_packed(int dtype, int B, int Hq, int Hkv, int d, int q, int bl, cons
   memcpy(a.ws, w_strides, sizeof(a.ws));
   memcpy(a.os, out_strides, sizeof(a.os));
   a.row_ids = row_ids; a.p_len = p_len; a.scale2 = sm_scale * kLog2e;
-  size_t need;
-  attn_plan(dtype, B, Hq, Hkv, d, q, n_rows, p_max, &a.chunk, &a.n_split, &a.nqt, &need);
-  const int64_t grid_units = (int64_t)n_rows * Hkv * a.nqt * a.n_split;
-  if (grid_units + 8 * (int64_t)a.nqt * a.n_split > ((int64_t)1 << 31) - 1)
+  const AttnPlan plan = attn_plan(dtype, B, Hq, Hkv, d, q, n_rows, p_max);
+  a.nw = plan.nw; a.nqt = plan.nqt; a.chunk = plan.chunk; a.n_split = plan.n_split;
+  const int64_t grid_units = (8 + (int64_t)n_rows * Hkv) * a.nqt * a.n_split;
+  if (grid_units > ((int64_t)1 << 31) - 1 || (int64_t)n_rows * Hq * a.nqt > ((int64_t)1 << 31) - 1)
     return fail(BD_ERR_INVALID_ARG, "bd_attn_packed: problem too large for one launch");
+  a.row_order = nullptr;
   a.part_o = a.part_ml = nullptr;
-  if (need > 0) {
-    if (!workspace || ws_bytes < need)
-      return fail(BD_ERR_WORKSPACE, "bd_attn_packed: workspace %zu bytes, need %zu", ws_bytes, need);
+  if (plan.ws_bytes > 0) {
+    if (!workspace || ws_bytes < plan.ws_bytes)
+      return fail(BD_ERR_WORKSPACE, "bd_attn_packed: workspace %zu bytes, need %zu", ws_bytes, plan.ws_bytes);
     if (((uintptr_t)workspace & 255u) != 0)
       return fail(BD_ERR_WORKSPACE, "bd_attn_packed: workspace must be 256-byte aligned");
-    const int64_t prows = (int64_t)n_rows * Hkv * a.nqt * a.n_split * G * 32;
-    a.part_o = (float *)workspace;
-    a.part_ml = (float *)((char *)workspace + align256((size_t)prows * d * sizeof(float)));
+    char *w = (char *)workspace;
+    if (plan.order) a.row_order = (int *)(w + plan.off_order);
+    if (plan.n_split > 1) {
+      a.part_o = (float *)(w + plan.off_part_o);
+      a.part_ml = (float *)(w + plan.off_part_ml);
+    }
   }
   return hip_status(launch_attn(a, (hipStream_t)stream), "bd_attn_packed launch");
 }

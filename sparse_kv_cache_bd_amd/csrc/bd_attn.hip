@@ -2,23 +2,37 @@
 // (FlowBlock review Eq. (6)); HERALD's denoising attention over a pool when
 // the prefix is a gathered pool.
 //
-// MFMA path (bf16, d = 128).  Work unit = (row, KV head h, tile of 32 window
-// queries, key chunk).  A 64-lane wave owns one query head of the GQA group,
-// so the G waves of a block share every K/V tile staged in LDS.  The wave
-// computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys on M, queries on
-// N): every lane then holds one query's scores, so the online softmax
-// (FlashAttention running max / sum) is lane-local apart from one exchange
-// with lane l^32.  O^T += V^T P^T reuses the S^T accumulator layout as the B
-// operand directly; V is staged transposed in LDS with the key order inside
-// each 16-key group permuted to match that layout.
+// MFMA path (bf16, d = 128).  A block of NW = 8 waves (two per SIMD, so
+// one wave's softmax overlaps the other's MFMAs) owns one (row, KV head,
+// query tile, key chunk) work item; 4-wave blocks serve small GQA windows.
+// The tile's columns are (query, query head) pairs of the GQA group, 32 per
+// wave.  Every column of a block sees the same prefix keys, so one K/V tile
+// staged in LDS serves all of them.
 //
-// All prefix keys are visible to every query, so the only masked tiles are
-// the ragged prefix end and the window part; keys at or past the prefix
-// length are never loaded (zero-filled in LDS), which keeps NaN sentinels in
-// unused cache rows out of the arithmetic.
+// Per 64-key tile a wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
+// (keys on M, columns on N): a lane then holds 16 scores of one column, so
+// the online softmax (FlashAttention running max / sum) is lane-local, with
+// one exchange with lane l^32 for the column max.  O^T += V^T P^T takes the
+// S^T accumulator registers directly as the B operand; V is staged
+// transposed in LDS with the key order inside each 16-key group permuted to
+// match.  The running max is only raised when a tile's max exceeds it by
+// more than 2^8 (the result is the same for any reference value; p stays
+// <= 256), so the O rescale runs on few tiles.
 //
-// Split-KV: when there are too few units to fill the 256 CUs, the prefix is
-// cut into chunks; each chunk writes unnormalised partial O with its running
+// Pipelining: K and V tiles are double-buffered in LDS with one barrier per
+// tile; the global loads of tile t+1 are issued before the MFMAs of tile t
+// and written to LDS after them.  Inside a tile the exponentials of the
+// second 32-key half are independent of the P V MFMAs of the first half.
+//
+// Rows at or past the prefix length are never read (the buffer range check
+// returns zeros for them, and their scores are masked), which keeps NaN
+// sentinels in unused rows out of the arithmetic.
+//
+// Scheduling: with more work items than the GPU holds at once, a planner
+// kernel ranks the rows by prefix length and blocks take rows longest first
+// (LPT order).  The items of one (row, KV head) go to the same XCD, so its
+// K/V come from HBM into that XCD's L2 once.  With few items the prefix is
+// cut into chunks; each chunk writes unnormalised partial O with its
 // (max, sum), and a combine kernel merges the chunks in a fixed order.
 #include "bd_common.h"
 
@@ -27,11 +41,13 @@ namespace bd {
 namespace {
 
 // ----------------------------------------------------------------- MFMA path
-constexpr int kD = 128;          // head dim of the MFMA path
-constexpr int kTileK = 64;       // keys per staged tile
-constexpr int kQT = 32;          // queries per tile (MFMA N)
-constexpr int kKStr = kD + 8;    // LDS row stride of K (elements): 272 B
-constexpr int kVStr = kTileK + 8;  // LDS row stride of V^T (elements): 144 B
+constexpr int kD = 128;            // head dim of the MFMA path
+constexpr int kTK = 64;            // keys per staged tile
+constexpr int kKStr = kD + 8;      // LDS row stride of K (elements): 272 B
+constexpr int kVStr = kTK + 8;     // LDS row stride of V^T (elements): 144 B
+constexpr int kKTile = kTK * kKStr;
+constexpr int kVTile = kD * kVStr;
+constexpr float kRescaleSlack = 8.f;  // log2 units
 
 __device__ inline bf16x8 ld_bf16x8(const bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 
@@ -42,188 +58,275 @@ __device__ inline int vt_slot(int k16) {
   return (k16 & 3) | ((k16 & 4) << 1) | ((k16 & 8) >> 1);
 }
 
-template <int G>
-__global__ __launch_bounds__(64 * G) void attn_mfma_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16 Ks[kTileK * kKStr];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[kD * kVStr];
+// Block of NW waves, one 32-column group per wave; two waves share a SIMD.
+// Tile staging: 256 V items (4 keys x 8 dims) and 1024 K pieces (16 bytes)
+// per 64-key tile.  With 8 waves, waves 0-3 stage V and waves 4-7 stage K
+// (4 loads per thread each); with 4 waves every thread stages 1 V item and
+// 4 K pieces.
+template <int NW, int G>
+struct Shape {
+  static constexpr int NT = 64 * NW;           // threads
+  static constexpr int NCG = NW;               // 32-column groups per block
+  static constexpr int QB = NCG / G;           // 32-query blocks per block
+  static constexpr int NQ = 32 * QB;           // queries per block
+  static constexpr int NCOL = 32 * NCG;        // columns per block
+  static constexpr bool SPLIT_STAGE = NW == 8;
+  static constexpr int KP = SPLIT_STAGE ? 4 : kTK * 16 / NT;  // K pieces per staging thread
+  static constexpr int VI = 1;                 // V items per staging thread
+  static_assert(QB >= 1 && NCG % G == 0, "GQA group larger than the block");
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+};
 
-  constexpr int NT = 64 * G;
+// Decoded work item of a block.
+struct Item {
+  int b, h, rl, u, c, nc;
+  int kbeg, kend;     // prefix keys of this chunk
+  bool with_window;   // last chunk also covers the window
+};
+
+__device__ inline bool decode_item(const AttnArgs &a, int bid, Item &it) {
+  const int per_group = a.nqt * a.n_split;
+  const int xcd = bid & 7;
+  const int sigma = bid >> 3;
+  const int gamma = xcd + 8 * (sigma / per_group);
+  if (gamma >= a.n_rows * a.Hkv) return false;
+  const int mem = sigma - (sigma / per_group) * per_group;
+  it.u = mem / a.n_split;
+  it.c = mem - it.u * a.n_split;
+  const int rank = gamma / a.Hkv;
+  it.h = gamma - rank * a.Hkv;
+  it.rl = a.row_order ? a.row_order[rank] : rank;
+  it.b = a.row_ids ? a.row_ids[it.rl] : it.rl;
+  if (it.b < 0 || it.b >= a.B) return false;
+  const int P = clampi(a.p_len[it.b], 0, min(a.p_max, a.p_cap));
+  it.nc = P > 0 ? (int)cdiv(P, a.chunk) : 1;
+  if (it.c >= it.nc) return false;
+  it.kbeg = it.c * a.chunk;
+  it.kend = min(P, it.kbeg + a.chunk);
+  it.with_window = (it.c == it.nc - 1);
+  return true;
+}
+
+template <int NW, int G>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) {
+  using S = Shape<NW, G>;
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2][kKTile];
+  __shared__ __attribute__((aligned(16))) bf16 Vt[2][kVTile];
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int hh = lane >> 5;     // lane half
-  const int ln = lane & 31;     // query column / M row inside a 32x32 tile
+  const int hh = lane >> 5;  // lane half
+  const int ln = lane & 31;  // column / M row inside a 32x32 tile
 
-  // ---- decode the unit (XCD-aware: the units of one (row, KV head) group
-  // are dispatched to the same XCD so its K/V stay in that XCD's L2)
-  const int per_group = a.nqt * a.n_split;
-  const int n_groups = a.n_rows * a.Hkv;
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7;
-  const int kk = bid >> 3;
-  const int group = xcd + 8 * (kk / per_group);
-  if (group >= n_groups) return;
-  const int mem = kk % per_group;
-  const int u = mem / a.n_split;
-  const int c = mem - u * a.n_split;
-  const int rl = group / a.Hkv;
-  const int h = group - rl * a.Hkv;
-  const int b = a.row_ids ? a.row_ids[rl] : rl;
-  if (b < 0 || b >= a.B) return;
-  const int P = clampi(a.p_len[b], 0, min(a.p_max, a.p_cap));
-  const int nc = P > 0 ? (int)cdiv(P, a.chunk) : 1;
-  if (c >= nc) return;
-  const int kbeg = c * a.chunk;
-  const int kend = min(P, kbeg + a.chunk);
-  const bool with_window = (c == nc - 1);
-  const int i0 = u * kQT;
-  const int ilast = min(i0 + kQT, a.q) - 1;
+  Item it;
+  if (!decode_item(a, blockIdx.x, it)) return;
+  const int b = it.b, h = it.h;
+  const int i0 = it.u * S::NQ;
+  const int ilast = min(i0 + S::NQ, a.q) - 1;
   const int win_len = window_limit(ilast, a.bl, a.q);
-  const int hq = h * G + wave;
-  const int qi = i0 + ln;              // this lane's query
-  const bool q_ok = qi < a.q;
-  const int lim_i = window_limit(q_ok ? qi : ilast, a.bl, a.q);
+  const int n_pref = it.kend > it.kbeg ? (int)cdiv(it.kend - it.kbeg, kTK) : 0;
+  const int n_tiles = n_pref + (it.with_window ? (int)cdiv(win_len, kTK) : 0);
 
-  // ---- Q operand (B of S^T = K Q^T): lane holds Q[qi][ks*16 + hh*8 .. +8]
+  // ---- this wave's column group: one query head, 32 queries
+  const int g = wave / S::QB;
+  const int qb = wave - g * S::QB;
+  const int hq = h * G + g;
+  const int qi = i0 + qb * 32 + ln;
+  const bool qok = qi < a.q;
+  const int lim = window_limit(qok ? qi : ilast, a.bl, a.q);
+
+  // ---- Q operands (B of S^T = K Q^T): lane holds Q[qi][ks*16 + hh*8 .. +8]
   bf16x8 qop[kD / 16];
   {
     const bf16 *qp = reinterpret_cast<const bf16 *>(a.Q) + (int64_t)b * a.qs[0] +
-                     (int64_t)qi * a.qs[1] + (int64_t)hq * a.qs[2] + hh * 8;
+                     (int64_t)(qok ? qi : 0) * a.qs[1] + (int64_t)hq * a.qs[2] + hh * 8;
 #pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks) {
-      if (q_ok)
-        qop[ks] = ld_bf16x8(qp + ks * 16);
-      else
-        qop[ks] = bf16x8{};
-    }
+    for (int ks = 0; ks < kD / 16; ++ks) qop[ks] = qok ? ld_bf16x8(qp + ks * 16) : bf16x8{};
   }
-
-  f32x16 acc_o[kD / 32];
-#pragma unroll
-  for (int dt = 0; dt < kD / 32; ++dt) acc_o[dt] = f32x16{};
-  float m_run = -INFINITY;  // running max of scaled scores (log2 units)
-  float l_run = 0.f;        // running sum of exp2(score - m_run)
 
   const bf16 *pkb = reinterpret_cast<const bf16 *>(a.pk) + (int64_t)b * a.ps[0] + (int64_t)h * a.ps[2];
   const bf16 *pvb = reinterpret_cast<const bf16 *>(a.pv) + (int64_t)b * a.ps[0] + (int64_t)h * a.ps[2];
   const bf16 *wkb = reinterpret_cast<const bf16 *>(a.wk) + (int64_t)b * a.ws[0] + (int64_t)h * a.ws[2];
   const bf16 *wvb = reinterpret_cast<const bf16 *>(a.wv) + (int64_t)b * a.ws[0] + (int64_t)h * a.ws[2];
 
-  const int n_pref_tiles = (kend > kbeg) ? (int)cdiv(kend - kbeg, kTileK) : 0;
-  const int n_win_tiles = with_window ? (int)cdiv(win_len, kTileK) : 0;
-  const int n_tiles = n_pref_tiles + n_win_tiles;
+  // tile tt: first key, end of the valid keys, source (prefix or window)
+  auto tile_base = [&](int tt) { return tt < n_pref ? it.kbeg + tt * kTK : (tt - n_pref) * kTK; };
+  auto tile_limit = [&](int tt) { return tt < n_pref ? it.kend : win_len; };
 
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const bool win = tile >= n_pref_tiles;
-    const int base = win ? (tile - n_pref_tiles) * kTileK : kbeg + tile * kTileK;
-    const int limit = win ? win_len : kend;
-    const bf16 *kb = win ? wkb : pkb;
-    const bf16 *vb = win ? wvb : pvb;
+  // ---- staging: global -> registers -> LDS with buffer loads.  Each tile
+  // gets a buffer resource based at its first key whose size ends at the
+  // tile's last valid key, so rows at or past the limit read as zeros (the
+  // hardware range check) and unused rows are never touched.  Offsets are
+  // 32-bit: one tile spans at most kTK rows (the host checks the row
+  // strides).
+  // K piece: key piece / 16, dims 8 * (piece % 16): 16 lanes read one
+  // 256-byte key row.  V item: keys 4*k4 .. 4*k4+3 with k4 = tid % 16 and
+  // dims 8 * (tid / 16 % 16): the 16 lanes of a write pass hold the 16
+  // key-quads of one dim chunk, so each transposed write pass fills one
+  // 128-byte V^T row.
+  const bool stage_v = !S::SPLIT_STAGE || wave < 4;
+  const bool stage_k = !S::SPLIT_STAGE || wave >= 4;
+  const int ktid = S::SPLIT_STAGE ? tid - 256 : tid;   // K staging thread index
+  const int kstep = S::SPLIT_STAGE ? 256 : S::NT;
+  bf16x8 kreg[S::KP];
+  bf16x8 vreg[4];
+  auto rsrc = [](const bf16 *p, int64_t row_el, int base, int limit) {
+    const int64_t rowb = row_el * 2;
+    const int rows = min(limit - base, kTK);
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(p + (int64_t)base * row_el), (short)0,
+                                             (int)(rows * rowb), 0x00020000);
+  };
+  // Byte offsets of the loads in flight; kept live until the LDS stores
+  // (keep_offsets) so that no later instruction reuses their registers while
+  // the loads are outstanding, which would make the compiler wait for them.
+  int koff[S::KP], voff[4];
+  auto load = [&](int tt) {
+    const bool win = tt >= n_pref;
     const int64_t sp = win ? a.ws[1] : a.ps[1];
-
-    __syncthreads();  // previous tile fully consumed
-    // ---- stage K [64 keys][128 d] row-major, 16 lanes per key row
-    for (int piece = tid; piece < kTileK * 16; piece += NT) {
-      const int key = piece >> 4;
-      const int ch = piece & 15;
-      const int gk = base + key;
-      bf16x8 v = bf16x8{};
-      if (gk < limit) v = ld_bf16x8(kb + (int64_t)gk * sp + ch * 8);
-      *reinterpret_cast<bf16x8 *>(&Ks[key * kKStr + ch * 8]) = v;
-    }
-    // ---- stage V transposed: V^T[d][slot(key)], 4 keys x 8 d per item
-    for (int item = tid; item < (kTileK / 4) * (kD / 8); item += NT) {
-      const int db = item & 15;
-      const int kb4 = item >> 4;  // keys 4*kb4 .. 4*kb4+3
-      bf16x8 v[4];
+    const int rowb = (int)(sp * 2);
+    const int base = tile_base(tt), limit = tile_limit(tt);
+    if (stage_k) {
+      const auto r = rsrc(win ? wkb : pkb, sp, base, limit);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int gk = base + 4 * kb4 + j;
-        v[j] = (gk < limit) ? ld_bf16x8(vb + (int64_t)gk * sp + db * 8) : bf16x8{};
+      for (int p = 0; p < S::KP; ++p) {
+        const int piece = ktid + p * kstep;
+        koff[p] = (piece >> 4) * rowb + (piece & 15) * 16;
+        kreg[p] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, koff[p], 0, 0));
       }
-      const int slot = (kb4 >> 2) * 16 + vt_slot((kb4 & 3) * 4);
+    }
+    if (stage_v) {
+      const auto r = rsrc(win ? wvb : pvb, sp, base, limit);
+      const int k4 = tid & 15, db = (tid >> 4) & 15;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        voff[jj] = (4 * k4 + jj) * rowb + db * 16;
+        vreg[jj] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff[jj], 0, 0));
+      }
+    }
+  };
+  auto keep_offsets = [&]() {
+#pragma unroll
+    for (int p = 0; p < S::KP; ++p) asm volatile("" ::"v"(koff[p]));
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) asm volatile("" ::"v"(voff[jj]));
+  };
+  auto store = [&](int buf) {
+    if (stage_k) {
+#pragma unroll
+      for (int p = 0; p < S::KP; ++p) {
+        const int piece = ktid + p * kstep;
+        *reinterpret_cast<bf16x8 *>(&Ks[buf][(piece >> 4) * kKStr + (piece & 15) * 8]) = kreg[p];
+      }
+    }
+    if (stage_v) {
+      const int k4 = tid & 15, db = (tid >> 4) & 15;
+      const int slot = (k4 >> 2) * 16 + vt_slot((k4 & 3) * 4);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        bf16x4 w = {v[0][e], v[1][e], v[2][e], v[3][e]};
-        *reinterpret_cast<bf16x4 *>(&Vt[(db * 8 + e) * kVStr + slot]) = w;
+        bf16x4 w = {vreg[0][e], vreg[1][e], vreg[2][e], vreg[3][e]};
+        *reinterpret_cast<bf16x4 *>(&Vt[buf][(db * 8 + e) * kVStr + slot]) = w;
       }
     }
-    __syncthreads();
+  };
 
-    // ---- S^T = K Q^T for two 32-key sub-tiles
+  f32x16 acc[kD / 32];
+#pragma unroll
+  for (int dt = 0; dt < kD / 32; ++dt) acc[dt] = f32x16{};
+  float m_run = -INFINITY;  // reference max of scaled scores (log2 units)
+  float l_run = 0.f;        // this lane's share of sum exp2(score - m_run)
+
+  // ---- one tile: S^T = K Q^T, softmax, O^T += V^T P^T
+  auto tile = [&](int tt, int buf) {
     f32x16 s[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       s[kt] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < kD / 16; ++ks) {
-        const bf16x8 kop = ld_bf16x8(&Ks[(kt * 32 + ln) * kKStr + ks * 16 + hh * 8]);
+        const bf16x8 kop = ld_bf16x8(&Ks[buf][(kt * 32 + ln) * kKStr + ks * 16 + hh * 8]);
         s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], s[kt], 0, 0, 0);
       }
     }
-
-    // ---- mask, scale, online softmax (lane = query column)
-    const int vlim = win ? lim_i : limit;
-    float mx = -INFINITY;
+    const int base = tile_base(tt), limit = tile_limit(tt);
+    const bool win = tt >= n_pref;
+    if (win || base + kTK > limit) {
+      const int vlim = win ? lim : limit;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = base + kt * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-        const float v = (key < vlim) ? s[kt][r] * a.scale2 : -INFINITY;
-        s[kt][r] = v;
-        mx = fmaxf(mx, v);
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int key = base + kt * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+          if (key >= vlim) s[kt][r] = -INFINITY;
+        }
     }
-    mx = fmaxf(mx, xor32(mx));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    float rs = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(s[kt][r] - m_use);
-        s[kt][r] = p;
-        rs += p;
-      }
-    }
-    rs += xor32(rs);
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < kD / 32; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc_o[dt][r] *= alpha;
-
-    // ---- P^T operands: registers 8k..8k+7 of s[kt] -> keys of k-step (kt, k)
-    bf16x8 pop[2][2];
+    // column max of the tile; the reference max is raised only when the
+    // tile's max exceeds it by more than 2^8
+    float mx = s[0][0];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+    mx = fmaxf(mx, xor32(mx)) * a.scale2;
+    const bool up = mx > m_run + kRescaleSlack;
+    if (__ballot(up)) {
+      const float m_new = up ? mx : m_run;
+      const float alpha = up ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pop[kt][k2][e] = (bf16)s[kt][8 * k2 + e];
-
-    // ---- O^T += V^T P^T
+      for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < kD / 32; ++dt) {
+        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+    }
+    const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < 2; ++kt) {
+      // p = exp2(score * scale2 - m); masked scores are -inf and give 0
+      bf16x8 pop[2];
+      float rs = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], a.scale2, neg_m));
+        rs += p;
+        pop[r >> 3][r & 7] = (bf16)p;
+      }
+      l_run += rs;
+#pragma unroll
+      for (int dt = 0; dt < kD / 32; ++dt) {
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
-          const bf16x8 vop =
-              ld_bf16x8(&Vt[(dt * 32 + ln) * kVStr + kt * 32 + k2 * 16 + hh * 8]);
-          acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[kt][k2], acc_o[dt], 0, 0, 0);
+          const bf16x8 vop = ld_bf16x8(&Vt[buf][(dt * 32 + ln) * kVStr + kt * 32 + k2 * 16 + hh * 8]);
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[k2], acc[dt], 0, 0, 0);
         }
       }
     }
+  };
+
+  // ---- tile loop: tile tt+1 is loaded during tile tt (double-buffered LDS)
+  if (n_tiles > 0) {
+    load(0);
+    store(0);
+  }
+  // every load issued so far (Q, tile 0) has landed: the loop below then
+  // only waits for its own prefetches, at the LDS stores
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int tt = 0; tt < n_tiles; ++tt) {
+    const bool more = tt + 1 < n_tiles;
+    if (more) load(tt + 1);
+    tile(tt, tt & 1);
+    if (more) {
+      store((tt + 1) & 1);
+      keep_offsets();
+    }
+    __syncthreads();
   }
 
   // ---- epilogue
-  if (!q_ok) return;
-  if (nc == 1) {
+  l_run += xor32(l_run);
+  if (it.nc == 1) {
+    if (!qok) return;
     const float inv = 1.f / l_run;
     bf16 *op = reinterpret_cast<bf16 *>(a.out) + (int64_t)b * a.os[0] + (int64_t)qi * a.os[1] +
                (int64_t)hq * a.os[2];
@@ -233,22 +336,23 @@ __global__ __launch_bounds__(64 * G) void attn_mfma_kernel(AttnArgs a) {
       for (int rq = 0; rq < 4; ++rq) {
         bf16x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc_o[dt][rq * 4 + e] * inv);
+        for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[dt][rq * 4 + e] * inv);
         *reinterpret_cast<bf16x4 *>(op + dt * 32 + rq * 8 + hh * 4) = w;
       }
     }
     if (a.lse && hh == 0)
       a.lse[((int64_t)b * a.Hq + hq) * a.q + qi] = (m_run + __log2f(l_run)) * kLn2;
   } else {
-    const int64_t unit = (int64_t)group * a.nqt + u;
-    const int64_t prow = ((unit * a.n_split + c) * G + wave) * kQT + ln;
+    // partial rows [unit][chunk][column], unit = (natural row, KV head, query tile)
+    const int64_t unit = ((int64_t)it.rl * a.Hkv + h) * a.nqt + it.u;
+    const int col = wave * 32 + ln;
+    const int64_t prow = (unit * a.n_split + it.c) * S::NCOL + col;
     float *po = a.part_o + prow * kD;
 #pragma unroll
     for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        f32x4 w = {acc_o[dt][rq * 4 + 0], acc_o[dt][rq * 4 + 1], acc_o[dt][rq * 4 + 2],
-                   acc_o[dt][rq * 4 + 3]};
+        f32x4 w = {acc[dt][rq * 4 + 0], acc[dt][rq * 4 + 1], acc[dt][rq * 4 + 2], acc[dt][rq * 4 + 3]};
         *reinterpret_cast<f32x4 *>(po + dt * 32 + rq * 8 + hh * 4) = w;
       }
     if (hh == 0) {
@@ -258,49 +362,72 @@ __global__ __launch_bounds__(64 * G) void attn_mfma_kernel(AttnArgs a) {
   }
 }
 
-// Merge split-KV partials of one unit (row, KV head, query tile): fixed chunk
-// order, so the result does not depend on scheduling.
-template <typename T>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int D) {
-  const int unit = blockIdx.x;
-  const int group = unit / a.nqt;
-  const int u = unit - group * a.nqt;
-  const int rl = group / a.Hkv;
-  const int h = group - rl * a.Hkv;
+// Merge the split-KV partials: one thread per (column, 4 dims), chunks in a
+// fixed order, so the result does not depend on scheduling.
+template <int NW, int G>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+  using S = Shape<NW, G>;
+  constexpr int CPB = 256 / (kD / 4);  // columns per block: 8
+  const int blocks_per_unit = S::NCOL / CPB;
+  const int64_t unit = blockIdx.x / blocks_per_unit;
+  const int col = (blockIdx.x - unit * blocks_per_unit) * CPB + threadIdx.x / (kD / 4);
+  const int d4 = threadIdx.x % (kD / 4);
+  const int u = (int)(unit % a.nqt);
+  const int64_t group = unit / a.nqt;
+  const int rl = (int)(group / a.Hkv);
+  const int h = (int)(group - (int64_t)rl * a.Hkv);
   const int b = a.row_ids ? a.row_ids[rl] : rl;
   if (b < 0 || b >= a.B) return;
   const int P = clampi(a.p_len[b], 0, min(a.p_max, a.p_cap));
   const int nc = P > 0 ? (int)cdiv(P, a.chunk) : 1;
   if (nc == 1) return;  // written directly by the attention kernel
-  const int rows = a.G * kQT;
-  for (int item = threadIdx.x; item < rows * (D / 4); item += blockDim.x) {
-    const int row = item / (D / 4);
-    const int d4 = item - row * (D / 4);
-    const int g = row / kQT;
-    const int il = row - g * kQT;
-    const int qi = u * kQT + il;
-    if (qi >= a.q) continue;
-    float M = -INFINITY;
-    for (int cc = 0; cc < nc; ++cc) {
-      const int64_t prow = (((int64_t)unit * a.n_split + cc) * a.G + g) * kQT + il;
-      M = fmaxf(M, a.part_ml[prow * 2]);
-    }
-    float L = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int cc = 0; cc < nc; ++cc) {
-      const int64_t prow = (((int64_t)unit * a.n_split + cc) * a.G + g) * kQT + il;
-      const float w = __builtin_amdgcn_exp2f(a.part_ml[prow * 2] - M);
-      L += a.part_ml[prow * 2 + 1] * w;
-      const f32x4 po = *reinterpret_cast<const f32x4 *>(a.part_o + prow * D + d4 * 4);
-      acc += po * w;
-    }
-    const float inv = 1.f / L;
-    const int hq = h * a.G + g;
-    T *op = reinterpret_cast<T *>(a.out) + (int64_t)b * a.os[0] + (int64_t)qi * a.os[1] +
-            (int64_t)hq * a.os[2] + d4 * 4;
+  const int cg = col / 32;
+  const int g = cg / S::QB;
+  const int qb = cg - g * S::QB;
+  const int qi = u * S::NQ + qb * 32 + (col & 31);
+  if (qi >= a.q) return;
+  const int64_t prow0 = unit * a.n_split * S::NCOL + col;
+  float M = -INFINITY;
+  for (int cc = 0; cc < nc; ++cc) M = fmaxf(M, a.part_ml[(prow0 + (int64_t)cc * S::NCOL) * 2]);
+  float L = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int cc = 0; cc < nc; ++cc) {
+    const int64_t prow = prow0 + (int64_t)cc * S::NCOL;
+    const float w = __builtin_amdgcn_exp2f(a.part_ml[prow * 2] - M);
+    L += a.part_ml[prow * 2 + 1] * w;
+    const f32x4 po = *reinterpret_cast<const f32x4 *>(a.part_o + prow * kD + d4 * 4);
+    acc += po * w;
+  }
+  const float inv = 1.f / L;
+  const int hq = h * G + g;
+  bf16 *op = reinterpret_cast<bf16 *>(a.out) + (int64_t)b * a.os[0] + (int64_t)qi * a.os[1] +
+             (int64_t)hq * a.os[2] + d4 * 4;
+  bf16x4 w4;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) op[e] = (T)(acc[e] * inv);
-    if (a.lse && d4 == 0) a.lse[((int64_t)b * a.Hq + hq) * a.q + qi] = (M + __log2f(L)) * kLn2;
+  for (int e = 0; e < 4; ++e) w4[e] = (bf16)(acc[e] * inv);
+  *reinterpret_cast<bf16x4 *>(op) = w4;
+  if (a.lse && d4 == 0) a.lse[((int64_t)b * a.Hq + hq) * a.q + qi] = (M + __log2f(L)) * kLn2;
+}
+
+// Rank the listed rows by prefix length, longest first (ties by list
+// position), so that blocks start on the longest rows.  One block.
+constexpr int kOrderMax = 1024;
+__global__ __launch_bounds__(1024) void attn_order_kernel(AttnArgs a) {
+  __shared__ int len[kOrderMax];
+  const int n = a.n_rows;
+  for (int r = threadIdx.x; r < n; r += blockDim.x) {
+    const int b = a.row_ids ? a.row_ids[r] : r;
+    len[r] = (b < 0 || b >= a.B) ? -1 : clampi(a.p_len[b], 0, min(a.p_max, a.p_cap));
+  }
+  __syncthreads();
+  for (int r = threadIdx.x; r < n; r += blockDim.x) {
+    const int lr = len[r];
+    int rank = 0;
+    for (int r2 = 0; r2 < n; ++r2) {
+      const int l2 = len[r2];
+      rank += (l2 > lr) || (l2 == lr && r2 < r);
+    }
+    a.row_order[rank] = r;
   }
 }
 
@@ -309,6 +436,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int D) {
 // lane owning D/8 dimensions.  fp32 arithmetic throughout; used for fp32
 // inputs and for shapes the MFMA path is not built for.
 constexpr int kGenKeys = 32;
+constexpr int kQT = 32;  // queries per block
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a) {
@@ -404,51 +532,96 @@ bool attn_generic_supported(int dtype, int d) {
   return (dtype == BD_BF16 || dtype == BD_F32) && (d == 64 || d == 128);
 }
 
-void attn_plan(int dtype, int B, int Hq, int Hkv, int d, int q, int n_rows, int p_max,
-               int *chunk, int *n_split, int *nqt, size_t *ws_bytes) {
+// Plan of the MFMA path.  Blocks of 4 waves serve GQA groups of at most 4
+// when one query tile of 4 waves covers every query (q * G <= 128);
+// otherwise 8 waves.  The prefix is cut into chunks only while there are
+// fewer blocks than block slots on the GPU (one 8-wave or two 4-wave blocks
+// per CU), and
+// never below kMinChunk keys: each extra chunk costs a partial O row of
+// 512 bytes per column.  Rows are ordered longest first when the blocks do
+// not all fit at once.
+constexpr int kCUs = 256;
+constexpr int kMinChunk = 512;
+
+AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int d, int q, int n_rows, int p_max) {
   (void)B;
+  AttnPlan p{};
   const int G = Hkv > 0 ? Hq / Hkv : 1;
-  *nqt = (int)cdiv(q, kQT);
-  *chunk = 1 << 30;
-  *n_split = 1;
-  *ws_bytes = 0;
-  if (!attn_mfma_supported(dtype, d, G) || p_max <= 0) return;
-  const int64_t units = (int64_t)n_rows * Hkv * (*nqt);
-  const int64_t target = 1024;  // blocks wanted to fill 256 CUs a few times
-  if (units >= target / 2) return;
-  int64_t want = cdiv(target, units);
-  const int64_t max_split = cdiv(p_max, kTileK);
-  if (want > max_split) want = max_split;
-  if (want <= 1) return;
-  int64_t ch = cdiv(cdiv(p_max, want), kTileK) * kTileK;
-  *chunk = (int)ch;
-  *n_split = (int)cdiv(p_max, ch);
-  if (*n_split <= 1) {
-    *chunk = 1 << 30;
-    *n_split = 1;
-    return;
+  p.chunk = 1 << 30;
+  p.n_split = 1;
+  if (!attn_mfma_supported(dtype, d, G)) {
+    p.nw = 0;
+    p.nqt = (int)cdiv(q, kQT);
+    return p;
   }
-  const int64_t prows = units * (*n_split) * G * kQT;
-  *ws_bytes = align256((size_t)prows * d * sizeof(float)) + align256((size_t)prows * 2 * sizeof(float));
+  p.nw = ((int64_t)q * G <= 128 && G <= 4) ? 4 : 8;
+  const int ncg = p.nw;
+  const int nq = 32 * (ncg / G);
+  const int ncol = 32 * ncg;
+  p.nqt = (int)cdiv(q, nq);
+  const int64_t slots = (int64_t)kCUs * (p.nw == 4 ? 2 : 1);
+  const int64_t units = (int64_t)n_rows * Hkv * p.nqt;
+  if (p_max > 0 && units < slots) {
+    const int64_t want = cdiv(slots, units);
+    int64_t ch = cdiv(cdiv(p_max, want), kTK) * kTK;
+    if (ch < kMinChunk) ch = kMinChunk;
+    if (ch < p_max) {
+      p.chunk = (int)ch;
+      p.n_split = (int)cdiv(p_max, ch);
+    }
+  }
+  p.order = n_rows > 1 && n_rows <= kOrderMax && units * p.n_split > slots;
+  size_t off = 0;
+  p.off_order = off;
+  if (p.order) off += align256((size_t)n_rows * sizeof(int));
+  p.off_part_o = off;
+  p.off_part_ml = off;
+  if (p.n_split > 1) {
+    const size_t prows = (size_t)units * p.n_split * ncol;
+    off += align256(prows * kD * sizeof(float));
+    p.off_part_ml = off;
+    off += align256(prows * 2 * sizeof(float));
+  }
+  p.ws_bytes = off;
+  return p;
 }
 
-hipError_t launch_attn(const AttnArgs &a_in, hipStream_t s) {
-  AttnArgs a = a_in;
-  if (attn_mfma_supported(a.dtype, a.d, a.G)) {
-    const int64_t n_groups = (int64_t)a.n_rows * a.Hkv;
-    const int64_t per_group = (int64_t)a.nqt * a.n_split;
-    const int64_t grid = 8 * cdiv(n_groups, 8) * per_group;
-    switch (a.G) {
-      case 1: hipLaunchKernelGGL(attn_mfma_kernel<1>, dim3((unsigned)grid), dim3(64), 0, s, a); break;
-      case 2: hipLaunchKernelGGL(attn_mfma_kernel<2>, dim3((unsigned)grid), dim3(128), 0, s, a); break;
-      case 4: hipLaunchKernelGGL(attn_mfma_kernel<4>, dim3((unsigned)grid), dim3(256), 0, s, a); break;
-      case 8: hipLaunchKernelGGL(attn_mfma_kernel<8>, dim3((unsigned)grid), dim3(512), 0, s, a); break;
-    }
+template <int NW, int G>
+static hipError_t launch_mfma(const AttnArgs &a, hipStream_t s) {
+  using S = Shape<NW, G>;
+  const int64_t n_groups = (int64_t)a.n_rows * a.Hkv;
+  const int64_t per_group = (int64_t)a.nqt * a.n_split;
+  const int64_t grid = 8 * cdiv(n_groups, 8) * per_group;
+  if (a.row_order) {
+    hipLaunchKernelGGL(attn_order_kernel, dim3(1), dim3(kOrderMax), 0, s, a);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.n_split <= 1) return e;
-    const int64_t units = n_groups * a.nqt;
-    hipLaunchKernelGGL(attn_combine_kernel<bf16>, dim3((unsigned)units), dim3(256), 0, s, a, a.d);
-    return hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((attn_mfma_kernel<NW, G>), dim3((unsigned)grid), dim3(S::NT), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_split <= 1) return e;
+  const int64_t cgrid = n_groups * a.nqt * (S::NCOL / 8);
+  hipLaunchKernelGGL((attn_combine_kernel<NW, G>), dim3((unsigned)cgrid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn(const AttnArgs &a, hipStream_t s) {
+  if (attn_mfma_supported(a.dtype, a.d, a.G)) {
+    if (a.nw == 4) {
+      switch (a.G) {
+        case 1: return launch_mfma<4, 1>(a, s);
+        case 2: return launch_mfma<4, 2>(a, s);
+        case 4: return launch_mfma<4, 4>(a, s);
+      }
+    } else {
+      switch (a.G) {
+        case 1: return launch_mfma<8, 1>(a, s);
+        case 2: return launch_mfma<8, 2>(a, s);
+        case 4: return launch_mfma<8, 4>(a, s);
+        case 8: return launch_mfma<8, 8>(a, s);
+      }
+    }
+    return hipErrorInvalidValue;
   }
   const int64_t grid = (int64_t)a.n_rows * a.Hq * a.nqt;
   if (a.dtype == BD_F32) {

@@ -13,6 +13,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // Error reporting (thread-local message, defined in bd_api.hip).
 void set_error(const char *fmt, ...);
@@ -93,13 +94,21 @@ struct AttnArgs {
   float *lse;
   const int32_t *row_ids, *p_len;
   float scale2;  // sm_scale * log2(e)
-  // split plan
+  // launch plan (attn_plan)
+  int nw;                 // waves per block of the MFMA path (2 or 4)
   int nqt, chunk, n_split;
+  int *row_order;         // rows by descending prefix length, or NULL (natural order)
   float *part_o, *part_ml;
 };
-// Split plan: number of key chunks per (row, KV head, query tile) unit.
-void attn_plan(int dtype, int B, int Hq, int Hkv, int d, int q, int n_rows, int p_max,
-               int *chunk, int *n_split, int *nqt, size_t *ws_bytes);
+// Launch plan of one bd_attn_packed call: block shape, query tiles, key
+// chunks per (row, KV head, query tile) unit, whether rows are ordered
+// longest first, and the workspace this needs (offsets of its parts).
+struct AttnPlan {
+  int nw, nqt, chunk, n_split;
+  bool order;
+  size_t off_order, off_part_o, off_part_ml, ws_bytes;
+};
+AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int d, int q, int n_rows, int p_max);
 hipError_t launch_attn(const AttnArgs &a, hipStream_t s);
 bool attn_mfma_supported(int dtype, int d, int G);
 bool attn_generic_supported(int dtype, int d);

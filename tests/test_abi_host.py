@@ -133,8 +133,11 @@ def test_workspace_sizes_monotone():
     assert 0 < a < b
     # few units: the attention splits its prefix and needs a workspace
     assert bd.attn_workspace_size(bd.BD_BF16, 1, 32, 8, 128, 32, 1, 6554) > 0
-    # many units: one chunk per unit, no workspace
-    assert bd.attn_workspace_size(bd.BD_BF16, 64, 32, 8, 128, 128, 64, 16384) == 0
+    # many units: one chunk per unit; the workspace only holds the longest-first
+    # row order (64 int32 rounded up to 256 bytes), no partial results
+    assert bd.attn_workspace_size(bd.BD_BF16, 64, 32, 8, 128, 128, 64, 16384) == 256
+    # units that fit the GPU at once: neither an order nor partial results
+    assert bd.attn_workspace_size(bd.BD_BF16, 16, 32, 8, 128, 128, 16, 900) == 0
 
 
 def _attn(L, ws_bytes=None, **kw):
