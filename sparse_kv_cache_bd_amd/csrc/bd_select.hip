@@ -1,68 +1,76 @@
 // Representative-query selection (HERALD Sec. IV-A2, Sec. IV-B4).
 //
-// Pipeline (one stream, no host round trip):
+// Four kernels on one stream, no host round trip:
 //   prep   q_rep = mean (or one row) of the block queries, pre-scaled by
-//          sm_scale*log2(e) and split into bf16 hi + lo parts; clears the
-//          top-k state of the active rows.
-//   scan   z[hq, s] = <q_rep[hq], K[s, h]> for s < S_b, streaming the K cache
-//          once in coalesced 16-byte loads.  The G query heads of a KV head
-//          are the rows of one v_mfma_f32_16x16x32_bf16 tile (q_rep hi and lo
-//          accumulate into the same fp32 result, so the query keeps ~16
-//          mantissa bits while K stays bf16).  Per-chunk running (max, sum);
-//          the last chunk of a row to finish merges them (fixed order).
-//   score  s_hat[h, s] = sum_g exp2(z[g, s] - m_g) / l_g, written once: these
-//          are exactly the values that get ranked.
-//   hist x3  exact radix select of the k-th largest score on its fp32 bit
-//          pattern (non-negative floats order like their bit patterns),
-//          digits of 11/11/10 bits; block histograms in LDS, merged with
-//          global atomics; the last block of a pass picks the digit.
-//   count, write  ordered stream compaction: every score above the threshold
-//          plus the lowest-index ties, written in ascending position order,
-//          then -1 padding.
+//          sm_scale*log2(e) and split into bf16 hi + lo parts.
+//   scan   z[hq, s] = <q_rep[hq], K[s, h]> for s < S_b: streams the K cache
+//          once with 16-byte loads; the loads of the next 64-token group are
+//          in flight while the current group is computed.  Tokens are the
+//          rows of v_mfma_f32_16x16x32_bf16 and the G query heads of a KV
+//          head its columns (q_rep hi and lo accumulate into the same fp32
+//          result, so the query keeps ~16 mantissa bits while K stays bf16);
+//          a lane then holds 4 consecutive tokens of one head.  z of the
+//          block's chunk is staged in LDS and written with coalesced 16-byte
+//          stores after the loop (stores share the load counter, so none are
+//          issued while loads are in flight).  Per-block running (max, sum)
+//          per query head.
+//   score  m_g, l_g = fixed-order merge of the scan's per-block (max, sum);
+//          s_hat[h, s] = sum_g exp2(z[g, s] - m_g) / l_g, written once: these
+//          are exactly the values that get ranked.  (No cross-block merge
+//          inside the scan: that needs device-scope fences, which write back
+//          and invalidate the L2 of the XCD on every block.)
+//   topk   one block per (row, KV head): exact radix select of the k-th
+//          largest score on its fp32 bit pattern (non-negative floats order
+//          like their bit patterns; digits of 11, 11 and 10 bits), then an
+//          ordered compaction: every score above the threshold plus the
+//          lowest-position ties, ascending, -1 padding.  Rows of up to
+//          kLdsKeys scores are read from memory once and kept in LDS.
+//
+// Histogram increments are aggregated per wave: lanes whose digit equals the
+// first active lane's digit add in one atomic (two rounds), so the strongly
+// clustered digits of softmax-like scores do not serialise on one LDS bank.
 #include "bd_common.h"
 
 namespace bd {
 
 namespace {
 
-constexpr int kSD = 128;     // head dim of the selection path
-constexpr int kTS = 256;     // tokens per scan block
-constexpr int kCK = 4096;    // scores per top-k block
-constexpr int kBins = 2048;  // radix digit bins (11 bits)
+constexpr int kSD = 128;           // head dim of the selection path
+constexpr int kTS = 256;           // tokens per scan block
+constexpr int kScoreTok = 1024;    // tokens per score block
+constexpr int kBins = 2048;        // radix digit bins (11 bits)
 constexpr int kThreads = 256;
+constexpr int kTopkThreads = 1024;
+constexpr int kPerThread = 16;     // consecutive scores per thread in the compaction
+constexpr int kLdsKeys = 24576;    // scores of one (row, KV head) kept in LDS by topk
+constexpr int kZStr = kTS + 16;    // LDS row stride of the scan's z staging (floats)
 
 struct SelLayout {
-  size_t qhi, qlo, z, part, stats, rowtick, scores, hist, tick, state, ccount, total;
-  int nch_scan, nch_topk;
+  size_t qhi, qlo, z, part, scores, total;
+  int nch_scan;
+  int zs;  // row stride of z (s_max rounded up to 4: 16-byte aligned rows)
 };
 
 SelLayout sel_layout(int B, int Hq, int Hkv, int d, int s_max) {
   SelLayout L;
   L.nch_scan = (int)cdiv(s_max > 0 ? s_max : 1, kTS);
-  L.nch_topk = (int)cdiv(s_max > 0 ? s_max : 1, kCK);
+  L.zs = (int)cdiv(s_max, 4) * 4;
   const size_t P = (size_t)B * Hkv;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
   L.qhi = take((size_t)B * Hq * d * 2);
   L.qlo = take((size_t)B * Hq * d * 2);
-  L.z = take((size_t)B * Hq * (size_t)s_max * 4);
+  L.z = take((size_t)B * Hq * (size_t)L.zs * 4);
   L.part = take((size_t)B * Hq * L.nch_scan * 2 * 4);
-  L.stats = take((size_t)B * Hq * 2 * 4);
-  L.rowtick = take((size_t)B * 4);
   L.scores = take(P * (size_t)s_max * 4);
-  L.hist = take(P * 3 * kBins * 4);
-  L.tick = take(P * 4 * 4);
-  L.state = take(P * 4 * 4);
-  L.ccount = take(P * L.nch_topk * 2 * 4);
   L.total = off;
   return L;
 }
 
 struct SelPtrs {
   bf16 *qhi, *qlo;
-  float *z, *part, *stats, *scores;
-  uint32_t *rowtick, *hist, *tick, *state, *ccount;
-  int nch_scan, nch_topk;
+  float *z, *part, *scores;
+  int nch_scan, zs;
 };
 
 __device__ inline void row_sizes(const SelectArgs &a, int b, int &S, int &kb) {
@@ -70,9 +78,18 @@ __device__ inline void row_sizes(const SelectArgs &a, int b, int &S, int &kb) {
   kb = clampi(a.k_sel[b], 0, a.k_max);
 }
 
-// Block-wide exclusive prefix sum over 256 threads (4 waves).
+// Merge running (max, sum) pairs in log2 units.
+__device__ inline void merge_ml(float &m, float &l, float mo, float lo) {
+  const float mn = fmaxf(m, mo);
+  if (mn == -INFINITY) return;
+  l = l * __builtin_amdgcn_exp2f(m - mn) + lo * __builtin_amdgcn_exp2f(mo - mn);
+  m = mn;
+}
+
+// Block-wide exclusive prefix sum (any multiple of 64 threads, <= 1024).
+// sh holds at least 16 ints.
 __device__ inline int block_excl_scan(int v, int *sh, int &total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   int x = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -84,8 +101,7 @@ __device__ inline int block_excl_scan(int v, int *sh, int &total) {
   __syncthreads();
   int before = 0;
   total = 0;
-#pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) {
+  for (int w = 0; w < nw; ++w) {
     const int t = sh[w];
     if (w < wave) before += t;
     total += t;
@@ -93,44 +109,70 @@ __device__ inline int block_excl_scan(int v, int *sh, int &total) {
   return before + x - v;
 }
 
+// Histogram increment for one key per lane (valid lanes only): two rounds of
+// per-wave aggregation of the most common digit, then single increments.
+__device__ inline void hist_add(uint32_t *h, uint32_t bin, bool valid) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int round = 0; round < 2; ++round) {
+    const uint64_t act = __ballot(valid);
+    if (act == 0) return;
+    const int leader = __builtin_ctzll(act);
+    const uint32_t b0 = __builtin_amdgcn_readlane(bin, leader);
+    const uint64_t same = __ballot(valid && bin == b0);
+    if (lane == leader) atomicAdd(&h[b0], (uint32_t)__builtin_popcountll(same));
+    if (bin == b0) valid = false;
+  }
+  if (valid) atomicAdd(&h[bin], 1u);
+}
+
 // ------------------------------------------------------------------- prep
-__global__ __launch_bounds__(kSD) void sel_prep_kernel(SelectArgs a, SelPtrs w) {
+// Block = (query head, row), 256 threads: thread t sums queries i = t/16,
+// t/16 + 16, ... over dims 8*(t%16) .. +8 (16-byte loads), then the 16
+// partial sums of each dim chunk are added in a fixed order.
+__global__ __launch_bounds__(kThreads) void sel_prep_kernel(SelectArgs a, SelPtrs w) {
   const int hq = blockIdx.x, b = blockIdx.y;
   int S, kb;
   row_sizes(a, b, S, kb);
   if (S == 0 || kb == 0) return;
-  const int d = threadIdx.x;
-  const bf16 *qp = a.q + (int64_t)b * a.qs[0] + (int64_t)hq * a.qs[2] + d;
-  float acc;
+  const int t = threadIdx.x, dc = t & 15, qs = t >> 4;
+  const bf16 *qp = a.q + (int64_t)b * a.qs[0] + (int64_t)hq * a.qs[2] + dc * 8;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (a.rep_mode == BD_REP_ROW) {
-    acc = (float)qp[(int64_t)a.rep_row * a.qs[1]];
+    if (qs == 0) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8 *>(qp + (int64_t)a.rep_row * a.qs[1]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = (float)v[e];
+    }
   } else {
-    acc = 0.f;
-    for (int i = 0; i < a.nq; ++i) acc += (float)qp[(int64_t)i * a.qs[1]];
-    acc /= (float)a.nq;
+    for (int i = qs; i < a.nq; i += 16) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8 *>(qp + (int64_t)i * a.qs[1]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += (float)v[e];
+    }
   }
-  const float v = acc * a.scale2;
-  const bf16 hi = (bf16)v;
-  const bf16 lo = (bf16)(v - (float)hi);
-  w.qhi[((int64_t)b * a.Hq + hq) * kSD + d] = hi;
-  w.qlo[((int64_t)b * a.Hq + hq) * kSD + d] = lo;
-  // clear the per-row ticket and the top-k state of this row's KV heads
-  if (hq == 0 && d == 0) w.rowtick[b] = 0;
-  const int words = a.Hkv * 3 * kBins;
-  uint32_t *hist = w.hist + (size_t)b * words;
-  for (int e = hq * kSD + d; e < words; e += a.Hq * kSD) hist[e] = 0;
-  if (hq == 0 && d < a.Hkv) {
-    const size_t p = (size_t)b * a.Hkv + d;
-    for (int e = 0; e < 4; ++e) w.tick[p * 4 + e] = 0;
-    w.state[p * 4 + 0] = 0;                 // threshold prefix
-    w.state[p * 4 + 1] = (uint32_t)min(kb, S);  // remaining rank inside the prefix
-    w.state[p * 4 + 2] = 0;
-    w.state[p * 4 + 3] = 0;
+  __shared__ float part[16][kSD + 4];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[qs][dc * 8 + e] = acc[e];
+  __syncthreads();
+  if (t < kSD) {
+    float sum = 0.f;
+    for (int i = 0; i < 16; ++i) sum += part[i][t];
+    if (a.rep_mode != BD_REP_ROW) sum /= (float)a.nq;
+    const float v = sum * a.scale2;
+    const bf16 hi = (bf16)v;
+    const bf16 lo = (bf16)(v - (float)hi);
+    w.qhi[((int64_t)b * a.Hq + hq) * kSD + t] = hi;
+    w.qlo[((int64_t)b * a.Hq + hq) * kSD + t] = lo;
   }
 }
 
 // ------------------------------------------------------------------- scan
-__global__ __launch_bounds__(kThreads) void sel_scan_kernel(SelectArgs a, SelPtrs w) {
+// Block = (token chunk of kTS, row).  Wave w handles KV heads w, w+4, ...;
+// its work is a flat list of (head, 64-token group) items.  The 16 loads of
+// 16 bytes per lane of item i+1 are issued before the MFMAs of item i.  The
+// row's q_rep hi / lo parts are staged in LDS once per block.
+__global__ __launch_bounds__(kThreads, 2) void sel_scan_kernel(SelectArgs a, SelPtrs w) {
   const int c = blockIdx.x, b = blockIdx.y;
   int S, kb;
   row_sizes(a, b, S, kb);
@@ -138,304 +180,329 @@ __global__ __launch_bounds__(kThreads) void sel_scan_kernel(SelectArgs a, SelPtr
   const int nch = (int)cdiv(S, kTS);
   if (c >= nch) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 15;   // token column of the 16x16 tile
-  const int grp = lane >> 4;   // k-group (A/B operands) and row group (C)
+  const int col = lane & 15;   // token row of the A operand; query head of B and C
+  const int grp = lane >> 4;   // k-group of A/B; row group of C
   const int G = a.G;
   const int s0 = c * kTS;
-  __shared__ int sh_ticket;
-
-  for (int h = wave; h < a.Hkv; h += kThreads / 64) {
-    // A operands: row col = query head h*G + col (zero rows past G)
-    bf16x8 ahi[kSD / 32], alo[kSD / 32];
-    {
-      const bool ok = col < G;
-      const bf16 *ph = w.qhi + ((int64_t)b * a.Hq + h * G + (ok ? col : 0)) * kSD + grp * 8;
-      const bf16 *pl = w.qlo + ((int64_t)b * a.Hq + h * G + (ok ? col : 0)) * kSD + grp * 8;
-#pragma unroll
-      for (int ks = 0; ks < kSD / 32; ++ks) {
-        ahi[ks] = ok ? *reinterpret_cast<const bf16x8 *>(ph + ks * 32) : bf16x8{};
-        alo[ks] = ok ? *reinterpret_cast<const bf16x8 *>(pl + ks * 32) : bf16x8{};
-      }
+  const int s_end = min(s0 + kTS, S);
+  // dynamic LDS: q_rep hi and lo [Hq][kSD] bf16, then z of this chunk [Hq][kZStr] fp32
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  bf16 *qs_hi = reinterpret_cast<bf16 *>(smem);
+  bf16 *qs_lo = qs_hi + a.Hq * kSD;
+  float *zs = reinterpret_cast<float *>(qs_lo + a.Hq * kSD);
+  __shared__ float ml_lds[64][2];   // per query head (max, sum) of this chunk
+  {
+    const bf16x8 *gh = reinterpret_cast<const bf16x8 *>(w.qhi + (int64_t)b * a.Hq * kSD);
+    const bf16x8 *gl = reinterpret_cast<const bf16x8 *>(w.qlo + (int64_t)b * a.Hq * kSD);
+    for (int e = tid; e < a.Hq * kSD / 8; e += kThreads) {
+      reinterpret_cast<bf16x8 *>(qs_hi)[e] = gh[e];
+      reinterpret_cast<bf16x8 *>(qs_lo)[e] = gl[e];
     }
-    float m[4], l[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) { m[r] = -INFINITY; l[r] = 0.f; }
+  }
+  __syncthreads();
+
+  const int n_groups = (int)cdiv(s_end - s0, 64);
+  const int n_heads = a.Hkv > wave ? (int)cdiv(a.Hkv - wave, kThreads / 64) : 0;
+  const int n_items = n_heads * n_groups;
+  auto item_head = [&](int i) { return wave + (kThreads / 64) * (i / n_groups); };
+  auto item_t0 = [&](int i) { return s0 + 64 * (i % n_groups); };
+
+  bf16x8 abuf[2][4][kSD / 32];
+  auto load = [&](int i, bf16x8 (&dst)[4][kSD / 32]) {
+    const int h = item_head(i), t0 = item_t0(i);
     const bf16 *kbase = a.k + (int64_t)b * a.ks[0] + (int64_t)h * a.ks[2] + grp * 8;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tok = min(t0 + 16 * j + col, S - 1);   // clamped rows are discarded below
+      const bf16 *kp = kbase + (int64_t)tok * a.ks[1];
+#pragma unroll
+      for (int ks = 0; ks < kSD / 32; ++ks) dst[j][ks] = *reinterpret_cast<const bf16x8 *>(kp + ks * 32);
+    }
+  };
 
-    for (int g16 = 0; g16 < kTS / 16; g16 += 2) {
-      bf16x8 bop[2][kSD / 32];
-      int tok[2];
+  float m = -INFINITY, l = 0.f;   // running stats of column col of the current head
+  auto flush = [&](int h) {
+    // merge over the 4 row groups holding the same column (lanes col + 16*grp)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        tok[j] = s0 + (g16 + j) * 16 + col;
-        const bool ok = tok[j] < S;
-        const bf16 *kp = kbase + (int64_t)(ok ? tok[j] : 0) * a.ks[1];
+    for (int o = 16; o < 64; o <<= 1) merge_ml(m, l, __shfl_xor(m, o), __shfl_xor(l, o));
+    if (grp == 0 && col < G) {
+      ml_lds[h * G + col][0] = m;
+      ml_lds[h * G + col][1] = l;
+    }
+    m = -INFINITY;
+    l = 0.f;
+  };
+  auto compute = [&](int i, bf16x8 (&aop)[4][kSD / 32]) {
+    const int h = item_head(i), t0 = item_t0(i);
+    const bf16 *qh = qs_hi + (h * G + min(col, G - 1)) * kSD + grp * 8;
+    const bf16 *ql = qs_lo + (h * G + min(col, G - 1)) * kSD + grp * 8;
+    const bool qok = col < G;
+    f32x4 z[4];
 #pragma unroll
-        for (int ks = 0; ks < kSD / 32; ++ks)
-          bop[j][ks] = ok ? *reinterpret_cast<const bf16x8 *>(kp + ks * 32) : bf16x8{};
-      }
+    for (int j = 0; j < 4; ++j) z[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < kSD / 32; ++ks) {
+      const bf16x8 bh = qok ? *reinterpret_cast<const bf16x8 *>(qh + ks * 32) : bf16x8{};
+      const bf16x8 bl = qok ? *reinterpret_cast<const bf16x8 *>(ql + ks * 32) : bf16x8{};
 #pragma unroll
-        for (int ks = 0; ks < kSD / 32; ++ks) {
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[ks], bop[j][ks], acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[ks], bop[j][ks], acc, 0, 0, 0);
-        }
-        if (tok[j] < S) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = grp * 4 + r;
-            if (row < G) {
-              const float z = acc[r];
-              w.z[((int64_t)b * a.Hq + h * G + row) * a.s_max + tok[j]] = z;
-              const float mn = fmaxf(m[r], z);
-              l[r] = l[r] * __builtin_amdgcn_exp2f(m[r] - mn) + __builtin_amdgcn_exp2f(z - mn);
-              m[r] = mn;
-            }
-          }
-        }
+      for (int j = 0; j < 4; ++j) {
+        z[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[j][ks], bh, z[j], 0, 0, 0);
+        z[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[j][ks], bl, z[j], 0, 0, 0);
       }
     }
-    // merge (m, l) over the 16 token columns of each row group
+    // lane (col < G, grp) holds tokens t0 + 16j + 4*grp + r of query head col
+    float mx = -INFINITY;
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float mo = __shfl_xor(m[r], o);
-        const float lo = __shfl_xor(l[r], o);
-        const float mn = fmaxf(m[r], mo);
-        if (mn == -INFINITY) continue;
-        l[r] = l[r] * __builtin_amdgcn_exp2f(m[r] - mn) + lo * __builtin_amdgcn_exp2f(mo - mn);
-        m[r] = mn;
+        const int tok = t0 + 16 * j + 4 * grp + r;
+        if (tok >= S) z[j][r] = -INFINITY;
+        mx = fmaxf(mx, z[j][r]);
+      }
+    if (col < G) {
+      float *zrow = zs + (h * G + col) * kZStr + (t0 - s0) + 4 * grp;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4 *>(zrow + 16 * j) = z[j];
+      const float mn = fmaxf(m, mx);
+      if (mn != -INFINITY) {
+        float acc = l * __builtin_amdgcn_exp2f(m - mn);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc += __builtin_amdgcn_exp2f(z[j][r] - mn);
+        l = acc;
+        m = mn;
       }
     }
-    if (col == 0) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = grp * 4 + r;
-        if (row < G) {
-          float *pp = w.part + (((int64_t)b * a.Hq + h * G + row) * w.nch_scan + c) * 2;
-          pp[0] = m[r];
-          pp[1] = l[r];
-        }
+    if (i % n_groups == n_groups - 1) flush(h);
+  };
+
+  if (n_items > 0) load(0, abuf[0]);
+  int i = 0;
+  for (; i + 1 < n_items; i += 2) {
+    load(i + 1, abuf[1]);
+    compute(i, abuf[0]);
+    load(min(i + 2, n_items - 1), abuf[0]);   // unconditional: keeps the wait counts exact
+    compute(i + 1, abuf[1]);
+  }
+  if (i < n_items) compute(i, abuf[0]);
+
+  // z and (max, sum) of the chunk to global memory: 16-byte stores,
+  // consecutive threads on consecutive tokens of one query head
+  __syncthreads();
+  for (int hq = tid; hq < a.Hq; hq += kThreads) {
+    float *pp = w.part + (((int64_t)b * a.Hq + hq) * w.nch_scan + c) * 2;
+    pp[0] = ml_lds[hq][0];
+    pp[1] = ml_lds[hq][1];
+  }
+  {
+    const int n4 = (int)cdiv(s_end - s0, 4);
+    for (int e = tid; e < a.Hq * n4; e += kThreads) {
+      const int hq = e / n4, q4 = e - hq * n4;
+      const int tok = s0 + 4 * q4;
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(zs + hq * kZStr + 4 * q4);
+      float *zp = w.z + ((int64_t)b * a.Hq + hq) * w.zs + tok;
+      if (tok + 3 < S) {
+        *reinterpret_cast<f32x4 *>(zp) = v;
+      } else {
+        for (int r = 0; r < 4; ++r)
+          if (tok + r < S) zp[r] = v[r];
       }
     }
   }
 
-  // the last block of the row merges all chunk statistics
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) sh_ticket = (int)atomicAdd(&w.rowtick[b], 1u);
-  __syncthreads();
-  if (sh_ticket != nch - 1) return;
-  __threadfence();
-  const int sub = tid & 7;
-  for (int hq = tid >> 3; hq < a.Hq; hq += kThreads / 8) {
-    float M = -INFINITY, L = 0.f;
-    for (int cc = sub; cc < nch; cc += 8) {
-      const float *pp = w.part + (((int64_t)b * a.Hq + hq) * w.nch_scan + cc) * 2;
-      const float mc = pp[0], lc = pp[1];
-      const float mn = fmaxf(M, mc);
-      if (mn == -INFINITY) continue;
-      L = L * __builtin_amdgcn_exp2f(M - mn) + lc * __builtin_amdgcn_exp2f(mc - mn);
-      M = mn;
-    }
-#pragma unroll
-    for (int o = 1; o < 8; o <<= 1) {
-      const float mo = __shfl_xor(M, o);
-      const float lo = __shfl_xor(L, o);
-      const float mn = fmaxf(M, mo);
-      if (mn == -INFINITY) continue;
-      L = L * __builtin_amdgcn_exp2f(M - mn) + lo * __builtin_amdgcn_exp2f(mo - mn);
-      M = mn;
-    }
-    if (sub == 0) {
-      w.stats[((int64_t)b * a.Hq + hq) * 2 + 0] = M;
-      w.stats[((int64_t)b * a.Hq + hq) * 2 + 1] = L;
-    }
-  }
 }
 
 // ------------------------------------------------------------------ score
+// Block = (chunk of kScoreTok tokens, KV head, row); 4 consecutive tokens per
+// thread.
 __global__ __launch_bounds__(kThreads) void sel_score_kernel(SelectArgs a, SelPtrs w) {
-  const int c = blockIdx.x, b = blockIdx.y;
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   int S, kb;
   row_sizes(a, b, S, kb);
   if (S == 0 || kb == 0) return;
-  if (c >= (int)cdiv(S, kTS)) return;
-  __shared__ float sm[64], sil[64];
-  for (int hq = threadIdx.x; hq < a.Hq; hq += kThreads) {
-    sm[hq] = w.stats[((int64_t)b * a.Hq + hq) * 2 + 0];
-    sil[hq] = 1.f / w.stats[((int64_t)b * a.Hq + hq) * 2 + 1];
+  constexpr int per = kScoreTok / kThreads;
+  if (c * kScoreTok >= S) return;
+  // (max, sum) of each query head of the group: merge of the scan's chunk
+  // partials, wave g for head g, chunks cc = lane, lane + 64, ..., then a
+  // fixed butterfly (the same result in every block)
+  __shared__ float st_m[8], st_il[8];
+  {
+    const int wv = threadIdx.x >> 6, ln = threadIdx.x & 63;
+    const int nch = (int)cdiv(S, kTS);
+    for (int g = wv; g < a.G; g += kThreads / 64) {
+      const float *pp = w.part + ((int64_t)b * a.Hq + h * a.G + g) * w.nch_scan * 2;
+      float M = -INFINITY, L = 0.f;
+      for (int cc = ln; cc < nch; cc += 64) merge_ml(M, L, pp[cc * 2], pp[cc * 2 + 1]);
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) merge_ml(M, L, __shfl_xor(M, o), __shfl_xor(L, o));
+      if (ln == 0) {
+        st_m[g] = M;
+        st_il[g] = 1.f / L;
+      }
+    }
   }
   __syncthreads();
-  const int s = c * kTS + threadIdx.x;
+  const int s = c * kScoreTok + threadIdx.x * per;
   if (s >= S) return;
-  for (int h = 0; h < a.Hkv; ++h) {
-    float acc = 0.f;
-    for (int g = 0; g < a.G; ++g) {
-      const int hq = h * a.G + g;
-      const float z = w.z[((int64_t)b * a.Hq + hq) * a.s_max + s];
-      acc += __builtin_amdgcn_exp2f(z - sm[hq]) * sil[hq];
+  const bool full = s + per <= S;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int g = 0; g < a.G; ++g) {
+    const int hq = h * a.G + g;
+    const float M = st_m[g];
+    const float inv_l = st_il[g];
+    const float *zp = w.z + ((int64_t)b * a.Hq + hq) * w.zs + s;
+    f32x4 z;
+    if (full) {
+      z = *reinterpret_cast<const f32x4 *>(zp);
+    } else {
+#pragma unroll
+      for (int r = 0; r < per; ++r) z[r] = (s + r < S) ? zp[r] : 0.f;
     }
-    w.scores[((int64_t)b * a.Hkv + h) * a.s_max + s] = acc;
+#pragma unroll
+    for (int r = 0; r < per; ++r) acc[r] += __builtin_amdgcn_exp2f(z[r] - M) * inv_l;
+  }
+  float *op = w.scores + ((int64_t)b * a.Hkv + h) * a.s_max + s;
+  if (full && ((uintptr_t)op & 15) == 0) {
+    *reinterpret_cast<f32x4 *>(op) = acc;
+  } else {
+#pragma unroll
+    for (int r = 0; r < per; ++r)
+      if (s + r < S) op[r] = acc[r];
   }
 }
 
 // ---------------------------------------------------------------- top-k
-template <int PASS>
-__global__ __launch_bounds__(kThreads) void sel_hist_kernel(SelectArgs a, SelPtrs w) {
-  const int c = blockIdx.x, p = blockIdx.y;
-  const int b = p / a.Hkv;
-  int S, kb;
-  row_sizes(a, b, S, kb);
-  if (S == 0 || kb == 0) return;
-  const int nch = (int)cdiv(S, kCK);
-  if (c >= nch) return;
-  constexpr int shift = PASS == 0 ? 21 : (PASS == 1 ? 10 : 0);
-  constexpr uint32_t dmask = PASS == 2 ? 1023u : 2047u;
-  const uint32_t prefix = w.state[p * 4 + 0];
-  const uint32_t krem = w.state[p * 4 + 1];
-  __shared__ uint32_t hist[kBins];
-  __shared__ int sh[8];
-  __shared__ int sh_ticket;
-  for (int e = threadIdx.x; e < kBins; e += kThreads) hist[e] = 0;
-  __syncthreads();
-  const uint32_t *keys = reinterpret_cast<const uint32_t *>(w.scores) + (size_t)p * a.s_max;
-  for (int e = 0; e < kCK / kThreads; ++e) {
-    const int s = c * kCK + e * kThreads + threadIdx.x;
-    if (s < S) {
-      const uint32_t key = keys[s];
-      bool match = true;
-      if (PASS == 1) match = (key >> 21) == (prefix >> 21);
-      if (PASS == 2) match = (key >> 10) == (prefix >> 10);
-      if (match) atomicAdd(&hist[(key >> shift) & dmask], 1u);
-    }
+// Digit D with count(digit > D) < krem <= count(digit >= D) over nb bins;
+// returns D and the rank left inside it.  One block of kTopkThreads.
+__device__ inline void find_digit(const uint32_t *cnt_of, int nb, uint32_t krem, int *sh,
+                                  uint32_t &D, uint32_t &rem) {
+  __shared__ uint32_t sd[2];
+  if (threadIdx.x == 0) {
+    sd[0] = 0;
+    sd[1] = krem;
   }
-  __syncthreads();
-  uint32_t *gh = w.hist + ((size_t)p * 3 + PASS) * kBins;
-  for (int e = threadIdx.x; e < kBins; e += kThreads)
-    if (hist[e]) atomicAdd(&gh[e], hist[e]);
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) sh_ticket = (int)atomicAdd(&w.tick[p * 4 + PASS], 1u);
-  __syncthreads();
-  if (sh_ticket != nch - 1) return;
-  __threadfence();
-  // last block: find digit D with count(> D) < krem <= count(>= D)
-  constexpr int per = kBins / kThreads;  // 8 bins per thread, descending order
-  const int hi_bin = kBins - 1 - threadIdx.x * per;
-  uint32_t cnt[per];
+  const int per = nb / kTopkThreads;  // 2 or 1 bins per thread, descending
+  const int hi_bin = nb - 1 - threadIdx.x * per;
+  uint32_t cnt[2] = {0u, 0u};
   int tsum = 0;
-#pragma unroll
   for (int e = 0; e < per; ++e) {
-    cnt[e] = gh[hi_bin - e];
+    cnt[e] = cnt_of[hi_bin - e];
     tsum += (int)cnt[e];
   }
   int total;
   const int before = block_excl_scan(tsum, sh, total);
   if ((uint32_t)before < krem && krem <= (uint32_t)(before + tsum)) {
     uint32_t cum = (uint32_t)before;
-#pragma unroll
     for (int e = 0; e < per; ++e) {
       if (cum + cnt[e] >= krem) {
-        const uint32_t D = (uint32_t)(hi_bin - e);
-        w.state[p * 4 + 0] = prefix | (D << shift);
-        w.state[p * 4 + 1] = krem - cum;
+        sd[0] = (uint32_t)(hi_bin - e);
+        sd[1] = krem - cum;
         break;
       }
       cum += cnt[e];
     }
   }
+  __syncthreads();
+  D = sd[0];
+  rem = sd[1];
+  __syncthreads();
 }
 
-__global__ __launch_bounds__(kThreads) void sel_count_kernel(SelectArgs a, SelPtrs w) {
-  const int c = blockIdx.x, p = blockIdx.y;
-  const int b = p / a.Hkv;
-  int S, kb;
-  row_sizes(a, b, S, kb);
-  if (S == 0 || kb == 0) return;
-  if (c >= (int)cdiv(S, kCK)) return;
-  const uint32_t thr = w.state[p * 4 + 0];
-  const uint32_t *keys = reinterpret_cast<const uint32_t *>(w.scores) + (size_t)p * a.s_max;
-  int gt = 0, eq = 0;
-  for (int e = 0; e < kCK / kThreads; ++e) {
-    const int s = c * kCK + e * kThreads + threadIdx.x;
-    if (s < S) {
-      const uint32_t key = keys[s];
-      gt += key > thr;
-      eq += key == thr;
+// Radix select + ordered compaction over keys[0, S) (LDS or global memory).
+__device__ inline void topk_body(const uint32_t *keys, int S, int keff, int32_t *out, uint32_t *hist,
+                                 int *sh) {
+  uint32_t prefix = 0, krem = (uint32_t)keff;
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const uint32_t dmask = pass == 2 ? 1023u : 2047u;
+    const int hi_shift = shift + (pass == 2 ? 10 : 11);  // bits above this digit
+    for (int e = threadIdx.x; e < kBins; e += kTopkThreads) hist[e] = 0;
+    __syncthreads();
+    for (int s0 = 0; s0 < S; s0 += kTopkThreads) {
+      const int s = s0 + threadIdx.x;
+      const uint32_t key = s < S ? keys[s] : 0u;
+      const bool match = s < S && (pass == 0 || (key >> hi_shift) == (prefix >> hi_shift));
+      hist_add(hist, (key >> shift) & dmask, match);
     }
+    __syncthreads();
+    uint32_t D;
+    find_digit(hist, pass == 2 ? 1024 : kBins, krem, sh, D, krem);
+    prefix |= D << shift;
   }
-  __shared__ int sh[8];
-  int tg, te;
-  block_excl_scan(gt, sh, tg);
-  block_excl_scan(eq, sh, te);
-  if (threadIdx.x == 0) {
-    w.ccount[((size_t)p * w.nch_topk + c) * 2 + 0] = (uint32_t)tg;
-    w.ccount[((size_t)p * w.nch_topk + c) * 2 + 1] = (uint32_t)te;
+  const uint32_t thr = prefix;
+  const int need_eq = (int)krem;
+
+  // ordered compaction: kPerThread consecutive scores per thread per chunk
+  int sel_base = 0, eq_base = 0;  // selections / ties before the current chunk
+  for (int c0 = 0; c0 < S; c0 += kTopkThreads * kPerThread) {
+    const int sb = c0 + threadIdx.x * kPerThread;
+    uint32_t kv[kPerThread];
+    int n_eq = 0;
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const int s = sb + e;
+      kv[e] = s < S ? keys[s] : 0u;
+      n_eq += s < S && kv[e] == thr;
+    }
+    int tot_eq;
+    const int eq_rank0 = eq_base + block_excl_scan(n_eq, sh, tot_eq);
+    int n_sel = 0, er = eq_rank0;
+    uint32_t selbits = 0;
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const int s = sb + e;
+      bool sel = false;
+      if (s < S) {
+        if (kv[e] > thr) {
+          sel = true;
+        } else if (kv[e] == thr) {
+          sel = er < need_eq;
+          ++er;
+        }
+      }
+      selbits |= (uint32_t)sel << e;
+      n_sel += sel;
+    }
+    int tot_sel;
+    int pos = sel_base + block_excl_scan(n_sel, sh, tot_sel);
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e)
+      if (selbits & (1u << e)) {
+        if (pos < keff) out[pos] = sb + e;
+        ++pos;
+      }
+    sel_base += tot_sel;
+    eq_base += tot_eq;
   }
 }
 
-__global__ __launch_bounds__(kThreads) void sel_write_kernel(SelectArgs a, SelPtrs w) {
-  const int c = blockIdx.x, p = blockIdx.y;
+__global__ __launch_bounds__(kTopkThreads) void sel_topk_kernel(SelectArgs a, SelPtrs w) {
+  const int p = blockIdx.x;
   const int b = p / a.Hkv;
   int S, kb;
   row_sizes(a, b, S, kb);
   const int keff = min(S, kb);
   int32_t *out = a.idx_out + (size_t)p * a.k_max;
-  if (c == 0)
-    for (int j = keff + threadIdx.x; j < a.k_max; j += kThreads) out[j] = -1;
+  for (int j = keff + threadIdx.x; j < a.k_max; j += kTopkThreads) out[j] = -1;
   if (keff == 0) return;
-  if (c >= (int)cdiv(S, kCK)) return;
-  const uint32_t thr = w.state[p * 4 + 0];
-  const int need_eq = (int)w.state[p * 4 + 1];
-  __shared__ int sh[8];
-  // selected before this chunk: all "greater" ones plus the first ties
-  int gtb = 0, eqb = 0;
-  for (int cc = threadIdx.x; cc < c; cc += kThreads) {
-    gtb += (int)w.ccount[((size_t)p * w.nch_topk + cc) * 2 + 0];
-    eqb += (int)w.ccount[((size_t)p * w.nch_topk + cc) * 2 + 1];
+  if (keff == S) {  // the whole prefix is selected
+    for (int j = threadIdx.x; j < S; j += kTopkThreads) out[j] = j;
+    return;
   }
-  int gt_before, eq_before;
-  block_excl_scan(gtb, sh, gt_before);
-  block_excl_scan(eqb, sh, eq_before);
-  // this thread's 16 consecutive positions
-  constexpr int per = kCK / kThreads;
-  const int s0 = c * kCK + threadIdx.x * per;
+  __shared__ uint32_t hist[kBins];
+  __shared__ int sh[16];
+  __shared__ uint32_t cache[kLdsKeys];
   const uint32_t *keys = reinterpret_cast<const uint32_t *>(w.scores) + (size_t)p * a.s_max;
-  uint32_t kv[per];
-  int n_eq = 0;
-#pragma unroll
-  for (int e = 0; e < per; ++e) {
-    const int s = s0 + e;
-    kv[e] = (s < S) ? keys[s] : 0u;
-    n_eq += (s < S) && kv[e] == thr;
+  if (S <= kLdsKeys) {
+    for (int e = threadIdx.x; e < S; e += kTopkThreads) cache[e] = keys[e];
+    __syncthreads();
+    topk_body(cache, S, keff, out, hist, sh);
+  } else {
+    topk_body(keys, S, keff, out, hist, sh);
   }
-  int tot;
-  const int eq_rank0 = eq_before + block_excl_scan(n_eq, sh, tot);
-  int n_sel = 0, er = eq_rank0;
-  uint32_t selbits = 0;
-#pragma unroll
-  for (int e = 0; e < per; ++e) {
-    const int s = s0 + e;
-    bool sel = false;
-    if (s < S) {
-      if (kv[e] > thr) sel = true;
-      else if (kv[e] == thr) { sel = er < need_eq; ++er; }
-    }
-    selbits |= (uint32_t)sel << e;
-    n_sel += sel;
-  }
-  const int pos0 = gt_before + min(eq_before, need_eq) + block_excl_scan(n_sel, sh, tot);
-  int pos = pos0;
-#pragma unroll
-  for (int e = 0; e < per; ++e)
-    if (selbits & (1u << e)) {
-      if (pos < keff) out[pos] = s0 + e;
-      ++pos;
-    }
 }
 
 }  // namespace
@@ -452,29 +519,19 @@ hipError_t launch_select(const SelectArgs &a, hipStream_t s) {
   w.qlo = reinterpret_cast<bf16 *>(a.ws + L.qlo);
   w.z = reinterpret_cast<float *>(a.ws + L.z);
   w.part = reinterpret_cast<float *>(a.ws + L.part);
-  w.stats = reinterpret_cast<float *>(a.ws + L.stats);
-  w.rowtick = reinterpret_cast<uint32_t *>(a.ws + L.rowtick);
   w.scores = a.score_out ? a.score_out : reinterpret_cast<float *>(a.ws + L.scores);
-  w.hist = reinterpret_cast<uint32_t *>(a.ws + L.hist);
-  w.tick = reinterpret_cast<uint32_t *>(a.ws + L.tick);
-  w.state = reinterpret_cast<uint32_t *>(a.ws + L.state);
-  w.ccount = reinterpret_cast<uint32_t *>(a.ws + L.ccount);
   w.nch_scan = L.nch_scan;
-  w.nch_topk = L.nch_topk;
+  w.zs = L.zs;
   hipError_t e;
-  hipLaunchKernelGGL(sel_prep_kernel, dim3(a.Hq, a.B), dim3(kSD), 0, s, a, w);
+  hipLaunchKernelGGL(sel_prep_kernel, dim3(a.Hq, a.B), dim3(kThreads), 0, s, a, w);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(sel_scan_kernel, dim3(L.nch_scan, a.B), dim3(kThreads), 0, s, a, w);
+  const size_t scan_lds = (size_t)a.Hq * (2 * kSD * sizeof(bf16) + kZStr * sizeof(float));
+  hipLaunchKernelGGL(sel_scan_kernel, dim3(L.nch_scan, a.B), dim3(kThreads), scan_lds, s, a, w);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(sel_score_kernel, dim3(L.nch_scan, a.B), dim3(kThreads), 0, s, a, w);
+  hipLaunchKernelGGL(sel_score_kernel, dim3((unsigned)cdiv(a.s_max, kScoreTok), a.Hkv, a.B),
+                     dim3(kThreads), 0, s, a, w);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const dim3 tg(L.nch_topk, a.B * a.Hkv);
-  hipLaunchKernelGGL(sel_hist_kernel<0>, tg, dim3(kThreads), 0, s, a, w);
-  hipLaunchKernelGGL(sel_hist_kernel<1>, tg, dim3(kThreads), 0, s, a, w);
-  hipLaunchKernelGGL(sel_hist_kernel<2>, tg, dim3(kThreads), 0, s, a, w);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(sel_count_kernel, tg, dim3(kThreads), 0, s, a, w);
-  hipLaunchKernelGGL(sel_write_kernel, tg, dim3(kThreads), 0, s, a, w);
+  hipLaunchKernelGGL(sel_topk_kernel, dim3(a.B * a.Hkv), dim3(kTopkThreads), 0, s, a, w);
   return hipGetLastError();
 }
 
