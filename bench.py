@@ -15,7 +15,13 @@ and scatter included.  ``breakdown`` gives each operation's own rate
 (TFLOP/s or GB/s of algorithmic bytes) and fraction of the MI355X peak.
 ``roofline`` reports the dominant kernel (dense-row attention), timed with
 HIP events on the stream it runs on.  ``cpu_baseline`` times the float64
-oracle on a bounded sample of the same step on the host cores.
+oracle on a bounded sample of the same step on the host cores.  ``configs``
+adds the other synthetic workloads (tiny fp32 block, packed wavefronts,
+sparse 32K and 128K prefixes) operation by operation.
+
+``--only OP`` times one operation of the step (for counter runs) and
+``--copy-probe MB`` runs a plain device copy of known size, whose
+FETCH_SIZE / WRITE_SIZE counters scale the attention's.
 """
 from __future__ import annotations
 
@@ -135,6 +141,94 @@ def cpu_baseline(wl, budget_s: float = 12.0):
             "seconds": round(el, 2)}
 
 
+def time_calls(fn, reps: int, warmup: int = 2) -> float:
+    """Average milliseconds per call of ``fn`` (HIP events on the current
+    stream, which is the stream the library launches on)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        fn()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    return sum(ev[i].elapsed_time(ev[i + 1]) for i in range(reps)) / reps
+
+
+def _rate(num, ms, scale):
+    return round(num / (ms * 1e-3) / scale, 2)
+
+
+def bench_configs(dev, reps: int = 10):
+    """The other synthetic workloads, each in the launch configuration its
+    parity test checks: per-operation times and rates."""
+    import torch
+    import synth
+    from sparse_kv_cache_bd_amd import bdattn as bd
+    from sparse_kv_cache_bd_amd.pipeline import BlockDiffusionStep
+    out = {}
+
+    def kv_bytes(wl):
+        return wl.Hkv * wl.d * (2 if wl.dtype == "bf16" else 4)
+
+    for name in ("tiny_dense", "packed_wavefront"):
+        log(f"config {name}")
+        wl = getattr(synth, name)()
+        Kc, Vc, Q, o = (x.to(dev) for x in (wl.Kc, wl.Vc, wl.Q, wl.o))
+        step = BlockDiffusionStep(Kc, Vc, Q, o, wl.bl, wl.sm_scale, p_max_dense=int(wl.o.max()))
+        ms_a = time_calls(step.attn_dense, reps)
+        ms_s = time_calls(step.scatter, reps)
+        flop = attention_flops(wl.o, range(wl.B), wl.q, wl.bl, wl.Hq, wl.d)
+        sbytes = wl.B * wl.q * kv_bytes(wl) * 2 * 2
+        unit_peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else 157.3
+        out[name] = {"dtype": wl.dtype, "rows": wl.B, "q": wl.q,
+                     "attn_us": round(ms_a * 1e3, 2), "attn_TFLOP/s": _rate(flop, ms_a, 1e12),
+                     "attn_frac_peak": round(flop / (ms_a * 1e-3) / 1e12 / unit_peak, 4),
+                     "scatter_us": round(ms_s * 1e3, 2), "scatter_GB/s": _rate(sbytes, ms_s, 1e9)}
+        del step, Kc, Vc, Q, o
+
+    for name in ("sparse_32k", "sparse_128k"):
+        log(f"config {name}")
+        wl = getattr(synth, name)()
+        Kc, Vc = wl.Kc.to(dev), wl.Vc.to(dev)
+        Qsel = wl.Qsel.to(dev)
+        s_len, k_sel = wl.s_len.to(dev), wl.k_sel.to(dev)
+        B, Hkv, d, k_max, s_max = wl.B, wl.Hkv, wl.d, wl.k_max, wl.s_max
+        idx = torch.empty((B, Hkv, k_max), dtype=torch.int32, device=dev)
+        ws = bd.workspace(bd.select_workspace_size(B, wl.Hq, Hkv, d, s_max, k_max), dev)
+        pool_k = torch.zeros((B, k_max, Hkv, d), dtype=Kc.dtype, device=dev)
+        pool_v = torch.zeros_like(pool_k)
+        ms_sel = time_calls(lambda: bd.select(Qsel, Kc, s_len, s_max, k_sel, k_max, wl.sm_scale,
+                                              idx_out=idx, ws=ws), reps)
+        ms_gat = time_calls(lambda: bd.gather(Kc, Vc, idx, k_sel, pool_k, pool_v), reps)
+        steps_q = [x.to(dev) for x in wl.extra["step_q"]]
+        steps_kv = [(a.to(dev), b.to(dev)) for a, b in wl.extra["step_kv"]]
+        outb = torch.empty_like(steps_q[0])
+        ws_a = bd.workspace(bd.attn_workspace_size(Qsel.dtype, B, wl.Hq, Hkv, d, wl.q, B, k_max), dev)
+
+        def steps():
+            for st in range(wl.T):
+                wk, wv = steps_kv[st]
+                bd.attn_packed(steps_q[st], pool_k, pool_v, k_sel, k_max, wk, wv, wl.bl,
+                               wl.sm_scale, out=outb, ws=ws_a)
+        ms_att = time_calls(steps, max(2, reps // 2))
+        sel_bytes = sum(int(wl.s_len[b]) for b in range(B)) * kv_bytes(wl) + B * Hkv * k_max * 4
+        gat_bytes = sum(int(wl.k_sel[b]) for b in range(B)) * kv_bytes(wl) * 2 * 2
+        flop = wl.T * attention_flops(wl.k_sel, range(B), wl.q, wl.bl, wl.Hq, wl.d)
+        out[name] = {"rows": B, "prefix": s_max, "k": k_max, "T": wl.T,
+                     "select_us": round(ms_sel * 1e3, 2), "select_GB/s": _rate(sel_bytes, ms_sel, 1e9),
+                     "select_frac_hbm": round(sel_bytes / (ms_sel * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "gather_us": round(ms_gat * 1e3, 2), "gather_GB/s": _rate(gat_bytes, ms_gat, 1e9),
+                     "attn_us_per_step": round(ms_att * 1e3 / wl.T, 2),
+                     "attn_TFLOP/s": _rate(flop, ms_att, 1e12),
+                     "block_us": round((ms_sel + ms_gat + ms_att) * 1e3, 2)}
+        del Kc, Vc, pool_k, pool_v, ws, ws_a
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -143,6 +237,12 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--skip-configs", action="store_true",
+                    help="skip the per-configuration measurements of the other workloads")
+    ap.add_argument("--only", choices=["select", "gather", "attn_dense", "attn_sparse", "scatter"],
+                    help="time only this operation of the step (for counter runs); prints one line")
+    ap.add_argument("--copy-probe", type=int, metavar="MB",
+                    help="run a plain device copy of MB megabytes 5 times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
@@ -158,6 +258,15 @@ def main():
     bd.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe:
+        n = args.copy_probe * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"copy probe: 5 copies of {n * 4} bytes", flush=True)
+        return
     log("generating the serving-mix workload")
     wl = synth.serving_mix(seed=args.seed)
     Kc, Vc, Q, o = (x.to(dev) for x in (wl.Kc, wl.Vc, wl.Q, wl.o))
@@ -170,6 +279,10 @@ def main():
     for _ in range(args.warmup):
         step.run()
     torch.cuda.synchronize()
+    if args.only:
+        ms = time_calls(getattr(step, args.only), args.steps, 0)
+        print(f"{args.only}: {ms * 1e3:.1f} us per call over {args.steps} calls", flush=True)
+        return
 
     ops = BlockDiffusionStep.OPS
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(args.steps)]
@@ -219,11 +332,18 @@ def main():
                       "mb": round(work["scatter_bytes"] / 1e6, 2)}
 
     traffic = traffic_for_attention()
-    roof = {"bound": "mfma", "kernel": "attn_mfma_kernel<4> (dense rows)",
+    roof = {"bound": "mfma", "kernel": "attn_mfma_kernel<8, 4> (dense rows)",
             "achieved": round(tf_d, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tf_d / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
             "algorithmic_bytes": work["attn_dense_bytes"],
             "intensity_flop_per_byte": round(work["attn_dense_flop"] / work["attn_dense_bytes"], 1)}
+
+    n_dense, n_sparse = step.n_dense, step.n_sparse
+    configs = None
+    if not args.skip_configs:
+        del step, Kc, Vc, Q, o
+        torch.cuda.empty_cache()
+        configs = bench_configs(dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -234,11 +354,11 @@ def main():
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic",
-           "config": {"workload": "serving_mix", "rows": wl.B, "dense_rows": step.n_dense,
-                      "sparse_rows": step.n_sparse, "prefix": "log-uniform 1K-16K",
+           "config": {"workload": "serving_mix", "rows": wl.B, "dense_rows": n_dense,
+                      "sparse_rows": n_sparse, "prefix": "log-uniform 1K-16K",
                       "bl": wl.bl, "W": wl.W, "q": wl.q, "Hq": wl.Hq, "Hkv": wl.Hkv, "d": wl.d,
                       "C": wl.C, "budget": 0.05, "seed": args.seed},
-           "roofline": roof, "cpu_baseline": cpu, "breakdown": bd_}
+           "roofline": roof, "cpu_baseline": cpu, "breakdown": bd_, "configs": configs}
     print(json.dumps(res), flush=True)
 
 
