@@ -19,12 +19,15 @@
 //          are exactly the values that get ranked.  (No cross-block merge
 //          inside the scan: that needs device-scope fences, which write back
 //          and invalidate the L2 of the XCD on every block.)
-//   topk   one block per (row, KV head): exact radix select of the k-th
-//          largest score on its fp32 bit pattern (non-negative floats order
-//          like their bit patterns; digits of 11, 11 and 10 bits), then an
-//          ordered compaction: every score above the threshold plus the
-//          lowest-position ties, ascending, -1 padding.  Rows of up to
-//          kLdsKeys scores are read from memory once and kept in LDS.
+//   topk   exact radix select of the k-th largest score on its fp32 bit
+//          pattern (non-negative floats order like their bit patterns;
+//          digits of 11, 11 and 10 bits), then an ordered compaction: every
+//          score above the threshold plus the lowest-position ties,
+//          ascending, -1 padding.  Rows of up to kLdsKeys scores: one block
+//          per (row, KV head) with the scores read once into LDS.  Longer
+//          rows: blocks of kCK scores; the score pass histograms the first
+//          digit, two passes the others, then per-block counts and an
+//          ordered write.
 //
 // Histogram increments are aggregated per wave: lanes whose digit equals the
 // first active lane's digit add in one atomic (two rounds), so the strongly
@@ -42,18 +45,22 @@ constexpr int kBins = 2048;        // radix digit bins (11 bits)
 constexpr int kThreads = 256;
 constexpr int kTopkThreads = 1024;
 constexpr int kPerThread = 16;     // consecutive scores per thread in the compaction
-constexpr int kLdsKeys = 24576;    // scores of one (row, KV head) kept in LDS by topk
+constexpr int kLdsKeys = 32768;    // longest score row ranked by one block from LDS
+constexpr int kCK = 4096;          // scores per block of the multi-block ranking path
 constexpr int kZStr = kTS + 16;    // LDS row stride of the scan's z staging (floats)
 
 struct SelLayout {
-  size_t qhi, qlo, z, part, scores, total;
-  int nch_scan;
+  size_t qhi, qlo, z, part, scores, hist, ccount, total;
+  int nch_scan, nch_topk;
+  bool multi;  // rows longer than kLdsKeys: multi-block ranking
   int zs;  // row stride of z (s_max rounded up to 4: 16-byte aligned rows)
 };
 
 SelLayout sel_layout(int B, int Hq, int Hkv, int d, int s_max) {
   SelLayout L;
   L.nch_scan = (int)cdiv(s_max > 0 ? s_max : 1, kTS);
+  L.nch_topk = (int)cdiv(s_max > 0 ? s_max : 1, kCK);
+  L.multi = s_max > kLdsKeys;
   L.zs = (int)cdiv(s_max, 4) * 4;
   const size_t P = (size_t)B * Hkv;
   size_t off = 0;
@@ -63,6 +70,8 @@ SelLayout sel_layout(int B, int Hq, int Hkv, int d, int s_max) {
   L.z = take((size_t)B * Hq * (size_t)L.zs * 4);
   L.part = take((size_t)B * Hq * L.nch_scan * 2 * 4);
   L.scores = take(P * (size_t)s_max * 4);
+  L.hist = L.multi ? take(P * 3 * kBins * 4) : 0;
+  L.ccount = L.multi ? take(P * L.nch_topk * 2 * 4) : 0;
   L.total = off;
   return L;
 }
@@ -70,7 +79,9 @@ SelLayout sel_layout(int B, int Hq, int Hkv, int d, int s_max) {
 struct SelPtrs {
   bf16 *qhi, *qlo;
   float *z, *part, *scores;
-  int nch_scan, zs;
+  uint32_t *hist, *ccount;   // multi-block ranking: digit histograms, per-chunk counts
+  int nch_scan, zs, nch_topk;
+  bool multi;
 };
 
 __device__ inline void row_sizes(const SelectArgs &a, int b, int &S, int &kb) {
@@ -164,6 +175,11 @@ __global__ __launch_bounds__(kThreads) void sel_prep_kernel(SelectArgs a, SelPtr
     const bf16 lo = (bf16)(v - (float)hi);
     w.qhi[((int64_t)b * a.Hq + hq) * kSD + t] = hi;
     w.qlo[((int64_t)b * a.Hq + hq) * kSD + t] = lo;
+  }
+  if (w.multi) {  // this row's digit histograms (Hkv x 3 x kBins words)
+    const int words = a.Hkv * 3 * kBins;
+    uint32_t *hist = w.hist + (size_t)b * words;
+    for (int e = hq * kThreads + t; e < words; e += a.Hq * kThreads) hist[e] = 0;
   }
 }
 
@@ -343,9 +359,11 @@ __global__ __launch_bounds__(kThreads) void sel_score_kernel(SelectArgs a, SelPt
       }
     }
   }
+  __shared__ uint32_t hist[kBins];
+  if (w.multi)
+    for (int e = threadIdx.x; e < kBins; e += kThreads) hist[e] = 0;
   __syncthreads();
   const int s = c * kScoreTok + threadIdx.x * per;
-  if (s >= S) return;
   const bool full = s + per <= S;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int g = 0; g < a.G; ++g) {
@@ -371,11 +389,20 @@ __global__ __launch_bounds__(kThreads) void sel_score_kernel(SelectArgs a, SelPt
     for (int r = 0; r < per; ++r)
       if (s + r < S) op[r] = acc[r];
   }
+  if (w.multi) {  // first radix digit (bits 31..21) of the scores just written
+#pragma unroll
+    for (int r = 0; r < per; ++r) hist_add(hist, __float_as_uint(acc[r]) >> 21, s + r < S);
+    __syncthreads();
+    uint32_t *gh = w.hist + ((size_t)b * a.Hkv + h) * 3 * kBins;
+    for (int e = threadIdx.x; e < kBins; e += kThreads)
+      if (hist[e]) atomicAdd(&gh[e], hist[e]);
+  }
 }
 
 // ---------------------------------------------------------------- top-k
 // Digit D with count(digit > D) < krem <= count(digit >= D) over nb bins;
-// returns D and the rank left inside it.  One block of kTopkThreads.
+// returns D and the rank left inside it.  Called by every thread of a block
+// of 256 or 1024 threads.
 __device__ inline void find_digit(const uint32_t *cnt_of, int nb, uint32_t krem, int *sh,
                                   uint32_t &D, uint32_t &rem) {
   __shared__ uint32_t sd[2];
@@ -383,9 +410,9 @@ __device__ inline void find_digit(const uint32_t *cnt_of, int nb, uint32_t krem,
     sd[0] = 0;
     sd[1] = krem;
   }
-  const int per = nb / kTopkThreads;  // 2 or 1 bins per thread, descending
+  const int per = nb / (int)blockDim.x;  // 1 to 8 bins per thread, descending
   const int hi_bin = nb - 1 - threadIdx.x * per;
-  uint32_t cnt[2] = {0u, 0u};
+  uint32_t cnt[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
   int tsum = 0;
   for (int e = 0; e < per; ++e) {
     cnt[e] = cnt_of[hi_bin - e];
@@ -496,13 +523,156 @@ __global__ __launch_bounds__(kTopkThreads) void sel_topk_kernel(SelectArgs a, Se
   __shared__ int sh[16];
   __shared__ uint32_t cache[kLdsKeys];
   const uint32_t *keys = reinterpret_cast<const uint32_t *>(w.scores) + (size_t)p * a.s_max;
-  if (S <= kLdsKeys) {
-    for (int e = threadIdx.x; e < S; e += kTopkThreads) cache[e] = keys[e];
-    __syncthreads();
-    topk_body(cache, S, keff, out, hist, sh);
-  } else {
-    topk_body(keys, S, keff, out, hist, sh);
+  for (int e = threadIdx.x; e < S; e += kTopkThreads) cache[e] = keys[e];  // S <= kLdsKeys
+  __syncthreads();
+  topk_body(cache, S, keff, out, hist, sh);
+}
+
+// ------------------------------------------------------ multi-block ranking
+// Rows longer than kLdsKeys: blocks of kCK scores.  Each kernel recomputes
+// the digits fixed so far from the global histograms (kernel boundaries
+// order the histogram updates; no fences).
+
+// Threshold prefix and remaining rank after `passes` digits.
+__device__ inline void known_digits(const SelPtrs &w, int p, uint32_t keff, int passes, int *sh,
+                                    uint32_t &prefix, uint32_t &krem) {
+  prefix = 0;
+  krem = keff;
+  for (int d = 0; d < passes; ++d) {
+    uint32_t D;
+    find_digit(w.hist + ((size_t)p * 3 + d) * kBins, d == 2 ? 1024 : kBins, krem, sh, D, krem);
+    prefix |= D << (d == 0 ? 21 : (d == 1 ? 10 : 0));
   }
+}
+
+__device__ inline bool rank_sizes(const SelectArgs &a, int p, int c, int &S, int &keff) {
+  int kb;
+  row_sizes(a, p / a.Hkv, S, kb);
+  keff = min(S, kb);
+  return keff > 0 && keff < S && c * kCK < S;
+}
+
+// Histogram of digit PASS + 1 (bits 20..10, then 9..0) over one block of
+// scores whose higher digits match the threshold's.
+template <int PASS>
+__global__ __launch_bounds__(kThreads) void sel_hist_kernel(SelectArgs a, SelPtrs w) {
+  const int c = blockIdx.x, p = blockIdx.y;
+  int S, keff;
+  if (!rank_sizes(a, p, c, S, keff)) return;
+  __shared__ uint32_t hist[kBins];
+  __shared__ int sh[16];
+  uint32_t prefix, krem;
+  known_digits(w, p, (uint32_t)keff, PASS, sh, prefix, krem);
+  for (int e = threadIdx.x; e < kBins; e += kThreads) hist[e] = 0;
+  __syncthreads();
+  constexpr int shift = PASS == 1 ? 10 : 0;
+  constexpr uint32_t dmask = PASS == 1 ? 2047u : 1023u;
+  constexpr int hi_shift = PASS == 1 ? 21 : 10;
+  const uint32_t *keys = reinterpret_cast<const uint32_t *>(w.scores) + (size_t)p * a.s_max;
+  for (int e = 0; e < kCK / kThreads; ++e) {
+    const int s = c * kCK + e * kThreads + threadIdx.x;
+    const uint32_t key = s < S ? keys[s] : 0u;
+    hist_add(hist, (key >> shift) & dmask, s < S && (key >> hi_shift) == (prefix >> hi_shift));
+  }
+  __syncthreads();
+  uint32_t *gh = w.hist + ((size_t)p * 3 + PASS) * kBins;
+  for (int e = threadIdx.x; e < kBins; e += kThreads)
+    if (hist[e]) atomicAdd(&gh[e], hist[e]);
+}
+
+// Per block: scores above the threshold and equal to it.
+__global__ __launch_bounds__(kThreads) void sel_count_kernel(SelectArgs a, SelPtrs w) {
+  const int c = blockIdx.x, p = blockIdx.y;
+  int S, keff;
+  if (!rank_sizes(a, p, c, S, keff)) return;
+  __shared__ int sh[16];
+  uint32_t thr, krem;
+  known_digits(w, p, (uint32_t)keff, 3, sh, thr, krem);
+  const uint32_t *keys = reinterpret_cast<const uint32_t *>(w.scores) + (size_t)p * a.s_max;
+  int gt = 0, eq = 0;
+  for (int e = 0; e < kCK / kThreads; ++e) {
+    const int s = c * kCK + e * kThreads + threadIdx.x;
+    if (s < S) {
+      const uint32_t key = keys[s];
+      gt += key > thr;
+      eq += key == thr;
+    }
+  }
+  int tg, te;
+  block_excl_scan(gt, sh, tg);
+  block_excl_scan(eq, sh, te);
+  if (threadIdx.x == 0) {
+    w.ccount[((size_t)p * w.nch_topk + c) * 2 + 0] = (uint32_t)tg;
+    w.ccount[((size_t)p * w.nch_topk + c) * 2 + 1] = (uint32_t)te;
+  }
+}
+
+// Ordered compaction of one block: positions after every earlier block's
+// selections; ties by position up to the threshold's remaining rank.  Block 0
+// also writes the -1 padding.  Rows whose budget covers the whole prefix
+// select every position.
+__global__ __launch_bounds__(kThreads) void sel_write_kernel(SelectArgs a, SelPtrs w) {
+  const int c = blockIdx.x, p = blockIdx.y;
+  int S, kb;
+  row_sizes(a, p / a.Hkv, S, kb);
+  const int keff = min(S, kb);
+  int32_t *out = a.idx_out + (size_t)p * a.k_max;
+  if (c == 0)
+    for (int j = keff + threadIdx.x; j < a.k_max; j += kThreads) out[j] = -1;
+  if (keff == 0 || c * kCK >= S) return;
+  if (keff == S) {
+    for (int j = c * kCK + threadIdx.x; j < min(S, (c + 1) * kCK); j += kThreads) out[j] = j;
+    return;
+  }
+  __shared__ int sh[16];
+  uint32_t thr, krem;
+  known_digits(w, p, (uint32_t)keff, 3, sh, thr, krem);
+  const int need_eq = (int)krem;
+  int gtb = 0, eqb = 0;
+  for (int cc = threadIdx.x; cc < c; cc += kThreads) {
+    gtb += (int)w.ccount[((size_t)p * w.nch_topk + cc) * 2 + 0];
+    eqb += (int)w.ccount[((size_t)p * w.nch_topk + cc) * 2 + 1];
+  }
+  int gt_before, eq_before;
+  block_excl_scan(gtb, sh, gt_before);
+  block_excl_scan(eqb, sh, eq_before);
+  constexpr int per = kCK / kThreads;  // 16 consecutive scores per thread
+  const int s0 = c * kCK + threadIdx.x * per;
+  const uint32_t *keys = reinterpret_cast<const uint32_t *>(w.scores) + (size_t)p * a.s_max;
+  uint32_t kv[per];
+  int n_eq = 0;
+#pragma unroll
+  for (int e = 0; e < per; ++e) {
+    const int s = s0 + e;
+    kv[e] = s < S ? keys[s] : 0u;
+    n_eq += s < S && kv[e] == thr;
+  }
+  int tot;
+  int er = eq_before + block_excl_scan(n_eq, sh, tot);
+  int n_sel = 0;
+  uint32_t selbits = 0;
+#pragma unroll
+  for (int e = 0; e < per; ++e) {
+    const int s = s0 + e;
+    bool sel = false;
+    if (s < S) {
+      if (kv[e] > thr) {
+        sel = true;
+      } else if (kv[e] == thr) {
+        sel = er < need_eq;
+        ++er;
+      }
+    }
+    selbits |= (uint32_t)sel << e;
+    n_sel += sel;
+  }
+  int pos = gt_before + min(eq_before, need_eq) + block_excl_scan(n_sel, sh, tot);
+#pragma unroll
+  for (int e = 0; e < per; ++e)
+    if (selbits & (1u << e)) {
+      if (pos < keff) out[pos] = s0 + e;
+      ++pos;
+    }
 }
 
 }  // namespace
@@ -522,6 +692,10 @@ hipError_t launch_select(const SelectArgs &a, hipStream_t s) {
   w.scores = a.score_out ? a.score_out : reinterpret_cast<float *>(a.ws + L.scores);
   w.nch_scan = L.nch_scan;
   w.zs = L.zs;
+  w.nch_topk = L.nch_topk;
+  w.multi = L.multi;
+  w.hist = reinterpret_cast<uint32_t *>(a.ws + L.hist);
+  w.ccount = reinterpret_cast<uint32_t *>(a.ws + L.ccount);
   hipError_t e;
   hipLaunchKernelGGL(sel_prep_kernel, dim3(a.Hq, a.B), dim3(kThreads), 0, s, a, w);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -531,7 +705,15 @@ hipError_t launch_select(const SelectArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(sel_score_kernel, dim3((unsigned)cdiv(a.s_max, kScoreTok), a.Hkv, a.B),
                      dim3(kThreads), 0, s, a, w);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(sel_topk_kernel, dim3(a.B * a.Hkv), dim3(kTopkThreads), 0, s, a, w);
+  if (!L.multi) {
+    hipLaunchKernelGGL(sel_topk_kernel, dim3(a.B * a.Hkv), dim3(kTopkThreads), 0, s, a, w);
+    return hipGetLastError();
+  }
+  const dim3 tg(L.nch_topk, a.B * a.Hkv);
+  hipLaunchKernelGGL(sel_hist_kernel<1>, tg, dim3(kThreads), 0, s, a, w);
+  hipLaunchKernelGGL(sel_hist_kernel<2>, tg, dim3(kThreads), 0, s, a, w);
+  hipLaunchKernelGGL(sel_count_kernel, tg, dim3(kThreads), 0, s, a, w);
+  hipLaunchKernelGGL(sel_write_kernel, tg, dim3(kThreads), 0, s, a, w);
   return hipGetLastError();
 }
 

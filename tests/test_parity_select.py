@@ -121,3 +121,26 @@ def test_planted_keys_recalled(bd):
     _check(wl.Qsel, wl.Kc, wl.s_len, wl.k_sel, wl.sm_scale, idx, sc, k_max, label="planted")
     for (b, h), pos in wl.planted.items():
         assert set(pos.tolist()) <= set(idx[b, h].tolist())
+
+
+@pytest.mark.parametrize("S_list,k_list,dup", [
+    ([40000, 33000, 5000], [2000, 40, 5000], False),   # multi-block ranking; k = S row
+    ([36864, 100], [1843, 5], True),                   # exact ties at the threshold
+])
+def test_select_long_rows(bd, S_list, k_list, dup):
+    """Rows longer than one block's LDS score cache: ranked by blocks of 4096
+    scores (digit histograms in global memory, per-block counts, ordered
+    write), ragged last blocks, a row whose budget covers its prefix."""
+    note(f"select long rows S={S_list} k={k_list} dup={dup}")
+    B = len(S_list)
+    Q, K = _case(11 + int(dup), B, S_list, 16, 4, dup=dup)
+    scale = 1.0 / math.sqrt(128)
+    idx, sc, k_max = _run(bd, Q, K, S_list, k_list, scale)
+    _check(Q, K, S_list, k_list, scale, idx, sc, k_max, label="long")
+    for b, (S, k) in enumerate(zip(S_list, k_list)):
+        n = min(S, k)
+        assert (idx[b, :, n:] == -1).all()
+        assert (np.diff(idx[b, :, :n], axis=1) > 0).all()
+    if dup:
+        kth = np.sort(sc[0, 0, :S_list[0]])[::-1][k_list[0] - 1]
+        assert (sc[0, 0, :S_list[0]] == kth).sum() >= 2
