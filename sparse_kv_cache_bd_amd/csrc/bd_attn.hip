@@ -239,11 +239,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
   // ---- one tile: S^T = K Q^T, softmax, O^T += V^T P^T
   auto tile = [&](int tt, int buf) {
     f32x16 s[2];
+    // the two 32-key halves interleaved: two independent accumulator chains
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      s[kt] = f32x16{};
+    for (int ks = 0; ks < kD / 16; ++ks) {
 #pragma unroll
-      for (int ks = 0; ks < kD / 16; ++ks) {
+      for (int kt = 0; kt < 2; ++kt) {
         const bf16x8 kop = ld_bf16x8(&Ks[buf][(kt * 32 + ln) * kKStr + ks * 16 + hh * 8]);
         s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], s[kt], 0, 0, 0);
       }
@@ -292,10 +294,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
         pop[r >> 3][r & 7] = (bf16)p;
       }
       l_run += rs;
+      // k-steps outer: four independent accumulators between dependent MFMAs
 #pragma unroll
-      for (int dt = 0; dt < kD / 32; ++dt) {
+      for (int k2 = 0; k2 < 2; ++k2) {
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
+        for (int dt = 0; dt < kD / 32; ++dt) {
           const bf16x8 vop = ld_bf16x8(&Vt[buf][(dt * 32 + ln) * kVStr + kt * 32 + k2 * 16 + hh * 8]);
           acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[k2], acc[dt], 0, 0, 0);
         }
@@ -541,7 +544,7 @@ bool attn_generic_supported(int dtype, int d) {
 // 512 bytes per column.  Rows are ordered longest first when the blocks do
 // not all fit at once.
 constexpr int kCUs = 256;
-constexpr int kMinChunk = 512;
+constexpr int kMinChunk = 256;
 
 AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int d, int q, int n_rows, int p_max) {
   (void)B;
