@@ -39,7 +39,7 @@ namespace bd {
 namespace {
 
 constexpr int kSD = 128;           // head dim of the selection path
-constexpr int kTS = 256;           // tokens per scan block
+constexpr int kTS = 128;           // tokens per scan block
 constexpr int kScoreTok = 1024;    // tokens per score block
 constexpr int kBins = 2048;        // radix digit bins (11 bits)
 constexpr int kThreads = 256;
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void sel_prep_kernel(SelectArgs a, SelPtr
 // ------------------------------------------------------------------- scan
 // Block = (token chunk of kTS, row).  Wave w handles KV heads w, w+4, ...;
 // its work is a flat list of (head, 64-token group) items.  The 16 loads of
-// 16 bytes per lane of item i+1 are issued before the MFMAs of item i.  The
+// 16 bytes per lane of items i+1 and i+2 are in flight during item i.  The
 // row's q_rep hi / lo parts are staged in LDS once per block.
 __global__ __launch_bounds__(kThreads, 2) void sel_scan_kernel(SelectArgs a, SelPtrs w) {
   const int c = blockIdx.x, b = blockIdx.y;
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(kThreads, 2) void sel_scan_kernel(SelectArgs a, Sel
   auto item_head = [&](int i) { return wave + (kThreads / 64) * (i / n_groups); };
   auto item_t0 = [&](int i) { return s0 + 64 * (i % n_groups); };
 
-  bf16x8 abuf[2][4][kSD / 32];
+  bf16x8 abuf[3][4][kSD / 32];
   auto load = [&](int i, bf16x8 (&dst)[4][kSD / 32]) {
     const int h = item_head(i), t0 = item_t0(i);
     const bf16 *kbase = a.k + (int64_t)b * a.ks[0] + (int64_t)h * a.ks[2] + grp * 8;
@@ -294,15 +294,23 @@ __global__ __launch_bounds__(kThreads, 2) void sel_scan_kernel(SelectArgs a, Sel
     if (i % n_groups == n_groups - 1) flush(h);
   };
 
-  if (n_items > 0) load(0, abuf[0]);
+  // three groups in flight: loads of items i+1 and i+2 overlap item i
+  // (unconditional loads, clamped to the last item: exact wait counts)
+  if (n_items > 0) {
+    load(0, abuf[0]);
+    load(min(1, n_items - 1), abuf[1]);
+  }
   int i = 0;
-  for (; i + 1 < n_items; i += 2) {
-    load(i + 1, abuf[1]);
+  for (; i + 2 < n_items; i += 3) {
+    load(i + 2, abuf[2]);
     compute(i, abuf[0]);
-    load(min(i + 2, n_items - 1), abuf[0]);   // unconditional: keeps the wait counts exact
+    load(min(i + 3, n_items - 1), abuf[0]);
     compute(i + 1, abuf[1]);
+    load(min(i + 4, n_items - 1), abuf[1]);
+    compute(i + 2, abuf[2]);
   }
   if (i < n_items) compute(i, abuf[0]);
+  if (i + 1 < n_items) compute(i + 1, abuf[1]);
 
   // z and (max, sum) of the chunk to global memory: 16-byte stores,
   // consecutive threads on consecutive tokens of one query head
@@ -438,6 +446,10 @@ __device__ inline void find_digit(const uint32_t *cnt_of, int nb, uint32_t krem,
 }
 
 // Radix select + ordered compaction over keys[0, S) (LDS or global memory).
+// Scores cached in LDS with one pad word per 16 (no bank conflicts when a
+// thread walks 16 consecutive scores, or when lanes walk consecutive ones).
+__device__ inline int cpos(int s) { return s + (s >> 4); }
+
 __device__ inline void topk_body(const uint32_t *keys, int S, int keff, int32_t *out, uint32_t *hist,
                                  int *sh) {
   uint32_t prefix = 0, krem = (uint32_t)keff;
@@ -450,9 +462,13 @@ __device__ inline void topk_body(const uint32_t *keys, int S, int keff, int32_t 
     __syncthreads();
     for (int s0 = 0; s0 < S; s0 += kTopkThreads) {
       const int s = s0 + threadIdx.x;
-      const uint32_t key = s < S ? keys[s] : 0u;
-      const bool match = s < S && (pass == 0 || (key >> hi_shift) == (prefix >> hi_shift));
-      hist_add(hist, (key >> shift) & dmask, match);
+      const uint32_t key = s < S ? keys[cpos(s)] : 0u;
+      if (pass == 0) {
+        // the first digit is dominated by the exponent: aggregate per wave
+        hist_add(hist, (key >> shift) & dmask, s < S);
+      } else if (s < S && (key >> hi_shift) == (prefix >> hi_shift)) {
+        atomicAdd(&hist[(key >> shift) & dmask], 1u);
+      }
     }
     __syncthreads();
     uint32_t D;
@@ -471,7 +487,7 @@ __device__ inline void topk_body(const uint32_t *keys, int S, int keff, int32_t 
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) {
       const int s = sb + e;
-      kv[e] = s < S ? keys[s] : 0u;
+      kv[e] = s < S ? keys[cpos(s)] : 0u;
       n_eq += s < S && kv[e] == thr;
     }
     int tot_eq;
@@ -521,9 +537,9 @@ __global__ __launch_bounds__(kTopkThreads) void sel_topk_kernel(SelectArgs a, Se
   }
   __shared__ uint32_t hist[kBins];
   __shared__ int sh[16];
-  __shared__ uint32_t cache[kLdsKeys];
+  __shared__ uint32_t cache[kLdsKeys + kLdsKeys / 16];
   const uint32_t *keys = reinterpret_cast<const uint32_t *>(w.scores) + (size_t)p * a.s_max;
-  for (int e = threadIdx.x; e < S; e += kTopkThreads) cache[e] = keys[e];  // S <= kLdsKeys
+  for (int e = threadIdx.x; e < S; e += kTopkThreads) cache[cpos(e)] = keys[e];  // S <= kLdsKeys
   __syncthreads();
   topk_body(cache, S, keff, out, hist, sh);
 }
