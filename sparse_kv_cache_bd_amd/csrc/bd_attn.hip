@@ -253,23 +253,27 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
     const int base = tile_base(tt), limit = tile_limit(tt);
     const bool win = tt >= n_pref;
     if (win || base + kTK > limit) {
-      const int vlim = win ? lim : limit;
+      // register r of half kt holds key base + kt*32 + (r/4)*8 + hh*4 + r%4;
+      // the lane part goes into the threshold so the offsets are immediates
+      const int thr = (win ? lim : limit) - base - hh * 4;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = base + kt * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-          if (key >= vlim) s[kt][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (kt * 32 + (r >> 2) * 8 + (r & 3) >= thr) s[kt][r] = -INFINITY;
     }
     // column max of the tile; the reference max is raised only when the
     // tile's max exceeds it by more than 2^8
-    float mx = s[0][0];
+    // (pairwise trees: short dependency chains between the S MFMAs and the
+    // exponentials)
+    float m16[16];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int r = 0; r < 16; ++r) m16[r] = fmaxf(s[0][r], s[1][r]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-    mx = fmaxf(mx, xor32(mx)) * a.scale2;
+    for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+      for (int r = 0; r < w; ++r) m16[r] = fmaxf(m16[r], m16[r + w]);
+    const float mx = fmaxf(m16[0], xor32(m16[0])) * a.scale2;
     const bool up = mx > m_run + kRescaleSlack;
     if (__ballot(up)) {
       const float m_new = up ? mx : m_run;
@@ -286,14 +290,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
     for (int kt = 0; kt < 2; ++kt) {
       // p = exp2(score * scale2 - m); masked scores are -inf and give 0
       bf16x8 pop[2];
-      float rs = 0.f;
+      float ps[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], a.scale2, neg_m));
-        rs += p;
-        pop[r >> 3][r & 7] = (bf16)p;
+        ps[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], a.scale2, neg_m));
+        pop[r >> 3][r & 7] = (bf16)ps[r];
       }
-      l_run += rs;
+#pragma unroll
+      for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+        for (int r = 0; r < w; ++r) ps[r] += ps[r + w];
+      l_run += ps[0];
       // k-steps outer: four independent accumulators between dependent MFMAs
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
