@@ -39,7 +39,7 @@ namespace bd {
 namespace {
 
 constexpr int kSD = 128;           // head dim of the selection path
-constexpr int kTS = 128;           // tokens per scan block
+constexpr int kTS = 256;           // tokens per scan block
 constexpr int kScoreTok = 1024;    // tokens per score block
 constexpr int kBins = 2048;        // radix digit bins (11 bits)
 constexpr int kThreads = 256;
@@ -156,10 +156,19 @@ __global__ __launch_bounds__(kThreads) void sel_prep_kernel(SelectArgs a, SelPtr
       for (int e = 0; e < 8; ++e) acc[e] = (float)v[e];
     }
   } else {
-    for (int i = qs; i < a.nq; i += 16) {
-      const bf16x8 v = *reinterpret_cast<const bf16x8 *>(qp + (int64_t)i * a.qs[1]);
+    // 8 loads in flight per round; summed in query order
+    for (int i0 = qs; i0 < a.nq; i0 += 16 * 8) {
+      bf16x8 v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += (float)v[e];
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + 16 * u;
+        v[u] = i < a.nq ? *reinterpret_cast<const bf16x8 *>(qp + (int64_t)i * a.qs[1]) : bf16x8{};
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (i0 + 16 * u < a.nq)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] += (float)v[u][e];
     }
   }
   __shared__ float part[16][kSD + 4];
@@ -358,7 +367,17 @@ __global__ __launch_bounds__(kThreads) void sel_score_kernel(SelectArgs a, SelPt
     for (int g = wv; g < a.G; g += kThreads / 64) {
       const float *pp = w.part + ((int64_t)b * a.Hq + h * a.G + g) * w.nch_scan * 2;
       float M = -INFINITY, L = 0.f;
-      for (int cc = ln; cc < nch; cc += 64) merge_ml(M, L, pp[cc * 2], pp[cc * 2 + 1]);
+      for (int c0 = ln; c0 < nch; c0 += 64 * 8) {  // 8 loads in flight, merged in order
+        float2 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int cc = c0 + 64 * u;
+          v[u] = cc < nch ? *reinterpret_cast<const float2 *>(pp + cc * 2) : float2{-INFINITY, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (c0 + 64 * u < nch) merge_ml(M, L, v[u].x, v[u].y);
+      }
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) merge_ml(M, L, __shfl_xor(M, o), __shfl_xor(L, o));
       if (ln == 0) {
@@ -374,20 +393,30 @@ __global__ __launch_bounds__(kThreads) void sel_score_kernel(SelectArgs a, SelPt
   const int s = c * kScoreTok + threadIdx.x * per;
   const bool full = s + per <= S;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int g = 0; g < a.G; ++g) {
-    const int hq = h * a.G + g;
-    const float M = st_m[g];
-    const float inv_l = st_il[g];
-    const float *zp = w.z + ((int64_t)b * a.Hq + hq) * w.zs + s;
-    f32x4 z;
-    if (full) {
-      z = *reinterpret_cast<const f32x4 *>(zp);
-    } else {
+  // z of every query head of the group loaded first (G <= 8), then summed
+  // over the heads in order
+  f32x4 zg[8];
 #pragma unroll
-      for (int r = 0; r < per; ++r) z[r] = (s + r < S) ? zp[r] : 0.f;
+  for (int g = 0; g < 8; ++g) {
+    zg[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (g < a.G) {
+      const float *zp = w.z + ((int64_t)b * a.Hq + h * a.G + g) * w.zs + s;
+      if (full) {
+        zg[g] = *reinterpret_cast<const f32x4 *>(zp);
+      } else {
+#pragma unroll
+        for (int r = 0; r < per; ++r) zg[g][r] = (s + r < S) ? zp[r] : 0.f;
+      }
     }
+  }
 #pragma unroll
-    for (int r = 0; r < per; ++r) acc[r] += __builtin_amdgcn_exp2f(z[r] - M) * inv_l;
+  for (int g = 0; g < 8; ++g) {
+    if (g < a.G) {
+      const float M = st_m[g];
+      const float inv_l = st_il[g];
+#pragma unroll
+      for (int r = 0; r < per; ++r) acc[r] += __builtin_amdgcn_exp2f(zg[g][r] - M) * inv_l;
+    }
   }
   float *op = w.scores + ((int64_t)b * a.Hkv + h) * a.s_max + s;
   if (full && ((uintptr_t)op & 15) == 0) {
@@ -422,10 +451,11 @@ __device__ inline void find_digit(const uint32_t *cnt_of, int nb, uint32_t krem,
   const int hi_bin = nb - 1 - threadIdx.x * per;
   uint32_t cnt[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
   int tsum = 0;
-  for (int e = 0; e < per; ++e) {
-    cnt[e] = cnt_of[hi_bin - e];
-    tsum += (int)cnt[e];
-  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (e < per) cnt[e] = cnt_of[hi_bin - e];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) tsum += (int)cnt[e];
   int total;
   const int before = block_excl_scan(tsum, sh, total);
   if ((uint32_t)before < krem && krem <= (uint32_t)(before + tsum)) {
@@ -539,7 +569,20 @@ __global__ __launch_bounds__(kTopkThreads) void sel_topk_kernel(SelectArgs a, Se
   __shared__ int sh[16];
   __shared__ uint32_t cache[kLdsKeys + kLdsKeys / 16];
   const uint32_t *keys = reinterpret_cast<const uint32_t *>(w.scores) + (size_t)p * a.s_max;
-  for (int e = threadIdx.x; e < S; e += kTopkThreads) cache[cpos(e)] = keys[e];  // S <= kLdsKeys
+  // S <= kLdsKeys; 16 loads in flight per thread
+  for (int e0 = threadIdx.x; e0 < S; e0 += kTopkThreads * 16) {
+    uint32_t v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = e0 + kTopkThreads * u;
+      v[u] = e < S ? keys[e] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = e0 + kTopkThreads * u;
+      if (e < S) cache[cpos(e)] = v[u];
+    }
+  }
   __syncthreads();
   topk_body(cache, S, keff, out, hist, sh);
 }
@@ -585,9 +628,16 @@ __global__ __launch_bounds__(kThreads) void sel_hist_kernel(SelectArgs a, SelPtr
   constexpr uint32_t dmask = PASS == 1 ? 2047u : 1023u;
   constexpr int hi_shift = PASS == 1 ? 21 : 10;
   const uint32_t *keys = reinterpret_cast<const uint32_t *>(w.scores) + (size_t)p * a.s_max;
+  uint32_t kv[kCK / kThreads];  // all loads in flight before the histogram updates
+#pragma unroll
   for (int e = 0; e < kCK / kThreads; ++e) {
     const int s = c * kCK + e * kThreads + threadIdx.x;
-    const uint32_t key = s < S ? keys[s] : 0u;
+    kv[e] = s < S ? keys[s] : 0u;
+  }
+#pragma unroll
+  for (int e = 0; e < kCK / kThreads; ++e) {
+    const int s = c * kCK + e * kThreads + threadIdx.x;
+    const uint32_t key = kv[e];
     hist_add(hist, (key >> shift) & dmask, s < S && (key >> hi_shift) == (prefix >> hi_shift));
   }
   __syncthreads();
@@ -606,12 +656,18 @@ __global__ __launch_bounds__(kThreads) void sel_count_kernel(SelectArgs a, SelPt
   known_digits(w, p, (uint32_t)keff, 3, sh, thr, krem);
   const uint32_t *keys = reinterpret_cast<const uint32_t *>(w.scores) + (size_t)p * a.s_max;
   int gt = 0, eq = 0;
+  uint32_t kv[kCK / kThreads];
+#pragma unroll
+  for (int e = 0; e < kCK / kThreads; ++e) {
+    const int s = c * kCK + e * kThreads + threadIdx.x;
+    kv[e] = s < S ? keys[s] : 0u;
+  }
+#pragma unroll
   for (int e = 0; e < kCK / kThreads; ++e) {
     const int s = c * kCK + e * kThreads + threadIdx.x;
     if (s < S) {
-      const uint32_t key = keys[s];
-      gt += key > thr;
-      eq += key == thr;
+      gt += kv[e] > thr;
+      eq += kv[e] == thr;
     }
   }
   int tg, te;
@@ -734,3 +790,4 @@ hipError_t launch_select(const SelectArgs &a, hipStream_t s) {
 }
 
 }  // namespace bd
+
