@@ -451,8 +451,9 @@ constexpr int kQT = 32;  // queries per block
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a) {
   constexpr int DL = D / 8;  // dims per lane
-  __shared__ float Kt[kGenKeys][D + 1];
-  __shared__ float Vt_[kGenKeys][D + 1];
+  constexpr int EPT = kGenKeys * D / 256;  // tile elements staged per thread
+  __shared__ float Kt[2][kGenKeys][D + 1];
+  __shared__ float Vt_[2][kGenKeys][D + 1];
   const int tid = threadIdx.x;
   const int ql = tid >> 3;   // query inside tile
   const int sub = tid & 7;   // dimension slice
@@ -487,28 +488,54 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a) {
   const T *wvb = reinterpret_cast<const T *>(a.wv) + (int64_t)b * a.ws[0] + (int64_t)h * a.ws[2];
   const int npt = (int)cdiv(P, kGenKeys);
   const int nwt = (int)cdiv(win_len, kGenKeys);
-  for (int tile = 0; tile < npt + nwt; ++tile) {
+  const int ntile = npt + nwt;
+  // staging: element tid + 256 i of the tile (consecutive threads on
+  // consecutive dims), every load of a tile in flight together; tile t+1 is
+  // loaded while tile t is computed (LDS double buffer)
+  float kreg[EPT], vreg[EPT];
+  auto gload = [&](int tile) {
     const bool win = tile >= npt;
     const int base = win ? (tile - npt) * kGenKeys : tile * kGenKeys;
     const int limit = win ? win_len : P;
     const T *kb = win ? wkb : pkb;
     const T *vb = win ? wvb : pvb;
     const int64_t sp = win ? a.ws[1] : a.ps[1];
-    __syncthreads();
-    for (int e = tid; e < kGenKeys * D; e += 256) {
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int e = tid + 256 * i;
       const int key = e / D, dd = e - key * D;
       const int gk = base + key;
       const bool ok = gk < limit;
-      Kt[key][dd] = ok ? (float)kb[(int64_t)gk * sp + dd] : 0.f;
-      Vt_[key][dd] = ok ? (float)vb[(int64_t)gk * sp + dd] : 0.f;
+      kreg[i] = ok ? (float)kb[(int64_t)gk * sp + dd] : 0.f;
+      vreg[i] = ok ? (float)vb[(int64_t)gk * sp + dd] : 0.f;
     }
-    __syncthreads();
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int e = tid + 256 * i;
+      const int key = e / D, dd = e - key * D;
+      Kt[buf][key][dd] = kreg[i];
+      Vt_[buf][key][dd] = vreg[i];
+    }
+  };
+  if (ntile > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+  for (int tile = 0; tile < ntile; ++tile) {
+    const int buf = tile & 1;
+    if (tile + 1 < ntile) gload(tile + 1);
+    const bool win = tile >= npt;
+    const int base = win ? (tile - npt) * kGenKeys : tile * kGenKeys;
+    const int limit = win ? win_len : P;
     const int vlim = win ? lim_i : limit;
     const int nk = min(kGenKeys, limit - base);
     for (int key = 0; key < nk; ++key) {
       float dot = 0.f;
 #pragma unroll
-      for (int e = 0; e < DL; ++e) dot += qv[e] * Kt[key][sub * DL + e];
+      for (int e = 0; e < DL; ++e) dot += qv[e] * Kt[buf][key][sub * DL + e];
       dot += __shfl_xor(dot, 1);
       dot += __shfl_xor(dot, 2);
       dot += __shfl_xor(dot, 4);
@@ -519,9 +546,11 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a) {
       const float p = exp2f(sc - m_new);
       l_run = l_run * alpha + p;
 #pragma unroll
-      for (int e = 0; e < DL; ++e) o[e] = o[e] * alpha + p * Vt_[key][sub * DL + e];
+      for (int e = 0; e < DL; ++e) o[e] = o[e] * alpha + p * Vt_[buf][key][sub * DL + e];
       m_run = m_new;
     }
+    if (tile + 1 < ntile) lstore(buf ^ 1);
+    __syncthreads();
   }
   if (!q_ok) return;
   T *op = reinterpret_cast<T *>(a.out) + (int64_t)b * a.os[0] + (int64_t)qi * a.os[1] +
