@@ -237,18 +237,42 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
   float l_run = 0.f;        // this lane's share of sum exp2(score - m_run)
 
   // ---- one tile: S^T = K Q^T, softmax, O^T += V^T P^T
+  // fragment reads run kFragAhead MFMAs ahead of their use (rolling window,
+  // fully unrolled; the order is pinned with sched_group_barrier, since the
+  // scheduler otherwise moves each read next to its MFMA), so the LDS
+  // latency is covered inside the wave.  3 to 5 measure the same; 6 is
+  // slower.
+  constexpr int kFragAhead = 4;
+  auto kfrag = [&](int buf, int i) {  // K fragment i = ks * 2 + kt
+    return ld_bf16x8(&Ks[buf][((i & 1) * 32 + ln) * kKStr + (i >> 1) * 16 + hh * 8]);
+  };
+  auto vfrag = [&](int buf, int j) {  // V^T fragment j = kt * 8 + k2 * 4 + dt
+    return ld_bf16x8(&Vt[buf][((j & 3) * 32 + ln) * kVStr + (j >> 3) * 32 + ((j >> 2) & 1) * 16 + hh * 8]);
+  };
   auto tile = [&](int tt, int buf) {
     f32x16 s[2];
     // the two 32-key halves interleaved: two independent accumulator chains
     s[0] = f32x16{};
     s[1] = f32x16{};
+    bf16x8 kf[16];
 #pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks) {
+    for (int i = 0; i < kFragAhead; ++i) kf[i] = kfrag(buf, i);
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 kop = ld_bf16x8(&Ks[buf][(kt * 32 + ln) * kKStr + ks * 16 + hh * 8]);
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], s[kt], 0, 0, 0);
-      }
+    for (int i = 0; i < 16; ++i) {
+      if (i + kFragAhead < 16) kf[i + kFragAhead] = kfrag(buf, i + kFragAhead);
+      s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qop[i >> 1], s[i & 1], 0, 0, 0);
+    }
+    // the first V^T fragments are read while the softmax runs
+    bf16x8 vf[16];
+#pragma unroll
+    for (int j = 0; j < kFragAhead; ++j) vf[j] = vfrag(buf, j);
+    // schedule: kFragAhead reads, then (1 MFMA, 1 read) x 16 (the last
+    // kFragAhead reads are the V^T prefetches)
+    __builtin_amdgcn_sched_group_barrier(0x100, kFragAhead, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     const int base = tile_base(tt), limit = tile_limit(tt);
     const bool win = tt >= n_pref;
@@ -306,10 +330,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
       for (int k2 = 0; k2 < 2; ++k2) {
 #pragma unroll
         for (int dt = 0; dt < kD / 32; ++dt) {
-          const bf16x8 vop = ld_bf16x8(&Vt[buf][(dt * 32 + ln) * kVStr + kt * 32 + k2 * 16 + hh * 8]);
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[k2], acc[dt], 0, 0, 0);
+          const int j = kt * 8 + k2 * 4 + dt;
+          if (j + kFragAhead < 16) vf[j + kFragAhead] = vfrag(buf, j + kFragAhead);
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], pop[k2], acc[dt], 0, 0, 0);
         }
       }
+    }
+    // schedule of the P V part: (1 MFMA, 1 read) for the reads still to
+    // issue, then the last MFMAs; the exponentials fill in around them
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (j + kFragAhead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
 
