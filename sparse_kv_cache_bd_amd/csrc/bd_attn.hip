@@ -331,17 +331,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
 #pragma unroll
         for (int dt = 0; dt < kD / 32; ++dt) {
           const int j = kt * 8 + k2 * 4 + dt;
-          if (j + kFragAhead < 16) vf[j + kFragAhead] = vfrag(buf, j + kFragAhead);
           acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], pop[k2], acc[dt], 0, 0, 0);
+          if (j + kFragAhead < 16) vf[j + kFragAhead] = vfrag(buf, j + kFragAhead);
+          // MFMAs and LDS reads keep this order (read j+4 after MFMA j);
+          // VALU, SALU and transcendental work may move across
+          __builtin_amdgcn_sched_barrier(0x406);
         }
       }
-    }
-    // schedule of the P V part: (1 MFMA, 1 read) for the reads still to
-    // issue, then the last MFMAs; the exponentials fill in around them
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (j + kFragAhead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
 
