@@ -4,8 +4,8 @@
 //   prep   q_rep = mean (or one row) of the block queries, pre-scaled by
 //          sm_scale*log2(e) and split into bf16 hi + lo parts.
 //   scan   z[hq, s] = <q_rep[hq], K[s, h]> for s < S_b: streams the K cache
-//          once with 16-byte loads; the loads of the next 64-token group are
-//          in flight while the current group is computed.  Tokens are the
+//          once with 16-byte loads; the loads of the next two 64-token
+//          groups are in flight while the current group is computed.  Tokens are the
 //          rows of v_mfma_f32_16x16x32_bf16 and the G query heads of a KV
 //          head its columns (q_rep hi and lo accumulate into the same fp32
 //          result, so the query keeps ~16 mantissa bits while K stays bf16);
