@@ -49,6 +49,9 @@ constexpr int kKTile = kTK * kKStr;
 constexpr int kVTile = kD * kVStr;
 constexpr float kRescaleSlack = 8.f;  // log2 units
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+struct bf16x2x4 { bf16x2 v[4]; };
+
 __device__ inline bf16x8 ld_bf16x8(const bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 
 // LDS slot of key k16 (0..15) inside a 16-key group of V^T: bits 2 and 3
@@ -234,7 +237,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
 #pragma unroll
   for (int dt = 0; dt < kD / 32; ++dt) acc[dt] = f32x16{};
   float m_run = -INFINITY;  // reference max of scaled scores (log2 units)
-  float l_run = 0.f;        // this lane's share of sum exp2(score - m_run)
+  // this lane's share of the softmax denominator, in four partial sums.  It
+  // sums the bf16-rounded weights the P V MFMAs use (bf16 dot products with
+  // ones), so the weights applied to V sum to one.
+  float l4[4] = {0.f, 0.f, 0.f, 0.f};
+  const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
 
   // ---- one tile: S^T = K Q^T, softmax, O^T += V^T P^T
   // fragment reads run kFragAhead MFMAs ahead of their use (rolling window,
@@ -290,20 +297,26 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
     // tile's max exceeds it by more than 2^8
     // (pairwise trees: short dependency chains between the S MFMAs and the
     // exponentials)
-    float m16[16];
+    // (three-input maxima: 32 -> 11 -> 4 -> 1)
+    float m11[11], m4[4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) m16[r] = fmaxf(s[0][r], s[1][r]);
+    for (int r = 0; r < 10; ++r) {
+      const int e = 3 * r;
+      m11[r] = fmaxf(fmaxf(s[e >> 4][e & 15], s[(e + 1) >> 4][(e + 1) & 15]), s[(e + 2) >> 4][(e + 2) & 15]);
+    }
+    m11[10] = fmaxf(s[1][14], s[1][15]);
 #pragma unroll
-    for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-      for (int r = 0; r < w; ++r) m16[r] = fmaxf(m16[r], m16[r + w]);
-    const float mx = fmaxf(m16[0], xor32(m16[0])) * a.scale2;
+    for (int r = 0; r < 3; ++r) m4[r] = fmaxf(fmaxf(m11[3 * r], m11[3 * r + 1]), m11[3 * r + 2]);
+    m4[3] = fmaxf(m11[9], m11[10]);
+    const float m1 = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+    const float mx = fmaxf(m1, xor32(m1)) * a.scale2;
     const bool up = mx > m_run + kRescaleSlack;
     if (__ballot(up)) {
       const float m_new = up ? mx : m_run;
       const float alpha = up ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
       m_run = m_new;
-      l_run *= alpha;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) l4[e] *= alpha;
 #pragma unroll
       for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll
@@ -314,17 +327,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
     for (int kt = 0; kt < 2; ++kt) {
       // p = exp2(score * scale2 - m); masked scores are -inf and give 0
       bf16x8 pop[2];
-      float ps[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        ps[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], a.scale2, neg_m));
-        pop[r >> 3][r & 7] = (bf16)ps[r];
+      for (int r = 0; r < 16; ++r)
+        pop[r >> 3][r & 7] = (bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], a.scale2, neg_m));
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const bf16x2x4 pp = __builtin_bit_cast(bf16x2x4, pop[k2]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) l4[e] = __builtin_amdgcn_fdot2_f32_bf16(pp.v[e], ones, l4[e], false);
       }
-#pragma unroll
-      for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-        for (int r = 0; r < w; ++r) ps[r] += ps[r + w];
-      l_run += ps[0];
       // k-steps outer: four independent accumulators between dependent MFMAs
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
@@ -362,6 +373,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
   }
 
   // ---- epilogue
+  float l_run = (l4[0] + l4[1]) + (l4[2] + l4[3]);
   l_run += xor32(l_run);
   if (it.nc == 1) {
     if (!qok) return;
