@@ -4,17 +4,19 @@ One step = one pass of every operation of the path over one batch of the
 64-row serving mix (log-uniform prefixes 1K-16K, W = 4 windows of 32-token
 blocks, 32/8 heads, d = 128, bf16): selection + gather for the rows whose
 prefix exceeds 8K (5 % budget), W-shaped attention of the dense rows over
-their own cache and of the sparse rows over their pools, and the KV
-write-back scatter of every row.  Inputs are resident in HBM before the
-timed region.
+their own cache and of the sparse rows over their pools (one launch for
+both), and the KV write-back scatter of every row.  Inputs are resident in
+HBM before the timed region.
 
 Prints one JSON line.  ``value`` is the whole-step throughput in attention
 TFLOP/s: the algorithmic attention FLOPs of the step (4*d per visible
 (query, key) pair per query head) divided by the step time, select, gather
 and scatter included.  ``breakdown`` gives each operation's own rate
 (TFLOP/s or GB/s of algorithmic bytes) and fraction of the MI355X peak.
-``roofline`` reports the dominant kernel (dense-row attention), timed with
-HIP events on the stream it runs on.  ``cpu_baseline`` times the float64
+``roofline`` reports the dominant kernel (the attention launch over all
+rows), timed with HIP events on the stream it runs on; ``attn_dense`` and
+``attn_sparse`` in ``breakdown`` time the two row kinds as separate
+launches for reference.  ``cpu_baseline`` times the float64
 oracle on a bounded sample of the same step on the host cores.  ``configs``
 adds the other synthetic workloads (tiny fp32 block, packed wavefronts,
 sparse 32K and 128K prefixes) operation by operation.
@@ -66,13 +68,15 @@ def step_work(wl):
     w["select_bytes"] = sum(int(wl.s_len[b]) * tok for b in sparse) + len(sparse) * Hkv * wl.k_max * 4
     w["gather_bytes"] = sum(int(wl.k_sel[b]) * tok * 2 * 2 for b in sparse)
     w["scatter_bytes"] = wl.B * q * tok * 2 * 2
-    # bytes the dense attention must move at least once: Q, O, prefix + window K/V
+    # bytes the attention must move at least once: Q, O, prefix (cache or
+    # pool) + window K/V
     w["attn_dense_bytes"] = sum(q * Hq * d * es * 2 + (int(wl.o[b]) + q) * tok * 2 for b in dense)
+    w["attn_sparse_bytes"] = sum(q * Hq * d * es * 2 + (int(wl.k_sel[b]) + q) * tok * 2 for b in sparse)
     return w
 
 
 def traffic_for_attention():
-    """HBM bytes per dense-attention launch from the committed rocprofv3
+    """HBM bytes per attention launch (all rows) from the committed rocprofv3
     counter summary, or None when the kernel source changed since."""
     try:
         with open(TRAFFIC_FILE) as f:
@@ -239,7 +243,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--skip-configs", action="store_true",
                     help="skip the per-configuration measurements of the other workloads")
-    ap.add_argument("--only", choices=["select", "gather", "attn_dense", "attn_sparse", "scatter"],
+    ap.add_argument("--only", choices=["select", "gather", "attn", "attn_dense", "attn_sparse", "scatter"],
                     help="time only this operation of the step (for counter runs); prints one line")
     ap.add_argument("--copy-probe", type=int, metavar="MB",
                     help="run a plain device copy of MB megabytes 5 times (counter calibration)")
@@ -304,23 +308,31 @@ def main():
         ", ".join(f"{k} {v * 1e3:.1f} us" for k, v in op_ms.items()))
 
     attn_flop = work["attn_dense_flop"] + work["attn_sparse_flop"]
+    attn_bytes = work["attn_dense_bytes"] + work["attn_sparse_bytes"]
     value = attn_flop / (ms_step * 1e-3) / 1e12
+    # the two row kinds as separate launches (reference figures)
+    ms_dense = time_calls(step.attn_dense, args.steps)
+    ms_sparse = time_calls(step.attn_sparse, args.steps)
 
     def rate(num, ms, scale):
         return num / (ms * 1e-3) / scale if ms > 0 else None
 
     bd_ = {}
-    tf_d = rate(work["attn_dense_flop"], op_ms["attn_dense"], 1e12)
-    tf_s = rate(work["attn_sparse_flop"], op_ms["attn_sparse"], 1e12)
+    tf_a = rate(attn_flop, op_ms["attn"], 1e12)
+    tf_d = rate(work["attn_dense_flop"], ms_dense, 1e12)
+    tf_s = rate(work["attn_sparse_flop"], ms_sparse, 1e12)
     gb_sel = rate(work["select_bytes"], op_ms["select"], 1e9)
     gb_gat = rate(work["gather_bytes"], op_ms["gather"], 1e9)
     gb_sca = rate(work["scatter_bytes"], op_ms["scatter"], 1e9)
-    bd_["attn_dense"] = {"us": round(op_ms["attn_dense"] * 1e3, 2), "TFLOP/s": round(tf_d, 2),
+    bd_["attn"] = {"us": round(op_ms["attn"] * 1e3, 2), "TFLOP/s": round(tf_a, 2),
+                   "frac_mfma_peak": round(tf_a / PEAK_BF16_TFLOPS, 4),
+                   "gflop": round(attn_flop / 1e9, 3)}
+    bd_["attn_dense"] = {"us": round(ms_dense * 1e3, 2), "TFLOP/s": round(tf_d, 2),
                          "frac_mfma_peak": round(tf_d / PEAK_BF16_TFLOPS, 4),
-                         "gflop": round(work["attn_dense_flop"] / 1e9, 3)}
-    bd_["attn_sparse"] = {"us": round(op_ms["attn_sparse"] * 1e3, 2), "TFLOP/s": round(tf_s, 2),
+                         "gflop": round(work["attn_dense_flop"] / 1e9, 3), "launch": "separate"}
+    bd_["attn_sparse"] = {"us": round(ms_sparse * 1e3, 2), "TFLOP/s": round(tf_s, 2),
                           "frac_mfma_peak": round(tf_s / PEAK_BF16_TFLOPS, 4),
-                          "gflop": round(work["attn_sparse_flop"] / 1e9, 3)}
+                          "gflop": round(work["attn_sparse_flop"] / 1e9, 3), "launch": "separate"}
     bd_["select"] = {"us": round(op_ms["select"] * 1e3, 2), "GB/s": round(gb_sel, 1),
                      "frac_hbm_peak": round(gb_sel / PEAK_HBM_GBS, 4),
                      "mb": round(work["select_bytes"] / 1e6, 2)}
@@ -332,11 +344,11 @@ def main():
                       "mb": round(work["scatter_bytes"] / 1e6, 2)}
 
     traffic = traffic_for_attention()
-    roof = {"bound": "mfma", "kernel": "attn_mfma_kernel<8, 4> (dense rows)",
-            "achieved": round(tf_d, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(tf_d / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-            "algorithmic_bytes": work["attn_dense_bytes"],
-            "intensity_flop_per_byte": round(work["attn_dense_flop"] / work["attn_dense_bytes"], 1)}
+    roof = {"bound": "mfma", "kernel": "attn_mfma_kernel<8, 4> (dense and sparse rows, one launch)",
+            "achieved": round(tf_a, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf_a / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+            "algorithmic_bytes": attn_bytes,
+            "intensity_flop_per_byte": round(attn_flop / attn_bytes, 1)}
 
     n_dense, n_sparse = step.n_dense, step.n_sparse
     configs = None

@@ -17,6 +17,9 @@
  *   bd_kv_scatter   write-back of the window's KV to its absolute positions
  *                   (FlowBlock review, Eq. (7) = paper Eq. 6).
  *
+ * bd_attn_packed_dual runs bd_attn_packed for two row lists with different
+ * prefix sources (cache rows and pool rows) in one launch.
+ *
  * Conventions shared by every call
  * --------------------------------
  * - Memory: every tensor pointer is device memory owned by the caller.  The
@@ -200,6 +203,46 @@ int bd_attn_packed(int dtype, int B, int Hq, int Hkv, int d, int q, int bl,
                    const void *wv, const int64_t w_strides[3], float sm_scale,
                    void *out, const int64_t out_strides[3], float *lse,
                    void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * bd_attn_packed_dual: bd_attn_packed over two row lists in one launch,
+ * each list with its own prefix source.  The rows of list a attend over
+ * pk_a/pv_a with lengths p_len_a, the rows of list b over pk_b/pv_b with
+ * lengths p_len_b; the queries, the window source and the output are
+ * shared.  The mask and the result of every row are exactly those of
+ * bd_attn_packed with that row's source (FlowBlock review Eq. (6) when the
+ * source is the cache; HERALD's denoising attention, Sec. III-C and
+ * Sec. IV-B1, when it is a pool).  It serves a batch whose rows are split
+ * between dense attention over their own cache and sparse attention over a
+ * gathered pool: one launch lets the short pool rows fill the tail of the
+ * long cache rows.
+ *
+ *   rows_a, rows_b  device int32 [n_a], [n_b]; required when the count is
+ *                   positive.  Entries outside [0, B) are skipped; a row in
+ *                   both lists is written by both (the result is one of
+ *                   the two).
+ *   pk_x/pv_x       [B, pX_cap, Hkv, d] with strides pX_strides; p_len_x
+ *                   device int32 [B], clamped to [0, min(p_max_x, pX_cap)].
+ *   everything else as in bd_attn_packed; the workspace is at least
+ *   bd_attn_dual_workspace_size(...) bytes.
+ *
+ * Errors as bd_attn_packed.  Built for the same dtype / d / GQA shapes.
+ */
+size_t bd_attn_dual_workspace_size(int dtype, int B, int Hq, int Hkv, int d,
+                                   int q, int n_a, int p_max_a, int n_b,
+                                   int p_max_b);
+int bd_attn_packed_dual(int dtype, int B, int Hq, int Hkv, int d, int q,
+                        int bl, const void *q_ptr, const int64_t q_strides[3],
+                        const int32_t *rows_a, int n_a, const void *pk_a,
+                        const void *pv_a, const int64_t pa_strides[3],
+                        int pa_cap, const int32_t *p_len_a, int p_max_a,
+                        const int32_t *rows_b, int n_b, const void *pk_b,
+                        const void *pv_b, const int64_t pb_strides[3],
+                        int pb_cap, const int32_t *p_len_b, int p_max_b,
+                        const void *wk, const void *wv,
+                        const int64_t w_strides[3], float sm_scale, void *out,
+                        const int64_t out_strides[3], float *lse,
+                        void *workspace, size_t ws_bytes, void *stream);
 
 /*
  * bd_mask_materialize: test hook for the attention mask.  Writes

@@ -42,6 +42,11 @@ _SIGS = {
     "bd_attn_packed": (_i, [_i, _i, _i, _i, _i, _i, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp, _i,
                             _vp, _i, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _sz,
                             _vp]),
+    "bd_attn_dual_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _i]),
+    "bd_attn_packed_dual": (_i, [_i, _i, _i, _i, _i, _i, _i, _vp, _vp,
+                                 _vp, _i, _vp, _vp, _vp, _i, _vp, _i,
+                                 _vp, _i, _vp, _vp, _vp, _i, _vp, _i,
+                                 _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _sz, _vp]),
     "bd_mask_materialize": (_i, [_i, _i, _i, _i, _vp, _vp, _vp]),
 }
 
@@ -215,6 +220,47 @@ def attn_packed(q, pk, pv, p_len, p_max: int, wk, wv, bl: int, sm_scale: float, 
                                 pk.shape[1], _ptr(p_len), p_max, _ptr(wk), _ptr(wv),
                                 _strides(wk, 3), float(sm_scale), _ptr(out), _strides(out, 3),
                                 _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(), _stream()))
+    return out
+
+
+def attn_dual_workspace_size(dtype, B: int, Hq: int, Hkv: int, d: int, q: int, n_a: int,
+                             p_max_a: int, n_b: int, p_max_b: int) -> int:
+    return int(lib().bd_attn_dual_workspace_size(_DTYPE.get(dtype, dtype), B, Hq, Hkv, d, q, n_a,
+                                                 p_max_a, n_b, p_max_b))
+
+
+def attn_packed_dual(q, src_a, src_b, wk, wv, bl: int, sm_scale: float, out=None, lse=None,
+                     ws=None):
+    """bd_attn_packed over two row lists in one launch.  src_a and src_b are
+    (rows, pk, pv, p_len, p_max) tuples: the rows of each list attend over
+    that list's prefix (e.g. the cache for dense rows, the pool for sparse
+    rows).  Returns out [B, q, Hq, d]."""
+    q = _dev(q, "q")
+    wk, wv = _dev(wk, "wk"), _dev(wv, "wv")
+    if wv.stride() != wk.stride():
+        raise ValueError("K and V tensors must share strides")
+    B, nqry, Hq, d = q.shape
+    srcs = []
+    for tag, (rows, pk, pv, p_len, p_max) in (("a", src_a), ("b", src_b)):
+        pk, pv = _dev(pk, "pk_" + tag), _dev(pv, "pv_" + tag)
+        if pv.stride() != pk.stride():
+            raise ValueError("K and V tensors must share strides")
+        srcs.append((_i32(rows, "rows_" + tag), pk, pv, _i32(p_len, "p_len_" + tag), int(p_max)))
+    (ra, pka, pva, pla, pma), (rb, pkb, pvb, plb, pmb) = srcs
+    Hkv = pka.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    need = attn_dual_workspace_size(q.dtype, B, Hq, Hkv, d, nqry, ra.numel(), pma, rb.numel(), pmb)
+    if ws is None:
+        ws = workspace(need, q.device)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be contiguous float32 [B, Hq, q]")
+    _check(lib().bd_attn_packed_dual(
+        _DTYPE[q.dtype], B, Hq, Hkv, d, nqry, bl, _ptr(q), _strides(q, 3),
+        _ptr(ra), ra.numel(), _ptr(pka), _ptr(pva), _strides(pka, 3), pka.shape[1], _ptr(pla), pma,
+        _ptr(rb), rb.numel(), _ptr(pkb), _ptr(pvb), _strides(pkb, 3), pkb.shape[1], _ptr(plb), pmb,
+        _ptr(wk), _ptr(wv), _strides(wk, 3), float(sm_scale), _ptr(out), _strides(out, 3),
+        _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(), _stream()))
     return out
 
 

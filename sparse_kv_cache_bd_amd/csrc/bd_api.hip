@@ -173,57 +173,106 @@ size_t bd_attn_workspace_size(int dtype, int B, int Hq, int Hkv, int d, int q, i
   return attn_plan(dtype, B, Hq, Hkv, d, q, n_rows, p_max).ws_bytes;
 }
 
-int bd_attn_packed(int dtype, int B, int Hq, int Hkv, int d, int q, int bl, const int32_t *row_ids,
-                   int n_rows, const void *q_ptr, const int64_t q_strides[3], const void *pk,
-                   const void *pv, const int64_t p_strides[3], int p_cap, const int32_t *p_len,
-                   int p_max, const void *wk, const void *wv, const int64_t w_strides[3],
-                   float sm_scale, void *out, const int64_t out_strides[3], float *lse,
-                   void *workspace, size_t ws_bytes, void *stream) {
+size_t bd_attn_dual_workspace_size(int dtype, int B, int Hq, int Hkv, int d, int q, int n_a,
+                                   int p_max_a, int n_b, int p_max_b) {
+  if (n_a < 0 || n_b < 0 || p_max_a < 0 || p_max_b < 0) return 0;
+  return bd_attn_workspace_size(dtype, B, Hq, Hkv, d, q, n_a + n_b, p_max_a > p_max_b ? p_max_a : p_max_b);
+}
+
+}  // extern "C"
+
+namespace {
+
+// One prefix source of an attention call: its row list and the prefix
+// tensors those rows attend over.
+struct PrefixArg {
+  const int32_t *rows;
+  int n;
+  const void *pk, *pv;
+  const int64_t *strides;
+  int cap;
+  const int32_t *p_len;
+  int p_max;
+};
+
+// Shared body of bd_attn_packed (one source) and bd_attn_packed_dual (two).
+int attn_entry(const char *fn, int dtype, int B, int Hq, int Hkv, int d, int q, int bl,
+               const void *q_ptr, const int64_t q_strides[3], const PrefixArg &pa,
+               const PrefixArg *pb, const void *wk, const void *wv, const int64_t w_strides[3],
+               float sm_scale, void *out, const int64_t out_strides[3], float *lse,
+               void *workspace, size_t ws_bytes, void *stream) {
   g_err[0] = 0;
   const int es = esize(dtype);
-  if (!es) return fail(BD_ERR_UNSUPPORTED, "bd_attn_packed: unknown dtype %d", dtype);
-  if (B < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || q < 0 || bl <= 0 || n_rows < 0 || p_cap < 0 || p_max < 0)
-    return fail(BD_ERR_INVALID_ARG, "bd_attn_packed: negative or zero size");
-  if (Hq % Hkv != 0) return fail(BD_ERR_INVALID_ARG, "bd_attn_packed: Hq %% Hkv != 0");
-  if (!row_ids && n_rows != B)
-    return fail(BD_ERR_INVALID_ARG, "bd_attn_packed: n_rows must equal B when row_ids is NULL");
+  if (!es) return fail(BD_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || q < 0 || bl <= 0)
+    return fail(BD_ERR_INVALID_ARG, "%s: negative or zero size", fn);
+  for (const PrefixArg *p : {&pa, pb}) {
+    if (p && (p->n < 0 || p->cap < 0 || p->p_max < 0))
+      return fail(BD_ERR_INVALID_ARG, "%s: negative row count, capacity or p_max", fn);
+  }
+  if (Hq % Hkv != 0) return fail(BD_ERR_INVALID_ARG, "%s: Hq %% Hkv != 0", fn);
+  if (!pb && !pa.rows && pa.n != B)
+    return fail(BD_ERR_INVALID_ARG, "%s: n_rows must equal B when row_ids is NULL", fn);
+  if (pb && ((pa.n > 0 && !pa.rows) || (pb->n > 0 && !pb->rows)))
+    return fail(BD_ERR_INVALID_ARG, "%s: null row list", fn);
   const int G = Hq / Hkv;
   if (!attn_mfma_supported(dtype, d, G) && !attn_generic_supported(dtype, d))
-    return fail(BD_ERR_UNSUPPORTED, "bd_attn_packed: dtype %d with d %d is not built", dtype, d);
+    return fail(BD_ERR_UNSUPPORTED, "%s: dtype %d with d %d is not built", fn, dtype, d);
+  const int n_rows = pa.n + (pb ? pb->n : 0);
+  if ((int64_t)pa.n + (pb ? pb->n : 0) > INT32_MAX / 2)
+    return fail(BD_ERR_INVALID_ARG, "%s: too many rows", fn);
   if (B == 0 || n_rows == 0 || q == 0) return BD_OK;
-  if (!q_ptr || !wk || !wv || !out || !p_len || !q_strides || !w_strides || !out_strides || !p_strides)
-    return fail(BD_ERR_INVALID_ARG, "bd_attn_packed: null pointer");
-  if (p_max > 0 && (!pk || !pv)) return fail(BD_ERR_INVALID_ARG, "bd_attn_packed: null prefix pointers");
-  if (!(sm_scale > 0.f) || sm_scale > 1e30f) return fail(BD_ERR_INVALID_ARG, "bd_attn_packed: bad sm_scale");
-  if (!strides_ok(q_strides, 3, es) || !strides_ok(p_strides, 3, es) || !strides_ok(w_strides, 3, es) ||
-      !strides_ok(out_strides, 3, es))
-    return fail(BD_ERR_INVALID_ARG, "bd_attn_packed: strides must be >= 0 and 16-byte multiples");
-  if (!aligned16(q_ptr) || !aligned16(wk) || !aligned16(wv) || !aligned16(out) ||
-      (p_max > 0 && (!aligned16(pk) || !aligned16(pv))))
-    return fail(BD_ERR_INVALID_ARG, "bd_attn_packed: base pointers must be 16-byte aligned");
-  if (p_strides[1] * es * 64 > INT32_MAX || w_strides[1] * es * 64 > INT32_MAX)
-    return fail(BD_ERR_INVALID_ARG, "bd_attn_packed: key row strides above 32 MB are not supported");
+  if (!q_ptr || !wk || !wv || !out || !q_strides || !w_strides || !out_strides)
+    return fail(BD_ERR_INVALID_ARG, "%s: null pointer", fn);
+  for (const PrefixArg *p : {&pa, pb}) {
+    if (!p || p->n == 0) continue;
+    if (!p->p_len || !p->strides) return fail(BD_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (p->p_max > 0 && (!p->pk || !p->pv)) return fail(BD_ERR_INVALID_ARG, "%s: null prefix pointers", fn);
+    if (!strides_ok(p->strides, 3, es))
+      return fail(BD_ERR_INVALID_ARG, "%s: strides must be >= 0 and 16-byte multiples", fn);
+    if (p->p_max > 0 && (!aligned16(p->pk) || !aligned16(p->pv)))
+      return fail(BD_ERR_INVALID_ARG, "%s: base pointers must be 16-byte aligned", fn);
+    if (p->strides[1] * es * 64 > INT32_MAX)
+      return fail(BD_ERR_INVALID_ARG, "%s: key row strides above 32 MB are not supported", fn);
+  }
+  if (!(sm_scale > 0.f) || sm_scale > 1e30f) return fail(BD_ERR_INVALID_ARG, "%s: bad sm_scale", fn);
+  if (!strides_ok(q_strides, 3, es) || !strides_ok(w_strides, 3, es) || !strides_ok(out_strides, 3, es))
+    return fail(BD_ERR_INVALID_ARG, "%s: strides must be >= 0 and 16-byte multiples", fn);
+  if (!aligned16(q_ptr) || !aligned16(wk) || !aligned16(wv) || !aligned16(out))
+    return fail(BD_ERR_INVALID_ARG, "%s: base pointers must be 16-byte aligned", fn);
+  if (w_strides[1] * es * 64 > INT32_MAX)
+    return fail(BD_ERR_INVALID_ARG, "%s: key row strides above 32 MB are not supported", fn);
   AttnArgs a;
   a.dtype = dtype; a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.d = d; a.q = q; a.bl = bl;
-  a.n_rows = n_rows; a.p_cap = p_cap; a.p_max = p_max;
-  a.Q = q_ptr; a.pk = pk; a.pv = pv; a.wk = wk; a.wv = wv; a.out = out; a.lse = lse;
+  a.n_rows = n_rows;
+  a.Q = q_ptr; a.wk = wk; a.wv = wv; a.out = out; a.lse = lse;
   memcpy(a.qs, q_strides, sizeof(a.qs));
-  memcpy(a.ps, p_strides, sizeof(a.ps));
   memcpy(a.ws, w_strides, sizeof(a.ws));
   memcpy(a.os, out_strides, sizeof(a.os));
-  a.row_ids = row_ids; a.p_len = p_len; a.scale2 = sm_scale * kLog2e;
+  const bool use_a = pa.n > 0;
+  a.n_rows1 = pa.n;
+  a.row_ids = pa.rows; a.p_len = use_a ? pa.p_len : nullptr;
+  a.pk = pa.pk; a.pv = pa.pv; a.p_cap = pa.cap; a.p_max = use_a ? pa.p_max : 0;
+  for (int i = 0; i < 3; ++i) a.ps[i] = use_a ? pa.strides[i] : 0;
+  const bool use_b = pb && pb->n > 0;
+  a.row_ids2 = use_b ? pb->rows : nullptr; a.p_len2 = use_b ? pb->p_len : nullptr;
+  a.pk2 = use_b ? pb->pk : nullptr; a.pv2 = use_b ? pb->pv : nullptr;
+  a.p_cap2 = use_b ? pb->cap : 0; a.p_max2 = use_b ? pb->p_max : 0;
+  for (int i = 0; i < 3; ++i) a.ps2[i] = use_b ? pb->strides[i] : 0;
+  a.scale2 = sm_scale * kLog2e;
+  const int p_max = a.p_max > a.p_max2 ? a.p_max : a.p_max2;
   const AttnPlan plan = attn_plan(dtype, B, Hq, Hkv, d, q, n_rows, p_max);
   a.nw = plan.nw; a.nqt = plan.nqt; a.chunk = plan.chunk; a.n_split = plan.n_split;
   const int64_t grid_units = (8 + (int64_t)n_rows * Hkv) * a.nqt * a.n_split;
   if (grid_units > ((int64_t)1 << 31) - 1 || (int64_t)n_rows * Hq * a.nqt > ((int64_t)1 << 31) - 1)
-    return fail(BD_ERR_INVALID_ARG, "bd_attn_packed: problem too large for one launch");
+    return fail(BD_ERR_INVALID_ARG, "%s: problem too large for one launch", fn);
   a.row_order = nullptr;
   a.part_o = a.part_ml = nullptr;
   if (plan.ws_bytes > 0) {
     if (!workspace || ws_bytes < plan.ws_bytes)
-      return fail(BD_ERR_WORKSPACE, "bd_attn_packed: workspace %zu bytes, need %zu", ws_bytes, plan.ws_bytes);
+      return fail(BD_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, plan.ws_bytes);
     if (((uintptr_t)workspace & 255u) != 0)
-      return fail(BD_ERR_WORKSPACE, "bd_attn_packed: workspace must be 256-byte aligned");
+      return fail(BD_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
     char *w = (char *)workspace;
     if (plan.order) a.row_order = (int *)(w + plan.off_order);
     if (plan.n_split > 1) {
@@ -231,7 +280,37 @@ int bd_attn_packed(int dtype, int B, int Hq, int Hkv, int d, int q, int bl, cons
       a.part_ml = (float *)(w + plan.off_part_ml);
     }
   }
-  return hip_status(launch_attn(a, (hipStream_t)stream), "bd_attn_packed launch");
+  return hip_status(launch_attn(a, (hipStream_t)stream), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int bd_attn_packed(int dtype, int B, int Hq, int Hkv, int d, int q, int bl, const int32_t *row_ids,
+                   int n_rows, const void *q_ptr, const int64_t q_strides[3], const void *pk,
+                   const void *pv, const int64_t p_strides[3], int p_cap, const int32_t *p_len,
+                   int p_max, const void *wk, const void *wv, const int64_t w_strides[3],
+                   float sm_scale, void *out, const int64_t out_strides[3], float *lse,
+                   void *workspace, size_t ws_bytes, void *stream) {
+  const PrefixArg pa{row_ids, n_rows, pk, pv, p_strides, p_cap, p_len, p_max};
+  return attn_entry("bd_attn_packed", dtype, B, Hq, Hkv, d, q, bl, q_ptr, q_strides, pa, nullptr, wk,
+                    wv, w_strides, sm_scale, out, out_strides, lse, workspace, ws_bytes, stream);
+}
+
+int bd_attn_packed_dual(int dtype, int B, int Hq, int Hkv, int d, int q, int bl, const void *q_ptr,
+                        const int64_t q_strides[3], const int32_t *rows_a, int n_a, const void *pk_a,
+                        const void *pv_a, const int64_t pa_strides[3], int pa_cap,
+                        const int32_t *p_len_a, int p_max_a, const int32_t *rows_b, int n_b,
+                        const void *pk_b, const void *pv_b, const int64_t pb_strides[3], int pb_cap,
+                        const int32_t *p_len_b, int p_max_b, const void *wk, const void *wv,
+                        const int64_t w_strides[3], float sm_scale, void *out,
+                        const int64_t out_strides[3], float *lse, void *workspace, size_t ws_bytes,
+                        void *stream) {
+  const PrefixArg pa{rows_a, n_a, pk_a, pv_a, pa_strides, pa_cap, p_len_a, p_max_a};
+  const PrefixArg pb{rows_b, n_b, pk_b, pv_b, pb_strides, pb_cap, p_len_b, p_max_b};
+  return attn_entry("bd_attn_packed_dual", dtype, B, Hq, Hkv, d, q, bl, q_ptr, q_strides, pa, &pb,
+                    wk, wv, w_strides, sm_scale, out, out_strides, lse, workspace, ws_bytes, stream);
 }
 
 int bd_mask_materialize(int B, int C, int q, int bl, const int32_t *o, uint8_t *out, void *stream) {

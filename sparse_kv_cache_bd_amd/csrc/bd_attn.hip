@@ -61,6 +61,44 @@ __device__ inline int vt_slot(int k16) {
   return (k16 & 3) | ((k16 & 4) << 1) | ((k16 & 8) >> 1);
 }
 
+// Row list position rl -> row and prefix source (the second source holds
+// the positions at or past n_rows1).
+struct RowRef {
+  int b;
+  bool alt;
+};
+__device__ inline RowRef row_ref(const AttnArgs &a, int rl) {
+  if (rl < a.n_rows1) return {a.row_ids ? a.row_ids[rl] : rl, false};
+  return {a.row_ids2[rl - a.n_rows1], true};
+}
+// prefix length of a row whose index b is in [0, B)
+__device__ inline int prefix_len(const AttnArgs &a, const RowRef &r) {
+  return r.alt ? clampi(a.p_len2[r.b], 0, min(a.p_max2, a.p_cap2))
+               : clampi(a.p_len[r.b], 0, min(a.p_max, a.p_cap));
+}
+// Wave-uniform 64-bit value in scalar registers.  Choosing between two
+// fields of the argument block through this keeps the choice a select of
+// values (a select of the fields' addresses would keep the block in memory).
+__device__ inline uint64_t uniform_u64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+// Prefix source of a row: K, V base of (row b, KV head h) and key row stride.
+struct PrefixSrc {
+  const char *k, *v;
+  int64_t row;
+};
+__device__ inline PrefixSrc prefix_src(const AttnArgs &a, const RowRef &r, int h, int es) {
+  const uint64_t pk = uniform_u64(r.alt ? reinterpret_cast<uint64_t>(a.pk2) : reinterpret_cast<uint64_t>(a.pk));
+  const uint64_t pv = uniform_u64(r.alt ? reinterpret_cast<uint64_t>(a.pv2) : reinterpret_cast<uint64_t>(a.pv));
+  const int64_t s0 = (int64_t)uniform_u64((uint64_t)(r.alt ? a.ps2[0] : a.ps[0]));
+  const int64_t s1 = (int64_t)uniform_u64((uint64_t)(r.alt ? a.ps2[1] : a.ps[1]));
+  const int64_t s2 = (int64_t)uniform_u64((uint64_t)(r.alt ? a.ps2[2] : a.ps[2]));
+  const int64_t off = ((int64_t)r.b * s0 + (int64_t)h * s2) * es;
+  return {reinterpret_cast<const char *>(pk) + off, reinterpret_cast<const char *>(pv) + off, s1};
+}
+
 // Block of NW waves, one 32-column group per wave; two waves share a SIMD.
 // Tile staging: 256 V items (4 keys x 8 dims) and 1024 K pieces (16 bytes)
 // per 64-key tile.  With 8 waves, waves 0-3 stage V and waves 4-7 stage K
@@ -82,6 +120,7 @@ struct Shape {
 
 // Decoded work item of a block.
 struct Item {
+  RowRef r;
   int b, h, rl, u, c, nc;
   int kbeg, kend;     // prefix keys of this chunk
   bool with_window;   // last chunk also covers the window
@@ -99,9 +138,10 @@ __device__ inline bool decode_item(const AttnArgs &a, int bid, Item &it) {
   const int rank = gamma / a.Hkv;
   it.h = gamma - rank * a.Hkv;
   it.rl = a.row_order ? a.row_order[rank] : rank;
-  it.b = a.row_ids ? a.row_ids[it.rl] : it.rl;
+  it.r = row_ref(a, it.rl);
+  it.b = it.r.b;
   if (it.b < 0 || it.b >= a.B) return false;
-  const int P = clampi(a.p_len[it.b], 0, min(a.p_max, a.p_cap));
+  const int P = prefix_len(a, it.r);
   it.nc = P > 0 ? (int)cdiv(P, a.chunk) : 1;
   if (it.c >= it.nc) return false;
   it.kbeg = it.c * a.chunk;
@@ -148,8 +188,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
     for (int ks = 0; ks < kD / 16; ++ks) qop[ks] = qok ? ld_bf16x8(qp + ks * 16) : bf16x8{};
   }
 
-  const bf16 *pkb = reinterpret_cast<const bf16 *>(a.pk) + (int64_t)b * a.ps[0] + (int64_t)h * a.ps[2];
-  const bf16 *pvb = reinterpret_cast<const bf16 *>(a.pv) + (int64_t)b * a.ps[0] + (int64_t)h * a.ps[2];
+  const PrefixSrc src = prefix_src(a, it.r, h, (int)sizeof(bf16));
+  const bf16 *pkb = reinterpret_cast<const bf16 *>(src.k);
+  const bf16 *pvb = reinterpret_cast<const bf16 *>(src.v);
+  const int64_t p_row = src.row, w_row = a.ws[1];   // key row strides
   const bf16 *wkb = reinterpret_cast<const bf16 *>(a.wk) + (int64_t)b * a.ws[0] + (int64_t)h * a.ws[2];
   const bf16 *wvb = reinterpret_cast<const bf16 *>(a.wv) + (int64_t)b * a.ws[0] + (int64_t)h * a.ws[2];
 
@@ -186,7 +228,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
   int koff[S::KP], voff[4];
   auto load = [&](int tt) {
     const bool win = tt >= n_pref;
-    const int64_t sp = win ? a.ws[1] : a.ps[1];
+    const int64_t sp = win ? w_row : p_row;
     const int rowb = (int)(sp * 2);
     const int base = tile_base(tt), limit = tile_limit(tt);
     if (stage_k) {
@@ -426,9 +468,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int64_t group = unit / a.nqt;
   const int rl = (int)(group / a.Hkv);
   const int h = (int)(group - (int64_t)rl * a.Hkv);
-  const int b = a.row_ids ? a.row_ids[rl] : rl;
+  const RowRef rr = row_ref(a, rl);
+  const int b = rr.b;
   if (b < 0 || b >= a.B) return;
-  const int P = clampi(a.p_len[b], 0, min(a.p_max, a.p_cap));
+  const int P = prefix_len(a, rr);
   const int nc = P > 0 ? (int)cdiv(P, a.chunk) : 1;
   if (nc == 1) return;  // written directly by the attention kernel
   const int cg = col / 32;
@@ -466,8 +509,8 @@ __global__ __launch_bounds__(1024) void attn_order_kernel(AttnArgs a) {
   __shared__ int len[kOrderMax];
   const int n = a.n_rows;
   for (int r = threadIdx.x; r < n; r += blockDim.x) {
-    const int b = a.row_ids ? a.row_ids[r] : r;
-    len[r] = (b < 0 || b >= a.B) ? -1 : clampi(a.p_len[b], 0, min(a.p_max, a.p_cap));
+    const RowRef rr = row_ref(a, r);
+    len[r] = (rr.b < 0 || rr.b >= a.B) ? -1 : prefix_len(a, rr);
   }
   __syncthreads();
   for (int r = threadIdx.x; r < n; r += blockDim.x) {
@@ -503,10 +546,11 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a) {
   unit /= nqt;
   const int hq = unit % a.Hq;
   const int rl = unit / a.Hq;
-  const int b = a.row_ids ? a.row_ids[rl] : rl;
+  const RowRef rr = row_ref(a, rl);
+  const int b = rr.b;
   if (b < 0 || b >= a.B) return;
   const int h = hq / a.G;
-  const int P = clampi(a.p_len[b], 0, min(a.p_max, a.p_cap));
+  const int P = prefix_len(a, rr);
   const int qi = u * kQT + ql;
   const bool q_ok = qi < a.q;
   const int ilast = min(u * kQT + kQT, a.q) - 1;
@@ -522,8 +566,10 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a) {
     o[e] = 0.f;
   }
   float m_run = -INFINITY, l_run = 0.f;
-  const T *pkb = reinterpret_cast<const T *>(a.pk) + (int64_t)b * a.ps[0] + (int64_t)h * a.ps[2];
-  const T *pvb = reinterpret_cast<const T *>(a.pv) + (int64_t)b * a.ps[0] + (int64_t)h * a.ps[2];
+  const PrefixSrc src = prefix_src(a, rr, h, (int)sizeof(T));
+  const T *pkb = reinterpret_cast<const T *>(src.k);
+  const T *pvb = reinterpret_cast<const T *>(src.v);
+  const int64_t p_row = src.row;
   const T *wkb = reinterpret_cast<const T *>(a.wk) + (int64_t)b * a.ws[0] + (int64_t)h * a.ws[2];
   const T *wvb = reinterpret_cast<const T *>(a.wv) + (int64_t)b * a.ws[0] + (int64_t)h * a.ws[2];
   const int npt = (int)cdiv(P, kGenKeys);
@@ -539,7 +585,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a) {
     const int limit = win ? win_len : P;
     const T *kb = win ? wkb : pkb;
     const T *vb = win ? wvb : pvb;
-    const int64_t sp = win ? a.ws[1] : a.ps[1];
+    const int64_t sp = win ? a.ws[1] : p_row;
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
       const int e = tid + 256 * i;

@@ -93,6 +93,14 @@ struct AttnArgs {
   int64_t os[3];
   float *lse;
   const int32_t *row_ids, *p_len;
+  // second prefix source (one launch over two row lists): list positions
+  // at or past n_rows1 are rows row_ids2[pos - n_rows1] whose prefix is
+  // pk2/pv2 with lengths p_len2.  A single-source call has n_rows1 = n_rows.
+  int n_rows1;
+  const int32_t *row_ids2, *p_len2;
+  const void *pk2, *pv2;
+  int64_t ps2[3];
+  int p_cap2, p_max2;
   float scale2;  // sm_scale * log2(e)
   // launch plan (attn_plan)
   int nw;                 // waves per block of the MFMA path (2 or 4)

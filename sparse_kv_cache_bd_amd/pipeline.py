@@ -6,9 +6,13 @@ and reuses them) and issues the library calls of one step in order:
 
   1. bd_select over the sparse rows (representative query + top-k),
   2. bd_gather of the selected K/V into the pool,
-  3. bd_attn_packed for the dense rows (prefix = the row's own cache),
-  4. bd_attn_packed for the sparse rows (prefix = the pool),
-  5. bd_kv_scatter of every row's window to its absolute position.
+  3. one bd_attn_packed_dual launch: the dense rows over their own cache,
+     the sparse rows over their pools (the short pool rows fill the tail of
+     the long cache rows); bd_attn_packed when only one kind is present,
+  4. bd_kv_scatter of every row's window to its absolute position.
+
+attn_dense / attn_sparse run the two row kinds as separate launches (the
+same results; used to time them one by one).
 
 Every step runs in the HIP kernels on the current stream; this class only
 marshals arguments.  Repeated steps are idempotent: the scatter writes the
@@ -62,6 +66,10 @@ class BlockDiffusionStep:
             self.ws_dense = bd.workspace(bd.attn_workspace_size(
                 Q.dtype, B, self.Hq, self.Hkv, self.d, self.q, self.n_dense, self.p_max_dense),
                 self.dev)
+        if self.n_dense and self.n_sparse:
+            self.ws_both = bd.workspace(bd.attn_dual_workspace_size(
+                Q.dtype, B, self.Hq, self.Hkv, self.d, self.q, self.n_dense, self.p_max_dense,
+                self.n_sparse, self.k_max), self.dev)
 
     # individual ops (so callers can time them one by one)
     def select(self):
@@ -85,15 +93,25 @@ class BlockDiffusionStep:
                            self.wv, self.bl, self.sm_scale, out=self.out,
                            row_ids=self.sparse_rows, ws=self.ws_sparse)
 
+    def attn(self):
+        """Attention of every row in one launch."""
+        if self.n_dense and self.n_sparse:
+            bd.attn_packed_dual(self.Q, (self.dense_rows, self.Kc, self.Vc, self.o, self.p_max_dense),
+                                (self.sparse_rows, self.pool_k, self.pool_v, self.k_sel, self.k_max),
+                                self.wk, self.wv, self.bl, self.sm_scale, out=self.out,
+                                ws=self.ws_both)
+        else:
+            self.attn_dense()
+            self.attn_sparse()
+
     def scatter(self):
         bd.kv_scatter(self.Kc, self.Vc, self.Kc, self.Vc, self.o, self.t, self.q)
 
-    OPS = ("select", "gather", "attn_dense", "attn_sparse", "scatter")
+    OPS = ("select", "gather", "attn", "scatter")
 
     def run(self):
         self.select()
         self.gather()
-        self.attn_dense()
-        self.attn_sparse()
+        self.attn()
         self.scatter()
         return self.out

@@ -24,7 +24,7 @@ def L():
 
 def test_exports_every_header_function(L):
     names = bd.header_functions()
-    assert len(names) == 9
+    assert len(names) == 11
     for n in names:
         assert hasattr(L, n), n
 
@@ -175,6 +175,54 @@ def test_attn_validation(L, kw, code):
 def test_attn_empty_is_ok(L):
     assert _attn(L, B=0, n_rows=0) == bd.BD_OK
     assert _attn(L, q=0) == bd.BD_OK
+
+
+def _attn_dual(L, ws_bytes=None, **kw):
+    a = dict(dtype=bd.BD_BF16, B=4, Hq=32, Hkv=8, d=128, q=64, bl=32,
+             Q=FAKE, qs=I3(64 * 4096, 4096, 128),
+             ra=FAKE, na=2, pka=FAKE, pva=FAKE2, psa=I3(1 << 22, 1024, 128), pcapa=4096,
+             plena=FAKE, pmaxa=4000,
+             rb=FAKE2, nb=2, pkb=FAKE2, pvb=FAKE, psb=I3(1 << 20, 1024, 128), pcapb=1024,
+             plenb=FAKE2, pmaxb=200,
+             wk=FAKE, wv=FAKE2, wsd=I3(1 << 22, 1024, 128), scale=0.088, out=FAKE2,
+             os=I3(64 * 4096, 4096, 128), lse=None, ws=FAKE)
+    a.update(kw)
+    need = bd.attn_dual_workspace_size(a["dtype"], a["B"], a["Hq"], a["Hkv"], a["d"], a["q"],
+                                       a["na"], a["pmaxa"], a["nb"], a["pmaxb"])
+    wsb = need if ws_bytes is None else ws_bytes
+    return L.bd_attn_packed_dual(a["dtype"], a["B"], a["Hq"], a["Hkv"], a["d"], a["q"], a["bl"],
+                                 a["Q"], a["qs"], a["ra"], a["na"], a["pka"], a["pva"], a["psa"],
+                                 a["pcapa"], a["plena"], a["pmaxa"], a["rb"], a["nb"], a["pkb"],
+                                 a["pvb"], a["psb"], a["pcapb"], a["plenb"], a["pmaxb"], a["wk"],
+                                 a["wv"], a["wsd"], a["scale"], a["out"], a["os"], a["lse"],
+                                 a["ws"], wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=3), bd.BD_ERR_UNSUPPORTED),
+    (dict(Hq=33), bd.BD_ERR_INVALID_ARG),
+    (dict(nb=-1), bd.BD_ERR_INVALID_ARG),
+    (dict(rb=None), bd.BD_ERR_INVALID_ARG),
+    (dict(ra=None), bd.BD_ERR_INVALID_ARG),
+    (dict(plenb=None), bd.BD_ERR_INVALID_ARG),
+    (dict(pkb=None), bd.BD_ERR_INVALID_ARG),
+    (dict(pvb=MISALIGNED), bd.BD_ERR_INVALID_ARG),
+    (dict(psb=I3(1 << 20, 1024, 129)), bd.BD_ERR_INVALID_ARG),
+    (dict(scale=0.0), bd.BD_ERR_INVALID_ARG),
+    (dict(ws=None), bd.BD_ERR_WORKSPACE),
+])
+def test_attn_dual_validation(L, kw, code):
+    assert _attn_dual(L, **kw) == code
+
+
+def test_attn_dual_empty_and_one_list(L):
+    assert _attn_dual(L, na=0, nb=0) == bd.BD_OK
+    assert _attn_dual(L, q=0) == bd.BD_OK
+    # an empty list needs neither rows nor a prefix source
+    assert _attn_dual(L, na=0, ra=None, pka=None, pva=None, plena=None, nb=0, rb=None) == bd.BD_OK
+    # the workspace is the one-list workspace of all rows and the longer prefix
+    assert (bd.attn_dual_workspace_size(bd.BD_BF16, 64, 32, 8, 128, 128, 48, 8000, 16, 800)
+            == bd.attn_workspace_size(bd.BD_BF16, 64, 32, 8, 128, 128, 64, 8000))
 
 
 def test_mask_validation(L):

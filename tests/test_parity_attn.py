@@ -188,3 +188,83 @@ def test_tiny_dense_config(bd):
     ref, ref_lse = orc.cache_attention_eq6(wl.Q, wl.Kc, wl.Vc, wl.o, wl.bl, wl.sm_scale)
     check_attention(out, ref, torch.float32, label="tiny_dense")
     np.testing.assert_allclose(L.cpu().numpy(), ref_lse, atol=1e-5, rtol=1e-5)
+
+
+def _pool_case(rs, B, P, Hkv, d, k, dtype):
+    """Pool [B, P, Hkv, d] whose entries at or past each row's k_b hold NaN."""
+    s = 1.0 / math.sqrt(d)
+    PK = rs.standard_normal((B, P, Hkv, d)).astype(np.float32) * s
+    PV = rs.standard_normal((B, P, Hkv, d)).astype(np.float32) * s
+    for b in range(B):
+        PK[b, k[b]:] = np.nan
+        PV[b, k[b]:] = np.nan
+    return torch.from_numpy(PK).to(dtype), torch.from_numpy(PV).to(dtype)
+
+
+@pytest.mark.parametrize("B,o_max,k_max,W,d,G,dtype", [
+    (6, 3000, 400, 4, 128, 4, torch.bfloat16),    # longest-first order, one chunk per unit
+    (3, 1500, 300, 1, 128, 4, torch.bfloat16),    # few units: split prefixes + combine
+    (4, 700, 200, 2, 64, 2, torch.float32),       # general path
+])
+def test_dual_sources_match_each_source(bd, B, o_max, k_max, W, d, G, dtype):
+    """bd_attn_packed_dual: rows of list a over the cache (FlowBlock Eq. (6)),
+    rows of list b over a pool (HERALD's denoising attention), one row in
+    neither list (left untouched); each row matches the oracle for its own
+    source, and the LSE too."""
+    note(f"dual B={B} o_max={o_max} k_max={k_max} W={W} d={d} G={G} {dtype}")
+    rs = np.random.default_rng(70 + B)
+    Hkv, bl = 2, 32
+    q = W * bl
+    C = o_max + 64 + q
+    o = [int(x) for x in rs.integers(1, o_max, size=B)]
+    o[0] = o_max
+    kb = [int(x) for x in rs.integers(1, k_max, size=B)]
+    kb[-1] = k_max
+    Q, K, V, q, t = _cache_case(80 + B, B, C, G * Hkv, Hkv, d, bl, W, o, dtype=dtype)
+    PK, PV = _pool_case(rs, B, k_max + 32, Hkv, d, kb, dtype)
+    rows_a = [b for b in range(B - 1) if b % 2 == 0]
+    rows_b = [b for b in range(B - 1) if b % 2 == 1]
+    Qd, Kd, Vd, PKd, PVd = Q.cuda(), K.cuda(), V.cuda(), PK.cuda(), PV.cuda()
+    out = torch.full_like(Qd, 5.0)
+    L = torch.full((B, G * Hkv, q), 5.0, device="cuda")
+    i32 = lambda x: torch.tensor(x, dtype=torch.int32).cuda()
+    bd.attn_packed_dual(Qd, (i32(rows_a), Kd, Vd, i32(o), max(o)),
+                        (i32(rows_b), PKd, PVd, i32(kb), k_max),
+                        Kd[:, t:], Vd[:, t:], bl, 1.0 / math.sqrt(d), out=out, lse=L)
+    torch.cuda.synchronize()
+    ref_a, lse_a = orc.block_attention(Q, K, V, o, K[:, t:], V[:, t:], bl, 1.0 / math.sqrt(d),
+                                       rows=rows_a)
+    ref_b, lse_b = orc.block_attention(Q, PK, PV, kb, K[:, t:], V[:, t:], bl, 1.0 / math.sqrt(d),
+                                       rows=rows_b)
+    check_attention(out, ref_a, dtype, rows=rows_a, label="dual list a")
+    check_attention(out, ref_b, dtype, rows=rows_b, label="dual list b")
+    Lh = L.cpu().numpy()
+    tol = (2e-3, 1e-3) if dtype == torch.bfloat16 else (1e-5, 1e-5)
+    np.testing.assert_allclose(Lh[rows_a], lse_a[rows_a], atol=tol[0], rtol=tol[1])
+    np.testing.assert_allclose(Lh[rows_b], lse_b[rows_b], atol=tol[0], rtol=tol[1])
+    assert torch.all(out[B - 1] == 5.0) and torch.all(L[B - 1] == 5.0), "unlisted row written"
+
+
+def test_dual_equals_two_single_calls(bd):
+    """The one-launch call gives bit-identical outputs to two bd_attn_packed
+    calls (each row's arithmetic does not depend on the other list).  Prefixes
+    stay at or below 256 keys, so no call splits them into chunks and every
+    call runs the same per-row plan."""
+    note("dual vs two single calls")
+    rs = np.random.default_rng(91)
+    B, Hkv, G, d, bl, W = 8, 2, 4, 128, 32, 4
+    q = W * bl
+    o = [int(x) for x in rs.integers(100, 257, size=B)]
+    kb = [int(x) for x in rs.integers(50, 257, size=B)]
+    Q, K, V, q, t = _cache_case(92, B, max(o) + 64 + q, G * Hkv, Hkv, d, bl, W, o)
+    PK, PV = _pool_case(rs, B, 288, Hkv, d, kb, torch.bfloat16)
+    Qd, Kd, Vd, PKd, PVd = Q.cuda(), K.cuda(), V.cuda(), PK.cuda(), PV.cuda()
+    i32 = lambda x: torch.tensor(x, dtype=torch.int32).cuda()
+    ra, rb = [0, 2, 3, 5, 6], [1, 4, 7]
+    one = bd.attn_packed_dual(Qd, (i32(ra), Kd, Vd, i32(o), max(o)), (i32(rb), PKd, PVd, i32(kb), 256),
+                              Kd[:, t:], Vd[:, t:], bl, 0.1)
+    two = torch.empty_like(Qd)
+    bd.attn_packed(Qd, Kd, Vd, i32(o), max(o), Kd[:, t:], Vd[:, t:], bl, 0.1, out=two, row_ids=i32(ra))
+    bd.attn_packed(Qd, PKd, PVd, i32(kb), 256, Kd[:, t:], Vd[:, t:], bl, 0.1, out=two, row_ids=i32(rb))
+    torch.cuda.synchronize()
+    assert torch.equal(one, two)
