@@ -8,6 +8,13 @@ their own cache and of the sparse rows over their pools (one launch for
 both), and the KV write-back scatter of every row.  Inputs are resident in
 HBM before the timed region.
 
+The default 50 untimed warm-up steps (about 30 ms) bring the GPU to its
+steady state: the first few dozen steps of a fresh process run up to 8 %
+slower.  The timed region holds exactly ``--steps`` steps with no event
+between operations; a second pass over the same number of steps records an
+event after every operation for ``breakdown`` (those events add about 8 us
+per step).
+
 Prints one JSON line.  ``value`` is the whole-step throughput in attention
 TFLOP/s: the algorithmic attention FLOPs of the step (4*d per visible
 (query, key) pair per query head) divided by the step time, select, gather
@@ -237,7 +244,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -288,10 +295,25 @@ def main():
         print(f"{args.only}: {ms * 1e3:.1f} us per call over {args.steps} calls", flush=True)
         return
 
+    # timed region: exactly K steps and nothing else on the stream (an event
+    # recorded between two kernels adds a gap of its own, so the per-operation
+    # events are taken in a separate pass below)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step.run()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    ev_step = ev0.elapsed_time(ev1) / args.steps
+
+    # per-operation pass: the same K steps with an event after every operation
     ops = BlockDiffusionStep.OPS
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for s in range(args.steps):
         e = ev[s]
         e[0].record()
@@ -299,13 +321,11 @@ def main():
             getattr(step, name)()
             e[i + 1].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     op_ms = {name: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
              for i, name in enumerate(ops)}
-    ms_step = wall * 1e3 / args.steps
-    ev_step = sum(ev[s][0].elapsed_time(ev[s][-1]) for s in range(args.steps)) / args.steps
-    log(f"step {ms_step:.3f} ms (events {ev_step:.3f} ms): " +
-        ", ".join(f"{k} {v * 1e3:.1f} us" for k, v in op_ms.items()))
+    ev_step_ops = sum(ev[s][0].elapsed_time(ev[s][-1]) for s in range(args.steps)) / args.steps
+    log(f"step {ms_step:.3f} ms (events {ev_step:.3f} ms); with an event after every operation "
+        f"{ev_step_ops:.3f} ms: " + ", ".join(f"{k} {v * 1e3:.1f} us" for k, v in op_ms.items()))
 
     attn_flop = work["attn_dense_flop"] + work["attn_sparse_flop"]
     attn_bytes = work["attn_dense_bytes"] + work["attn_sparse_bytes"]
