@@ -154,12 +154,16 @@ def cpu_baseline(wl, budget_s: float = 12.0):
 
 def time_calls(fn, reps: int, warmup: int = 2) -> float:
     """Average milliseconds per call of ``fn`` (HIP events on the current
-    stream, which is the stream the library launches on)."""
+    stream, which is the stream the library launches on).  A spin kernel
+    ahead of the first event gives the host time to queue every call, so
+    short calls are timed back to back on the GPU, not at the host's launch
+    rate."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    torch.cuda._sleep(400_000)   # about 0.2 ms: the host gets ahead and stays ahead
     ev[0].record()
     for i in range(reps):
         fn()
@@ -172,14 +176,52 @@ def _rate(num, ms, scale):
     return round(num / (ms * 1e-3) / scale, 2)
 
 
+FLUSH_BYTES = 512 << 20   # larger than the MALL (256 MB) plus every L2
+
+
+def time_cold(fn, flush, reps: int):
+    """Milliseconds per call of ``fn`` with L2 and MALL flushed before each
+    call, outside the event pair: (median, p10, p90).  The flush reads a
+    512 MB buffer (an int64 sum), so the caches then hold clean lines; a
+    flush by writing would leave up to 256 MB of dirty lines whose write-back
+    the timed call would pay for."""
+    import torch
+    ts = []
+    for i in range(reps + 1):
+        flush.view(torch.int64).sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        if i > 0:   # the first call is a warm-up
+            ts.append(e0.elapsed_time(e1))
+    ts.sort()
+    q = lambda f: ts[min(len(ts) - 1, int(f * (len(ts) - 1) + 0.5))]
+    return q(0.5), q(0.1), q(0.9)
+
+
+def attainable_tflops(flop, nbytes, peak_tflops):
+    """min(MFMA peak, intensity x HBM peak)."""
+    return min(peak_tflops, flop / nbytes * PEAK_HBM_GBS / 1e3)
+
+
 def bench_configs(dev, reps: int = 10):
     """The other synthetic workloads, each in the launch configuration its
-    parity test checks: per-operation times and rates."""
+    parity test checks: per-operation times and rates, warm (back-to-back
+    calls, mean) and cold (L2 and MALL flushed before every call; median,
+    p10, p90 in ``*_cold_us``)."""
     import torch
     import synth
     from sparse_kv_cache_bd_amd import bdattn as bd
     from sparse_kv_cache_bd_amd.pipeline import BlockDiffusionStep
     out = {}
+    flush = torch.ones(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    cold_reps = 20
+
+    def cold(fn):
+        med, p10, p90 = time_cold(fn, flush, cold_reps)
+        return med, [round(med * 1e3, 2), round(p10 * 1e3, 2), round(p90 * 1e3, 2)]
 
     def kv_bytes(wl):
         return wl.Hkv * wl.d * (2 if wl.dtype == "bf16" else 4)
@@ -191,13 +233,23 @@ def bench_configs(dev, reps: int = 10):
         step = BlockDiffusionStep(Kc, Vc, Q, o, wl.bl, wl.sm_scale, p_max_dense=int(wl.o.max()))
         ms_a = time_calls(step.attn_dense, reps)
         ms_s = time_calls(step.scatter, reps)
+        ms_ac, q_ac = cold(step.attn_dense)
+        ms_sc, q_sc = cold(step.scatter)
         flop = attention_flops(wl.o, range(wl.B), wl.q, wl.bl, wl.Hq, wl.d)
+        es = 2 if wl.dtype == "bf16" else 4
+        abytes = sum(wl.q * wl.Hq * wl.d * es * 2 + (int(wl.o[b]) + wl.q) * kv_bytes(wl) * 2
+                     for b in range(wl.B))
         sbytes = wl.B * wl.q * kv_bytes(wl) * 2 * 2
         unit_peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else 157.3
+        att = attainable_tflops(flop, abytes, unit_peak)
         out[name] = {"dtype": wl.dtype, "rows": wl.B, "q": wl.q,
                      "attn_us": round(ms_a * 1e3, 2), "attn_TFLOP/s": _rate(flop, ms_a, 1e12),
                      "attn_frac_peak": round(flop / (ms_a * 1e-3) / 1e12 / unit_peak, 4),
-                     "scatter_us": round(ms_s * 1e3, 2), "scatter_GB/s": _rate(sbytes, ms_s, 1e9)}
+                     "attn_cold_us": q_ac,
+                     "attn_cold_frac_attainable": round(flop / (ms_ac * 1e-3) / 1e12 / att, 4),
+                     "attainable_TFLOP/s": round(att, 1),
+                     "scatter_us": round(ms_s * 1e3, 2), "scatter_GB/s": _rate(sbytes, ms_s, 1e9),
+                     "scatter_cold_us": q_sc, "scatter_cold_GB/s": _rate(sbytes, ms_sc, 1e9)}
         del step, Kc, Vc, Q, o
 
     for name in ("sparse_32k", "sparse_128k"):
@@ -211,9 +263,12 @@ def bench_configs(dev, reps: int = 10):
         ws = bd.workspace(bd.select_workspace_size(B, wl.Hq, Hkv, d, s_max, k_max), dev)
         pool_k = torch.zeros((B, k_max, Hkv, d), dtype=Kc.dtype, device=dev)
         pool_v = torch.zeros_like(pool_k)
-        ms_sel = time_calls(lambda: bd.select(Qsel, Kc, s_len, s_max, k_sel, k_max, wl.sm_scale,
-                                              idx_out=idx, ws=ws), reps)
-        ms_gat = time_calls(lambda: bd.gather(Kc, Vc, idx, k_sel, pool_k, pool_v), reps)
+        f_sel = lambda: bd.select(Qsel, Kc, s_len, s_max, k_sel, k_max, wl.sm_scale, idx_out=idx, ws=ws)
+        f_gat = lambda: bd.gather(Kc, Vc, idx, k_sel, pool_k, pool_v)
+        ms_sel = time_calls(f_sel, reps)
+        ms_gat = time_calls(f_gat, reps)
+        ms_selc, q_selc = cold(f_sel)
+        ms_gatc, q_gatc = cold(f_gat)
         steps_q = [x.to(dev) for x in wl.extra["step_q"]]
         steps_kv = [(a.to(dev), b.to(dev)) for a, b in wl.extra["step_kv"]]
         outb = torch.empty_like(steps_q[0])
@@ -225,18 +280,33 @@ def bench_configs(dev, reps: int = 10):
                 bd.attn_packed(steps_q[st], pool_k, pool_v, k_sel, k_max, wk, wv, wl.bl,
                                wl.sm_scale, out=outb, ws=ws_a)
         ms_att = time_calls(steps, max(2, reps // 2))
+        wk0, wv0 = steps_kv[0]
+        ms_attc, q_attc = cold(lambda: bd.attn_packed(steps_q[0], pool_k, pool_v, k_sel, k_max, wk0, wv0,
+                                                      wl.bl, wl.sm_scale, out=outb, ws=ws_a))
         sel_bytes = sum(int(wl.s_len[b]) for b in range(B)) * kv_bytes(wl) + B * Hkv * k_max * 4
         gat_bytes = sum(int(wl.k_sel[b]) for b in range(B)) * kv_bytes(wl) * 2 * 2
-        flop = wl.T * attention_flops(wl.k_sel, range(B), wl.q, wl.bl, wl.Hq, wl.d)
+        flop1 = attention_flops(wl.k_sel, range(B), wl.q, wl.bl, wl.Hq, wl.d)
+        flop = wl.T * flop1
+        abytes1 = sum(wl.q * wl.Hq * wl.d * 2 * 2 + (int(wl.k_sel[b]) + wl.q) * kv_bytes(wl) * 2
+                      for b in range(B))
+        att = attainable_tflops(flop1, abytes1, PEAK_BF16_TFLOPS)
         out[name] = {"rows": B, "prefix": s_max, "k": k_max, "T": wl.T,
                      "select_us": round(ms_sel * 1e3, 2), "select_GB/s": _rate(sel_bytes, ms_sel, 1e9),
                      "select_frac_hbm": round(sel_bytes / (ms_sel * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "select_cold_us": q_selc, "select_cold_GB/s": _rate(sel_bytes, ms_selc, 1e9),
+                     "select_cold_frac_hbm": round(sel_bytes / (ms_selc * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                      "gather_us": round(ms_gat * 1e3, 2), "gather_GB/s": _rate(gat_bytes, ms_gat, 1e9),
+                     "gather_cold_us": q_gatc, "gather_cold_GB/s": _rate(gat_bytes, ms_gatc, 1e9),
                      "attn_us_per_step": round(ms_att * 1e3 / wl.T, 2),
                      "attn_TFLOP/s": _rate(flop, ms_att, 1e12),
+                     "attn_cold_us_per_step": q_attc,
+                     "attn_cold_frac_attainable": round(flop1 / (ms_attc * 1e-3) / 1e12 / att, 4),
+                     "attainable_TFLOP/s": round(att, 1),
                      "block_us": round((ms_sel + ms_gat + ms_att) * 1e3, 2)}
         del Kc, Vc, pool_k, pool_v, ws, ws_a
         torch.cuda.empty_cache()
+    del flush
+    torch.cuda.empty_cache()
     return out
 
 
