@@ -480,16 +480,39 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int qi = u * S::NQ + qb * 32 + (col & 31);
   if (qi >= a.q) return;
   const int64_t prow0 = unit * a.n_split * S::NCOL + col;
+  // the partials of 8 chunks are loaded together (8 loads in flight), then
+  // merged in chunk order
+  constexpr int U = 8;
   float M = -INFINITY;
-  for (int cc = 0; cc < nc; ++cc) M = fmaxf(M, a.part_ml[(prow0 + (int64_t)cc * S::NCOL) * 2]);
+  for (int c0 = 0; c0 < nc; c0 += U) {
+    float mu[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      mu[u] = c0 + u < nc ? a.part_ml[(prow0 + (int64_t)(c0 + u) * S::NCOL) * 2] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) M = fmaxf(M, mu[u]);
+  }
   float L = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int cc = 0; cc < nc; ++cc) {
-    const int64_t prow = prow0 + (int64_t)cc * S::NCOL;
-    const float w = __builtin_amdgcn_exp2f(a.part_ml[prow * 2] - M);
-    L += a.part_ml[prow * 2 + 1] * w;
-    const f32x4 po = *reinterpret_cast<const f32x4 *>(a.part_o + prow * kD + d4 * 4);
-    acc += po * w;
+  for (int c0 = 0; c0 < nc; c0 += U) {
+    float2 ml[U];
+    f32x4 po[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c0 + u < nc) {
+        const int64_t prow = prow0 + (int64_t)(c0 + u) * S::NCOL;
+        ml[u] = *reinterpret_cast<const float2 *>(a.part_ml + prow * 2);
+        po[u] = *reinterpret_cast<const f32x4 *>(a.part_o + prow * kD + d4 * 4);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c0 + u < nc) {
+        const float w = __builtin_amdgcn_exp2f(ml[u].x - M);
+        L += ml[u].y * w;
+        acc += po[u] * w;
+      }
+    }
   }
   const float inv = 1.f / L;
   const int hq = h * G + g;
