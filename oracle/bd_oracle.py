@@ -45,6 +45,7 @@ __all__ = [
     "rep_query",
     "center_row",
     "selection_scores",
+    "multi_query_scores",
     "topk_select",
     "gather",
     "kv_scatter",
@@ -266,6 +267,44 @@ def selection_scores(q_rep, K, s_len, sm_scale: float):
             m[b, h * G:(h + 1) * G] = mg[:, 0]
             l[b, h * G:(h + 1) * G] = lg[:, 0]
     return s_hat, m, l
+
+
+def multi_query_scores(Q, K, s_len, sm_scale: float):
+    """Exact multi-query importance: every block query ranks the prefix.
+
+    HERALD Sec. III-C and Sec. IV-A2: before the query reduction, the
+    selection phase runs exact attention of all of the block's queries over
+    the full prefix KV (MAGE's selection at a block's first step; the
+    queries form a GEMM), and Fig. 8 sweeps the number of queries used.
+    The per-query probabilities are aggregated the way Sec. IV-B4 aggregates
+    the G query heads of a KV head: summed.  For row ``b``, KV head ``h``,
+    query ``i < nq`` and group head ``g < G``:
+    ``z[i, g, s] = sm_scale * <Q[b, i, h*G+g], K[b, s, h]>`` for ``s < S_b``
+    and ``s_hat[s] = sum_i sum_g exp(z[i, g, s] - m_ig) / l_ig`` with
+    ``m_ig = max_s z[i, g, s]``, ``l_ig = sum_s exp(z[i, g, s] - m_ig)``.
+    With ``nq = 1`` this is ``selection_scores`` with that query as q_rep.
+
+    Q: ``[B, nq, Hq, d]``; K: ``[B, C, Hkv, d]``; s_len: ``[B]``.
+    Returns ``s_hat [B, Hkv, max(s_len)]`` (0 past ``S_b``).
+    """
+    s_len = _i64(s_len)
+    B, nq, Hq, d = Q.shape
+    Hkv = K.shape[2]
+    G = Hq // Hkv
+    s_max = int(s_len.max()) if len(s_len) else 0
+    s_hat = np.zeros((B, Hkv, s_max))
+    for b in range(B):
+        S = int(s_len[b])
+        if S == 0:
+            continue
+        Qb = _f64(Q[b])                                    # [nq, Hq, d]
+        for h in range(Hkv):
+            cols = Qb[:, h * G:(h + 1) * G].reshape(nq * G, d)   # rows (i, g)
+            z = sm_scale * (cols @ _f64(K[b, :S, h]).T)          # [nq*G, S]
+            m = z.max(axis=1, keepdims=True)
+            e = np.exp(z - m)
+            s_hat[b, h, :S] = (e / e.sum(axis=1, keepdims=True)).sum(axis=0)
+    return s_hat
 
 
 def topk_select(scores, s_len, k_sel, k_max: int) -> np.ndarray:

@@ -137,3 +137,84 @@ def test_planted_keys_recalled():
         mask = np.zeros(wl.s_max, bool)
         mask[pos] = True
         assert sh[b, h, mask].min() > sh[b, h, ~mask].max()
+
+
+# ---------------------------------------------------------------------------
+# exact multi-query selection (HERALD Sec. III-C, Sec. IV-A2 Fig. 8)
+# ---------------------------------------------------------------------------
+
+def _mq_case(rs, B=2, nq=5, S=40, Hq=8, Hkv=2, d=16):
+    Q = rs.standard_normal((B, nq, Hq, d))
+    K = rs.standard_normal((B, S + 3, Hkv, d))
+    return Q, K
+
+
+def test_multi_query_single_query_reduces_to_selection_scores():
+    """nq = 1: exactly HERALD's single-query importance with that query."""
+    rs = np.random.default_rng(11)
+    Q, K = _mq_case(rs, B=2, nq=1, S=45)
+    s_len = np.array([45, 17])
+    got = orc.multi_query_scores(Q, K, s_len, 0.6)
+    want, _, _ = orc.selection_scores(Q[:, 0], K, s_len, 0.6)
+    np.testing.assert_allclose(got, want, rtol=1e-13, atol=1e-15)
+
+
+def test_multi_query_sum_and_attention_identity():
+    """sum_s s_hat = nq * G, and sum_s s_hat[s] V[s] equals the summed
+    attention outputs of every (query, head) column (torch SDPA)."""
+    rs = np.random.default_rng(12)
+    B, nq, S, Hq, Hkv, d = 2, 6, 33, 8, 2, 16
+    G = Hq // Hkv
+    Q, K = _mq_case(rs, B, nq, S, Hq, Hkv, d)
+    V = rs.standard_normal(K.shape)
+    s_len = np.array([S, 9])
+    sh = orc.multi_query_scores(Q, K, s_len, 0.45)
+    for b in range(B):
+        Sb = int(s_len[b])
+        for h in range(Hkv):
+            assert abs(sh[b, h, :Sb].sum() - nq * G) < 1e-11
+            assert (sh[b, h, Sb:] == 0).all()
+            qt = torch.from_numpy(Q[b, :, h * G:(h + 1) * G].reshape(nq * G, 1, d))
+            kt = torch.from_numpy(K[b, :Sb, h])[None].expand(nq * G, -1, -1)
+            vt = torch.from_numpy(V[b, :Sb, h])[None].expand(nq * G, -1, -1)
+            att = F.scaled_dot_product_attention(qt, kt, vt, scale=0.45)[:, 0].sum(0).numpy()
+            np.testing.assert_allclose(sh[b, h, :Sb] @ V[b, :Sb, h], att, rtol=1e-11, atol=1e-11)
+
+
+def test_multi_query_identical_queries_and_permutation():
+    """nq copies of one query give nq times its single-query scores (so the
+    same ranking); reordering the queries changes nothing."""
+    rs = np.random.default_rng(13)
+    Q, K = _mq_case(rs, B=1, nq=4, S=50)
+    same = np.repeat(Q[:, :1], 4, axis=1)
+    one, _, _ = orc.selection_scores(Q[:, 0], K, [50], 0.3)
+    np.testing.assert_allclose(orc.multi_query_scores(same, K, [50], 0.3), 4 * one, rtol=1e-12)
+    base = orc.multi_query_scores(Q, K, [50], 0.3)
+    perm = orc.multi_query_scores(Q[:, [2, 0, 3, 1]], K, [50], 0.3)
+    np.testing.assert_allclose(perm, base, rtol=1e-12, atol=1e-15)
+
+
+def test_multi_query_bruteforce_and_closed_forms():
+    """Brute force with math.exp on a tiny case; S = 1 gives nq*G; S = 2 is a
+    sum of logistic functions of the logit differences."""
+    rs = np.random.default_rng(14)
+    B, nq, S, Hq, Hkv, d = 1, 3, 6, 4, 2, 5
+    G = Hq // Hkv
+    Q, K = _mq_case(rs, B, nq, S, Hq, Hkv, d)
+    sh = orc.multi_query_scores(Q, K, [S], 0.8)
+    for h in range(Hkv):
+        for s in range(S):
+            tot = 0.0
+            for i in range(nq):
+                for g in range(G):
+                    z = [0.8 * sum(Q[0, i, h * G + g, e] * K[0, u, h, e] for e in range(d)) for u in range(S)]
+                    tot += math.exp(z[s]) / sum(math.exp(v) for v in z)
+            assert abs(sh[0, h, s] - tot) < 1e-12
+    sh1 = orc.multi_query_scores(Q, K, [1], 0.8)
+    np.testing.assert_allclose(sh1[0, :, 0], nq * G, rtol=1e-15)
+    sh2 = orc.multi_query_scores(Q, K, [2], 0.8)
+    for h in range(Hkv):
+        qc = Q[0, :, h * G:(h + 1) * G].reshape(-1, d)
+        dz = 0.8 * (qc @ (K[0, 0, h] - K[0, 1, h]))
+        np.testing.assert_allclose(sh2[0, h, 0], sps.expit(dz).sum(), rtol=1e-13)
+        np.testing.assert_allclose(sh2[0, h, 1], sps.expit(-dz).sum(), rtol=1e-13)
