@@ -206,6 +206,33 @@ def attainable_tflops(flop, nbytes, peak_tflops):
     return min(peak_tflops, flop / nbytes * PEAK_HBM_GBS / 1e3)
 
 
+def select_multi_sweep(bd, wl, Kc, s_len, k_sel, sel_bytes, ms_rep, dev, reps):
+    """Exact multi-query selection (every one of nq block queries ranks the
+    prefix) against the query count, as HERALD's Fig. 8 sweeps it: time per
+    call, K bytes read once over the call time (the kernels read K twice),
+    logit FLOPs (2*d per (query, query head, token)) and throughput relative
+    to nq = 32.  ``rep_mean_us`` is bd_select with the mean query."""
+    import torch
+    B, Hq, Hkv, d, k_max, s_max = wl.B, wl.Hq, wl.Hkv, wl.d, wl.k_max, wl.s_max
+    idx = torch.empty((B, Hkv, k_max), dtype=torch.int32, device=dev)
+    tokens = sum(int(wl.s_len[b]) for b in range(B))
+    res = {"rep_mean_us": round(ms_rep * 1e3, 2)}
+    for nq in (1, 2, 4, 8, 16, 32):
+        Qn = wl.Qsel[:, :nq].contiguous().to(dev)
+        ws = bd.workspace(bd.select_multi_workspace_size(B, Hq, Hkv, d, nq, s_max, k_max), dev)
+        ms = time_calls(lambda: bd.select_multi(Qn, Kc, s_len, s_max, k_sel, k_max, wl.sm_scale,
+                                                idx_out=idx, ws=ws), reps)
+        res[str(nq)] = {"us": round(ms * 1e3, 2), "GB/s": _rate(sel_bytes, ms, 1e9),
+                        "frac_hbm_once": round(sel_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                        "frac_hbm_two_passes": round(2 * sel_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                        "logit_TFLOP/s": _rate(2 * d * nq * Hq * tokens, ms, 1e12)}
+        del ws
+    base = res["32"]["us"]
+    for nq in (1, 2, 4, 8, 16, 32):
+        res[str(nq)]["speedup_vs_32"] = round(base / res[str(nq)]["us"], 3)
+    return res
+
+
 def bench_configs(dev, reps: int = 10):
     """The other synthetic workloads, each in the launch configuration its
     parity test checks: per-operation times and rates, warm (back-to-back
@@ -290,6 +317,9 @@ def bench_configs(dev, reps: int = 10):
         abytes1 = sum(wl.q * wl.Hq * wl.d * 2 * 2 + (int(wl.k_sel[b]) + wl.q) * kv_bytes(wl) * 2
                       for b in range(B))
         att = attainable_tflops(flop1, abytes1, PEAK_BF16_TFLOPS)
+        sweep = None
+        if name == "sparse_32k":
+            sweep = select_multi_sweep(bd, wl, Kc, s_len, k_sel, sel_bytes, ms_sel, dev, reps)
         out[name] = {"rows": B, "prefix": s_max, "k": k_max, "T": wl.T,
                      "select_us": round(ms_sel * 1e3, 2), "select_GB/s": _rate(sel_bytes, ms_sel, 1e9),
                      "select_frac_hbm": round(sel_bytes / (ms_sel * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
@@ -303,6 +333,8 @@ def bench_configs(dev, reps: int = 10):
                      "attn_cold_frac_attainable": round(flop1 / (ms_attc * 1e-3) / 1e12 / att, 4),
                      "attainable_TFLOP/s": round(att, 1),
                      "block_us": round((ms_sel + ms_gat + ms_att) * 1e3, 2)}
+        if sweep:
+            out[name]["select_multi_sweep"] = sweep
         del Kc, Vc, pool_k, pool_v, ws, ws_a
         torch.cuda.empty_cache()
     del flush

@@ -18,7 +18,9 @@
  *                   (FlowBlock review, Eq. (7) = paper Eq. 6).
  *
  * bd_attn_packed_dual runs bd_attn_packed for two row lists with different
- * prefix sources (cache rows and pool rows) in one launch.
+ * prefix sources (cache rows and pool rows) in one launch.  bd_select_multi
+ * is the exact selection in which every block query ranks the prefix (the
+ * step HERALD reduces to one representative query).
  *
  * Conventions shared by every call
  * --------------------------------
@@ -161,6 +163,41 @@ int bd_select(int dtype, int B, int Hq, int Hkv, int d, const void *q,
               const int32_t *s_len, int s_max, const int32_t *k_sel, int k_max,
               float sm_scale, int32_t *idx_out, float *score_out,
               void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * bd_select_multi: exact multi-query selection, the selection phase of
+ * HERALD Sec. III-C / Sec. IV-A2 before the query reduction (every block
+ * query ranks the prefix, as in MAGE's full-KV selection at a block's first
+ * step; Fig. 8 sweeps the number of queries).
+ *
+ * For every row b with S_b = s_len[b] > 0 and k_b = k_sel[b] > 0, KV head h,
+ * query i < nq and group head g < G = Hq / Hkv:
+ *   z[i, g, s]  = sm_scale * <q[b, i, h*G+g], k[b, s, h, :]>   for s < S_b
+ *   m_ig, l_ig  = max_s z[i, g, s],  sum_s exp(z[i, g, s] - m_ig)
+ *   score[h, s] = sum_i sum_g exp(z[i, g, s] - m_ig) / l_ig
+ * (the per-query probabilities are summed like the group heads' in
+ * Sec. IV-B4; nq = 1 gives bd_select's score with that query), and idx_out
+ * as in bd_select: the positions of the min(k_b, S_b) largest scores, ties to
+ * the lower position, ascending, -1 padded to k_max.
+ *
+ * Arguments, layouts, clamping and score_out are those of bd_select; q holds
+ * the nq raw block queries [B, nq, Hq, d] (no mean is taken).  The logits are
+ * bf16 products accumulated in fp32; K is read twice (statistics, then
+ * scores), the score matrix is never stored.
+ *   workspace at least bd_select_multi_workspace_size(...) bytes, 256-byte
+ *             aligned.
+ *
+ * Built for dtype BD_BF16 with d == 128 and nq * Hq / Hkv <= 128.
+ */
+size_t bd_select_multi_workspace_size(int B, int Hq, int Hkv, int d, int nq,
+                                      int s_max, int k_max);
+int bd_select_multi(int dtype, int B, int Hq, int Hkv, int d, const void *q,
+                    const int64_t q_strides[3], int nq, const void *k,
+                    const int64_t k_strides[3], int k_cap,
+                    const int32_t *s_len, int s_max, const int32_t *k_sel,
+                    int k_max, float sm_scale, int32_t *idx_out,
+                    float *score_out, void *workspace, size_t ws_bytes,
+                    void *stream);
 
 /*
  * bd_attn_packed: FlowBlock review Eq. (6) (paper Eq. 5) in prefix/window

@@ -38,6 +38,9 @@ _SIGS = {
     "bd_select_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
     "bd_select": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _i, _i, _i, _vp, _vp, _i, _vp, _i, _vp, _i,
                        ctypes.c_float, _vp, _vp, _vp, _sz, _vp]),
+    "bd_select_multi_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "bd_select_multi": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _i, _vp, _vp, _i, _vp, _i, _vp, _i,
+                             ctypes.c_float, _vp, _vp, _vp, _sz, _vp]),
     "bd_attn_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "bd_attn_packed": (_i, [_i, _i, _i, _i, _i, _i, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp, _i,
                             _vp, _i, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _sz,
@@ -189,6 +192,31 @@ def select(q, k, s_len, s_max: int, k_sel, k_max: int, sm_scale: float, rep_mode
                            rep_row, _ptr(k), _strides(k, 3), k.shape[1], _ptr(s_len), s_max,
                            _ptr(k_sel), k_max, float(sm_scale), _ptr(idx_out), _ptr(score_out),
                            _ptr(ws), 0 if ws is None else ws.numel(), _stream()))
+    return idx_out
+
+
+def select_multi_workspace_size(B, Hq, Hkv, d, nq, s_max, k_max) -> int:
+    return int(lib().bd_select_multi_workspace_size(B, Hq, Hkv, d, nq, s_max, k_max))
+
+
+def select_multi(q, k, s_len, s_max: int, k_sel, k_max: int, sm_scale: float, idx_out=None,
+                 score_out=None, ws=None):
+    """Exact multi-query top-k: every one of the nq queries of q
+    [B, nq, Hq, d] ranks k [B, C, Hkv, d].  Returns idx [B, Hkv, k_max]."""
+    q, k = _dev(q, "q"), _dev(k, "k")
+    B, nq, Hq, d = q.shape
+    Hkv = k.shape[2]
+    s_len, k_sel = _i32(s_len, "s_len"), _i32(k_sel, "k_sel")
+    if idx_out is None:
+        idx_out = torch.empty((B, Hkv, k_max), dtype=torch.int32, device=q.device)
+    need = select_multi_workspace_size(B, Hq, Hkv, d, nq, s_max, k_max)
+    if ws is None:
+        ws = workspace(need, q.device)
+    _check(lib().bd_select_multi(_DTYPE[q.dtype], B, Hq, Hkv, d, _ptr(q), _strides(q, 3), nq,
+                                 _ptr(k), _strides(k, 3), k.shape[1], _ptr(s_len), s_max,
+                                 _ptr(k_sel), k_max, float(sm_scale), _ptr(idx_out),
+                                 _ptr(score_out), _ptr(ws), 0 if ws is None else ws.numel(),
+                                 _stream()))
     return idx_out
 
 

@@ -168,6 +168,48 @@ int bd_select(int dtype, int B, int Hq, int Hkv, int d, const void *q, const int
   return hip_status(launch_select(a, (hipStream_t)stream), "bd_select launch");
 }
 
+size_t bd_select_multi_workspace_size(int B, int Hq, int Hkv, int d, int nq, int s_max, int k_max) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || nq <= 0 || s_max < 0 || k_max < 0) return 0;
+  return select_multi_workspace(B, Hkv, s_max);
+}
+
+int bd_select_multi(int dtype, int B, int Hq, int Hkv, int d, const void *q, const int64_t q_strides[3],
+                    int nq, const void *k, const int64_t k_strides[3], int k_cap, const int32_t *s_len,
+                    int s_max, const int32_t *k_sel, int k_max, float sm_scale, int32_t *idx_out,
+                    float *score_out, void *workspace, size_t ws_bytes, void *stream) {
+  g_err[0] = 0;
+  if (dtype != BD_BF16) return fail(BD_ERR_UNSUPPORTED, "bd_select_multi: only BD_BF16 is built");
+  if (d != 128) return fail(BD_ERR_UNSUPPORTED, "bd_select_multi: only d == 128 is built");
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || s_max < 0 || k_max < 0 || k_cap < 0)
+    return fail(BD_ERR_INVALID_ARG, "bd_select_multi: negative or zero size");
+  if (Hq % Hkv != 0) return fail(BD_ERR_INVALID_ARG, "bd_select_multi: Hq %% Hkv != 0");
+  if (nq <= 0) return fail(BD_ERR_INVALID_ARG, "bd_select_multi: nq must be positive");
+  if ((int64_t)nq * (Hq / Hkv) > 128)
+    return fail(BD_ERR_UNSUPPORTED, "bd_select_multi: needs nq * Hq/Hkv <= 128 (got %d * %d)", nq, Hq / Hkv);
+  if (B == 0 || k_max == 0) return BD_OK;
+  if (!idx_out || !s_len || !k_sel) return fail(BD_ERR_INVALID_ARG, "bd_select_multi: null pointer");
+  if (s_max > 0 && (!q || !k || !q_strides || !k_strides))
+    return fail(BD_ERR_INVALID_ARG, "bd_select_multi: null pointer");
+  if (!(sm_scale > 0.f) || sm_scale > 1e30f) return fail(BD_ERR_INVALID_ARG, "bd_select_multi: bad sm_scale");
+  if ((int64_t)B * Hkv > 65535 || B > 65535 || Hkv > 65535)
+    return fail(BD_ERR_INVALID_ARG, "bd_select_multi: too many rows for one launch");
+  if (s_max > 0 && (!strides_ok(q_strides, 3, 2) || !strides_ok(k_strides, 3, 2) || !aligned16(q) || !aligned16(k)))
+    return fail(BD_ERR_INVALID_ARG, "bd_select_multi: q/k must be 16-byte aligned with 16-byte stride multiples");
+  const size_t need = select_multi_workspace(B, Hkv, s_max);
+  if (!workspace || ws_bytes < need)
+    return fail(BD_ERR_WORKSPACE, "bd_select_multi: workspace %zu bytes, need %zu", ws_bytes, need);
+  if (((uintptr_t)workspace & 255u) != 0)
+    return fail(BD_ERR_WORKSPACE, "bd_select_multi: workspace must be 256-byte aligned");
+  SelectArgs a;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.d = d; a.nq = nq; a.rep_mode = BD_REP_MEAN;
+  a.rep_row = 0; a.k_cap = k_cap; a.s_max = s_max; a.k_max = k_max;
+  a.q = (const bf16 *)q; a.k = (const bf16 *)k;
+  for (int i = 0; i < 3; ++i) { a.qs[i] = q_strides ? q_strides[i] : 0; a.ks[i] = k_strides ? k_strides[i] : 0; }
+  a.s_len = s_len; a.k_sel = k_sel; a.scale2 = sm_scale * kLog2e;
+  a.idx_out = idx_out; a.score_out = score_out; a.ws = (char *)workspace;
+  return hip_status(launch_select_multi(a, (hipStream_t)stream), "bd_select_multi launch");
+}
+
 size_t bd_attn_workspace_size(int dtype, int B, int Hq, int Hkv, int d, int q, int n_rows, int p_max) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || q <= 0 || n_rows <= 0 || p_max < 0) return 0;
   return attn_plan(dtype, B, Hq, Hkv, d, q, n_rows, p_max).ws_bytes;

@@ -135,5 +135,8 @@ struct SelectArgs {
 };
 size_t select_workspace(int B, int Hq, int Hkv, int d, int s_max, int k_max);
 hipError_t launch_select(const SelectArgs &a, hipStream_t s);
+// Exact multi-query selection: nq * G <= 128 columns per KV head.
+size_t select_multi_workspace(int B, int Hkv, int s_max);
+hipError_t launch_select_multi(const SelectArgs &a, hipStream_t s);
 
 }  // namespace bd

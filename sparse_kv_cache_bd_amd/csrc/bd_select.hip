@@ -747,6 +747,303 @@ __global__ __launch_bounds__(kThreads) void sel_write_kernel(SelectArgs a, SelPt
     }
 }
 
+// ------------------------------------------------ exact multi-query selection
+// Every one of the nq block queries ranks the prefix (HERALD Sec. III-C and
+// Sec. IV-A2, the selection phase before the query reduction).  The columns
+// of KV head h are the nq*G pairs (query i, group head g), column c = i*G+g,
+// at most kMCols.  Two passes over K; no score matrix is stored:
+//   stats  per kMTok-token chunk and column, the (max, sum) of the logits in
+//          log2 units, from S = K Q^T with the tokens on the M side of
+//          v_mfma_f32_16x16x32_bf16 (a lane holds 4 tokens of one column, so
+//          the running statistics are lane-local).
+//   merge  fixed-order merge of the chunks: mp[c] = m_c + log2(l_c).
+//   score  the same dot products with the columns on the M side (a lane
+//          holds 4 columns of one token); s_hat[s] = sum_c exp2(z - mp[c]),
+//          written once: these are the values the top-k kernels rank.
+// The K fragments are loaded straight into registers (a lane reads 16 bytes
+// of 4 k-groups of one token: 64 contiguous bytes per token per load); the
+// next 64-token group is in flight while the current one is computed.  The
+// query columns (raw bf16, scaled after the MFMA in fp32) sit in LDS.
+constexpr int kMTok = 1024;     // tokens per block of the two passes
+constexpr int kMCols = 128;     // columns (query, group head) per KV head
+constexpr int kQStr = kSD + 8;  // LDS row stride of the staged columns (elements)
+
+struct MultiLayout {
+  size_t part, mp, scores, hist, ccount, total;
+  int nch, nch_topk;
+  bool multi;
+};
+
+MultiLayout multi_layout(int B, int Hkv, int s_max) {
+  MultiLayout L;
+  L.nch = (int)cdiv(s_max > 0 ? s_max : 1, kMTok);
+  L.nch_topk = (int)cdiv(s_max > 0 ? s_max : 1, kCK);
+  L.multi = s_max > kLdsKeys;
+  const size_t P = (size_t)B * Hkv;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  L.part = take(P * kMCols * (size_t)L.nch * 2 * 4);
+  L.mp = take(P * kMCols * 4);
+  L.scores = take(P * (size_t)s_max * 4);
+  L.hist = L.multi ? take(P * 3 * kBins * 4) : 0;
+  L.ccount = L.multi ? take(P * L.nch_topk * 2 * 4) : 0;
+  L.total = off;
+  return L;
+}
+
+struct MultiPtrs {
+  float *part, *mp, *scores;
+  uint32_t *hist;
+  int nch, ncol;
+  bool multi;
+};
+
+// Query columns of (row b, KV head h) into LDS, zero past ncol up to ncp.
+__device__ inline void stage_columns(const SelectArgs &a, int b, int h, int ncol, int ncp, bf16 *qs) {
+  for (int e = threadIdx.x; e < ncp * 16; e += blockDim.x) {
+    const int c = e >> 4, piece = e & 15;
+    bf16x8 v = bf16x8{};
+    if (c < ncol) {
+      const int i = c / a.G, g = c - i * a.G;
+      v = *reinterpret_cast<const bf16x8 *>(a.q + (int64_t)b * a.qs[0] + (int64_t)i * a.qs[1] +
+                                            (int64_t)(h * a.G + g) * a.qs[2] + piece * 8);
+    }
+    *reinterpret_cast<bf16x8 *>(qs + c * kQStr + piece * 8) = v;
+  }
+}
+
+// K fragments of one 64-token group: kf[tb][ks] holds token
+// t0 + 16*tb + (lane & 15), dims 32*ks + 8*(lane >> 4) .. +8.  Tokens past S
+// re-read token S-1 (their logits are masked or their scores not written).
+__device__ inline void load_group(const bf16 *kbase, int64_t kstride, int t0, int S, bf16x8 (&kf)[4][4]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    const int tok = min(t0 + 16 * tb + (lane & 15), S - 1);
+    const bf16 *kp = kbase + (int64_t)tok * kstride + 8 * (lane >> 4);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kf[tb][ks] = *reinterpret_cast<const bf16x8 *>(kp + 32 * ks);
+  }
+}
+
+// Block = (chunk of kMTok tokens, KV head, row), 4 waves; wave w takes the
+// 64-token groups w, w+4, w+8, w+12 of the chunk.
+__global__ __launch_bounds__(kThreads, 2) void selm_stats_kernel(SelectArgs a, MultiPtrs w) {
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int S, kb;
+  row_sizes(a, b, S, kb);
+  if (S == 0 || kb == 0 || c * kMTok >= S) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ncol = w.ncol, ncb = (ncol + 15) >> 4;
+  __shared__ __attribute__((aligned(16))) bf16 qs[kMCols * kQStr];
+  __shared__ float ml_lds[4][kMCols][2];
+  stage_columns(a, b, h, ncol, ncb * 16, qs);
+  __syncthreads();
+
+  const int s0 = c * kMTok, s_end = min(s0 + kMTok, S);
+  const int ng_all = (int)cdiv(s_end - s0, 64);
+  const int ng = ng_all > wave ? (int)cdiv(ng_all - wave, 4) : 0;   // this wave's groups
+  const bf16 *kbase = a.k + (int64_t)b * a.ks[0] + (int64_t)h * a.ks[2];
+  float m[8], l[8];
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb) {
+    m[cb] = -INFINITY;
+    l[cb] = 0.f;
+  }
+  auto t0_of = [&](int j) { return s0 + 64 * (wave + 4 * min(j, ng - 1)); };
+  auto compute = [&](int j, bf16x8 (&kf)[4][4]) {
+    const int t0 = t0_of(j);
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+      if (cb >= ncb) break;
+      bf16x8 qf[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        qf[ks] = *reinterpret_cast<const bf16x8 *>(qs + (cb * 16 + (lane & 15)) * kQStr + 32 * ks + 8 * (lane >> 4));
+      f32x4 z[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) z[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) z[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[tb][ks], qf[ks], z[tb], 0, 0, 0);
+      // lane holds tokens t0 + 16*tb + 4*(lane >> 4) + r of column cb*16 + (lane & 15)
+      float mx = -INFINITY;
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          z[tb][r] *= a.scale2;
+          if (t0 + 16 * tb + 4 * (lane >> 4) + r >= S) z[tb][r] = -INFINITY;
+          mx = fmaxf(mx, z[tb][r]);
+        }
+      const float mn = fmaxf(m[cb], mx);
+      if (mn != -INFINITY) {
+        float acc = l[cb] * __builtin_amdgcn_exp2f(m[cb] - mn);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc += __builtin_amdgcn_exp2f(z[tb][r] - mn);
+        l[cb] = acc;
+        m[cb] = mn;
+      }
+    }
+  };
+  if (ng > 0) {
+    bf16x8 ka[4][4], kb2[4][4];
+    load_group(kbase, a.ks[1], t0_of(0), S, ka);
+    load_group(kbase, a.ks[1], t0_of(1), S, kb2);
+    compute(0, ka);
+    load_group(kbase, a.ks[1], t0_of(2), S, ka);
+    if (1 < ng) compute(1, kb2);
+    load_group(kbase, a.ks[1], t0_of(3), S, kb2);
+    if (2 < ng) compute(2, ka);
+    if (3 < ng) compute(3, kb2);
+  }
+  // merge the 4 lane groups holding the same column, then the 4 waves
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb) {
+    if (cb >= ncb) break;
+#pragma unroll
+    for (int o = 16; o < 64; o <<= 1) merge_ml(m[cb], l[cb], __shfl_xor(m[cb], o), __shfl_xor(l[cb], o));
+    if (lane < 16) {
+      ml_lds[wave][cb * 16 + lane][0] = m[cb];
+      ml_lds[wave][cb * 16 + lane][1] = l[cb];
+    }
+  }
+  __syncthreads();
+  for (int col = tid; col < ncol; col += kThreads) {
+    float M = -INFINITY, Lsum = 0.f;
+    for (int wv = 0; wv < 4; ++wv) merge_ml(M, Lsum, ml_lds[wv][col][0], ml_lds[wv][col][1]);
+    float *pp = w.part + ((((int64_t)b * a.Hkv + h) * kMCols + col) * w.nch + c) * 2;
+    pp[0] = M;
+    pp[1] = Lsum;
+  }
+}
+
+// Block = (KV head, row), kMCols threads: mp[c] = m_c + log2(l_c) over the
+// chunks in order; clears the row's digit histograms for the ranking.
+__global__ __launch_bounds__(kMCols) void selm_merge_kernel(SelectArgs a, MultiPtrs w) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  int S, kb;
+  row_sizes(a, b, S, kb);
+  if (S == 0 || kb == 0) return;
+  const int nch = (int)cdiv(S, kMTok);
+  const int col = threadIdx.x;
+  if (col < w.ncol) {
+    const float *pp = w.part + (((int64_t)b * a.Hkv + h) * kMCols + col) * w.nch * 2;
+    float M = -INFINITY, Lsum = 0.f;
+    for (int c0 = 0; c0 < nch; c0 += 8) {  // 8 loads in flight, merged in order
+      float2 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = c0 + u < nch ? *reinterpret_cast<const float2 *>(pp + (c0 + u) * 2) : float2{-INFINITY, 0.f};
+#pragma unroll
+      for (int u = 0; u < 8; ++u) merge_ml(M, Lsum, v[u].x, v[u].y);
+    }
+    w.mp[((int64_t)b * a.Hkv + h) * kMCols + col] = M + __log2f(Lsum);
+  }
+  if (w.multi) {
+    uint32_t *hist = w.hist + ((size_t)b * a.Hkv + h) * 3 * kBins;
+    for (int e = threadIdx.x; e < 3 * kBins; e += kMCols) hist[e] = 0;
+  }
+}
+
+// Block = (chunk of kMTok tokens, KV head, row), 4 waves as in the stats pass.
+__global__ __launch_bounds__(kThreads, 2) void selm_score_kernel(SelectArgs a, MultiPtrs w) {
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int S, kb;
+  row_sizes(a, b, S, kb);
+  if (S == 0 || kb == 0 || c * kMTok >= S) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ncol = w.ncol, ncb = (ncol + 15) >> 4;
+  __shared__ __attribute__((aligned(16))) bf16 qs[kMCols * kQStr];
+  __shared__ __attribute__((aligned(16))) float mps[kMCols];
+  __shared__ uint32_t hist[kBins];
+  stage_columns(a, b, h, ncol, ncb * 16, qs);
+  for (int col = tid; col < kMCols; col += kThreads)
+    mps[col] = col < ncol ? w.mp[((int64_t)b * a.Hkv + h) * kMCols + col] : INFINITY;
+  if (w.multi)
+    for (int e = tid; e < kBins; e += kThreads) hist[e] = 0;
+  __syncthreads();
+
+  const int s0 = c * kMTok, s_end = min(s0 + kMTok, S);
+  const int ng_all = (int)cdiv(s_end - s0, 64);
+  const int ng = ng_all > wave ? (int)cdiv(ng_all - wave, 4) : 0;
+  const bf16 *kbase = a.k + (int64_t)b * a.ks[0] + (int64_t)h * a.ks[2];
+  float *orow = w.scores + ((int64_t)b * a.Hkv + h) * a.s_max;
+  auto t0_of = [&](int j) { return s0 + 64 * (wave + 4 * min(j, ng - 1)); };
+  auto compute = [&](int j, bf16x8 (&kf)[4][4]) {
+    const int t0 = t0_of(j);
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+      if (cb >= ncb) break;
+      bf16x8 qf[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        qf[ks] = *reinterpret_cast<const bf16x8 *>(qs + (cb * 16 + (lane & 15)) * kQStr + 32 * ks + 8 * (lane >> 4));
+      // columns cb*16 + 4*(lane >> 4) + r of the lane
+      const f32x4 mp = *reinterpret_cast<const f32x4 *>(mps + cb * 16 + 4 * (lane >> 4));
+      f32x4 z[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) z[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) z[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], kf[tb][ks], z[tb], 0, 0, 0);
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[tb] += __builtin_amdgcn_exp2f(__builtin_fmaf(z[tb][r], a.scale2, -mp[r]));
+    }
+    // sum over the 4 lane groups (the other columns), fixed butterfly
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      acc[tb] += __shfl_xor(acc[tb], 16);
+      acc[tb] += __shfl_xor(acc[tb], 32);
+    }
+    // lane L writes token t0 + L: token block L >> 4, token L & 15 of it
+    const int grp = lane >> 4;
+    const float v = grp == 0 ? acc[0] : (grp == 1 ? acc[1] : (grp == 2 ? acc[2] : acc[3]));
+    const int tok = t0 + lane;
+    if (tok < S) orow[tok] = v;
+    if (w.multi) hist_add(hist, __float_as_uint(v) >> 21, tok < S);
+  };
+  if (ng > 0) {
+    bf16x8 ka[4][4], kb2[4][4];
+    load_group(kbase, a.ks[1], t0_of(0), S, ka);
+    load_group(kbase, a.ks[1], t0_of(1), S, kb2);
+    compute(0, ka);
+    load_group(kbase, a.ks[1], t0_of(2), S, ka);
+    if (1 < ng) compute(1, kb2);
+    load_group(kbase, a.ks[1], t0_of(3), S, kb2);
+    if (2 < ng) compute(2, ka);
+    if (3 < ng) compute(3, kb2);
+  }
+  if (w.multi) {  // first radix digit of the scores just written
+    __syncthreads();
+    uint32_t *gh = w.hist + ((size_t)b * a.Hkv + h) * 3 * kBins;
+    for (int e = tid; e < kBins; e += kThreads)
+      if (hist[e]) atomicAdd(&gh[e], hist[e]);
+  }
+}
+
+// Top-k of the scores in w.scores (one LDS block per row, or the
+// multi-block ranking for rows longer than kLdsKeys).
+hipError_t launch_rank(const SelectArgs &a, const SelPtrs &w, hipStream_t s) {
+  if (!w.multi) {
+    hipLaunchKernelGGL(sel_topk_kernel, dim3(a.B * a.Hkv), dim3(kTopkThreads), 0, s, a, w);
+    return hipGetLastError();
+  }
+  const dim3 tg(w.nch_topk, a.B * a.Hkv);
+  hipLaunchKernelGGL(sel_hist_kernel<1>, tg, dim3(kThreads), 0, s, a, w);
+  hipLaunchKernelGGL(sel_hist_kernel<2>, tg, dim3(kThreads), 0, s, a, w);
+  hipLaunchKernelGGL(sel_count_kernel, tg, dim3(kThreads), 0, s, a, w);
+  hipLaunchKernelGGL(sel_write_kernel, tg, dim3(kThreads), 0, s, a, w);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 size_t select_workspace(int B, int Hq, int Hkv, int d, int s_max, int k_max) {
@@ -777,16 +1074,36 @@ hipError_t launch_select(const SelectArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(sel_score_kernel, dim3((unsigned)cdiv(a.s_max, kScoreTok), a.Hkv, a.B),
                      dim3(kThreads), 0, s, a, w);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (!L.multi) {
-    hipLaunchKernelGGL(sel_topk_kernel, dim3(a.B * a.Hkv), dim3(kTopkThreads), 0, s, a, w);
-    return hipGetLastError();
-  }
-  const dim3 tg(L.nch_topk, a.B * a.Hkv);
-  hipLaunchKernelGGL(sel_hist_kernel<1>, tg, dim3(kThreads), 0, s, a, w);
-  hipLaunchKernelGGL(sel_hist_kernel<2>, tg, dim3(kThreads), 0, s, a, w);
-  hipLaunchKernelGGL(sel_count_kernel, tg, dim3(kThreads), 0, s, a, w);
-  hipLaunchKernelGGL(sel_write_kernel, tg, dim3(kThreads), 0, s, a, w);
-  return hipGetLastError();
+  return launch_rank(a, w, s);
+}
+
+size_t select_multi_workspace(int B, int Hkv, int s_max) { return multi_layout(B, Hkv, s_max).total; }
+
+hipError_t launch_select_multi(const SelectArgs &a, hipStream_t s) {
+  const MultiLayout L = multi_layout(a.B, a.Hkv, a.s_max);
+  MultiPtrs m;
+  m.part = reinterpret_cast<float *>(a.ws + L.part);
+  m.mp = reinterpret_cast<float *>(a.ws + L.mp);
+  m.scores = a.score_out ? a.score_out : reinterpret_cast<float *>(a.ws + L.scores);
+  m.hist = reinterpret_cast<uint32_t *>(a.ws + L.hist);
+  m.nch = L.nch;
+  m.ncol = a.nq * a.G;
+  m.multi = L.multi;
+  SelPtrs w{};
+  w.scores = m.scores;
+  w.hist = m.hist;
+  w.ccount = reinterpret_cast<uint32_t *>(a.ws + L.ccount);
+  w.nch_topk = L.nch_topk;
+  w.multi = L.multi;
+  const dim3 grid(L.nch, a.Hkv, a.B);
+  hipError_t e;
+  hipLaunchKernelGGL(selm_stats_kernel, grid, dim3(kThreads), 0, s, a, m);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(selm_merge_kernel, dim3(a.Hkv, a.B), dim3(kMCols), 0, s, a, m);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(selm_score_kernel, grid, dim3(kThreads), 0, s, a, m);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return launch_rank(a, w, s);
 }
 
 }  // namespace bd

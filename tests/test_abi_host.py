@@ -24,7 +24,7 @@ def L():
 
 def test_exports_every_header_function(L):
     names = bd.header_functions()
-    assert len(names) == 11
+    assert len(names) == 13
     for n in names:
         assert hasattr(L, n), n
 
@@ -125,6 +125,48 @@ def test_select_workspace_too_small(L):
     assert need > 0
     assert _select(L, ws_bytes=need - 1) == bd.BD_ERR_WORKSPACE
     assert "need" in bd.last_error()
+
+
+def _select_multi(L, ws_bytes=None, **kw):
+    a = dict(dtype=bd.BD_BF16, B=2, Hq=32, Hkv=8, d=128, q=FAKE, qs=I3(32 * 4096, 4096, 128),
+             nq=32, k=FAKE2, ks=I3(1 << 22, 1024, 128), kcap=4000, s_len=FAKE, s_max=4000,
+             k_sel=FAKE, k_max=200, scale=0.088, idx=FAKE, score=None, ws=FAKE)
+    a.update(kw)
+    need = bd.select_multi_workspace_size(a["B"], a["Hq"], a["Hkv"], a["d"], a["nq"], a["s_max"],
+                                          a["k_max"])
+    wsb = need if ws_bytes is None else ws_bytes
+    return L.bd_select_multi(a["dtype"], a["B"], a["Hq"], a["Hkv"], a["d"], a["q"], a["qs"],
+                             a["nq"], a["k"], a["ks"], a["kcap"], a["s_len"], a["s_max"],
+                             a["k_sel"], a["k_max"], a["scale"], a["idx"], a["score"], a["ws"],
+                             wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=bd.BD_F32), bd.BD_ERR_UNSUPPORTED),
+    (dict(d=64), bd.BD_ERR_UNSUPPORTED),
+    (dict(Hq=30), bd.BD_ERR_INVALID_ARG),
+    (dict(nq=33), bd.BD_ERR_UNSUPPORTED),               # 33 * 4 columns > 128
+    (dict(Hq=64, Hkv=8, nq=17), bd.BD_ERR_UNSUPPORTED),  # 17 * 8 > 128
+    (dict(nq=0), bd.BD_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), bd.BD_ERR_INVALID_ARG),
+    (dict(idx=None), bd.BD_ERR_INVALID_ARG),
+    (dict(q=MISALIGNED), bd.BD_ERR_INVALID_ARG),
+    (dict(qs=I3(32 * 4096, 4096, 100)), bd.BD_ERR_INVALID_ARG),   # head stride not 16 B
+    (dict(ws=None), bd.BD_ERR_WORKSPACE),
+    (dict(ws=ctypes.c_void_p(0x100010)), bd.BD_ERR_WORKSPACE),
+])
+def test_select_multi_validation(L, kw, code):
+    assert _select_multi(L, **kw) == code
+
+
+def test_select_multi_workspace(L):
+    need = bd.select_multi_workspace_size(2, 32, 8, 128, 32, 4000, 200)
+    assert need > 0
+    assert _select_multi(L, ws_bytes=need - 1) == bd.BD_ERR_WORKSPACE
+    assert _select_multi(L, B=0) == bd.BD_OK and _select_multi(L, k_max=0) == bd.BD_OK
+    # more prefix needs more chunk partials and scores; longer than 32K adds the ranking histograms
+    assert bd.select_multi_workspace_size(1, 32, 8, 128, 32, 40000, 200) > \
+        bd.select_multi_workspace_size(1, 32, 8, 128, 32, 32768, 200) > need // 2 > 0
 
 
 def test_workspace_sizes_monotone():
