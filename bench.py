@@ -241,7 +241,7 @@ def bench_configs(dev, reps: int = 10):
     import torch
     import synth
     from sparse_kv_cache_bd_amd import bdattn as bd
-    from sparse_kv_cache_bd_amd.pipeline import BlockDiffusionStep
+    from sparse_kv_cache_bd_amd.pipeline import BlockDiffusionStep, SparseBlockPipeline
     out = {}
     flush = torch.ones(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     cold_reps = 20
@@ -310,6 +310,14 @@ def bench_configs(dev, reps: int = 10):
         wk0, wv0 = steps_kv[0]
         ms_attc, q_attc = cold(lambda: bd.attn_packed(steps_q[0], pool_k, pool_v, k_sel, k_max, wk0, wv0,
                                                       wl.bl, wl.sm_scale, out=outb, ws=ws_a))
+        # HERALD's dual-stream schedule: block n+1's select + gather on a second
+        # stream under block n's denoising steps, double-buffered pools
+        pipe = SparseBlockPipeline(Kc, Vc, Qsel, s_len, k_sel, s_max, k_max, wl.sm_scale, wl.bl,
+                                   steps_q, steps_kv)
+        nb = 4
+        ms_pseq = time_calls(lambda: pipe.run_sequential(nb), max(2, reps // 2)) / nb
+        ms_povl = time_calls(lambda: pipe.run_overlapped(nb), max(2, reps // 2)) / nb
+        del pipe
         sel_bytes = sum(int(wl.s_len[b]) for b in range(B)) * kv_bytes(wl) + B * Hkv * k_max * 4
         gat_bytes = sum(int(wl.k_sel[b]) for b in range(B)) * kv_bytes(wl) * 2 * 2
         flop1 = attention_flops(wl.k_sel, range(B), wl.q, wl.bl, wl.Hq, wl.d)
@@ -332,7 +340,10 @@ def bench_configs(dev, reps: int = 10):
                      "attn_cold_us_per_step": q_attc,
                      "attn_cold_frac_attainable": round(flop1 / (ms_attc * 1e-3) / 1e12 / att, 4),
                      "attainable_TFLOP/s": round(att, 1),
-                     "block_us": round((ms_sel + ms_gat + ms_att) * 1e3, 2)}
+                     "block_us": round((ms_sel + ms_gat + ms_att) * 1e3, 2),
+                     "pipeline": {"blocks": nb, "block_us_sequential": round(ms_pseq * 1e3, 2),
+                                  "block_us_overlapped": round(ms_povl * 1e3, 2),
+                                  "speedup": round(ms_pseq / ms_povl, 3)}}
         if sweep:
             out[name]["select_multi_sweep"] = sweep
         del Kc, Vc, pool_k, pool_v, ws, ws_a

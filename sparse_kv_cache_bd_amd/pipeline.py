@@ -115,3 +115,93 @@ class BlockDiffusionStep:
         self.attn()
         self.scatter()
         return self.out
+
+
+class SparseBlockPipeline:
+    """HERALD's dual-stream schedule of the sparse path on one GPU (Sec.
+    IV-B2, Fig. 10; double-buffered sparse pools of Sec. IV-B1).
+
+    Block n denoises for T steps on the main stream, each step one
+    bd_attn_packed over pool[n % 2] plus that step's in-block KV.  Block
+    n+1's selection phase (bd_select + bd_gather into pool[(n+1) % 2]) runs
+    on a second stream: it starts once block n's second step has been issued
+    (HERALD's draft of block n exists from then on) and block n+1's first
+    step waits for its gather.  The pool a selection writes was last read by
+    block n-1, which the main stream finished before block n's second step.
+
+    ``run_sequential`` issues the same calls in order on one stream; both
+    give bit-identical pools and outputs (the same kernels on the same
+    inputs).  The selection inputs are the same for every block: the
+    schedule, not the content of successive blocks, is what this measures.
+    Both streams have the default priority.
+    """
+
+    def __init__(self, Kc, Vc, Qsel, s_len, k_sel, s_max: int, k_max: int, sm_scale: float,
+                 bl: int, steps_q, steps_kv):
+        self.dev = Kc.device
+        self.Kc, self.Vc, self.Qsel = Kc, Vc, Qsel
+        self.B, _, self.Hkv, self.d = Kc.shape
+        self.Hq = Qsel.shape[2]
+        self.s_len, self.k_sel = s_len, k_sel
+        self.s_max, self.k_max = int(s_max), int(k_max)
+        self.sm_scale, self.bl = sm_scale, bl
+        self.steps_q, self.steps_kv = steps_q, steps_kv
+        self.T = len(steps_q)
+        i32 = dict(dtype=torch.int32, device=self.dev)
+        self.idx = torch.empty((self.B, self.Hkv, self.k_max), **i32)
+        self.pools = [(torch.zeros((self.B, self.k_max, self.Hkv, self.d), dtype=Kc.dtype,
+                                   device=self.dev),
+                       torch.zeros((self.B, self.k_max, self.Hkv, self.d), dtype=Kc.dtype,
+                                   device=self.dev)) for _ in range(2)]
+        self.out = torch.zeros_like(steps_q[0])
+        nq = steps_q[0].shape[1]
+        self.ws_sel = bd.workspace(bd.select_workspace_size(self.B, self.Hq, self.Hkv, self.d,
+                                                            self.s_max, self.k_max), self.dev)
+        self.ws_attn = bd.workspace(bd.attn_workspace_size(steps_q[0].dtype, self.B, self.Hq,
+                                                           self.Hkv, self.d, nq, self.B,
+                                                           self.k_max), self.dev)
+        self.retrieval = torch.cuda.Stream(device=self.dev)
+        self.ev_ready = [torch.cuda.Event(), torch.cuda.Event()]
+        self.ev_draft = torch.cuda.Event()
+
+    def retrieve(self, slot: int):
+        """Selection phase of one block into pool ``slot`` (current stream)."""
+        pk, pv = self.pools[slot]
+        bd.select(self.Qsel, self.Kc, self.s_len, self.s_max, self.k_sel, self.k_max,
+                  self.sm_scale, idx_out=self.idx, ws=self.ws_sel)
+        bd.gather(self.Kc, self.Vc, self.idx, self.k_sel, pk, pv)
+
+    def denoise(self, slot: int, st: int):
+        """Denoising step ``st`` of one block over pool ``slot`` (current stream)."""
+        pk, pv = self.pools[slot]
+        wk, wv = self.steps_kv[st]
+        bd.attn_packed(self.steps_q[st], pk, pv, self.k_sel, self.k_max, wk, wv, self.bl,
+                       self.sm_scale, out=self.out, ws=self.ws_attn)
+
+    def run_sequential(self, n_blocks: int):
+        for n in range(n_blocks):
+            self.retrieve(n % 2)
+            for st in range(self.T):
+                self.denoise(n % 2, st)
+        return self.out
+
+    def run_overlapped(self, n_blocks: int):
+        main, ret = torch.cuda.current_stream(self.dev), self.retrieval
+        ret.wait_stream(main)
+        with torch.cuda.stream(ret):
+            self.retrieve(0)
+            self.ev_ready[0].record(ret)
+        start_next = min(1, self.T - 1)   # after block n's second step
+        for n in range(n_blocks):
+            slot = n % 2
+            main.wait_event(self.ev_ready[slot])
+            for st in range(self.T):
+                self.denoise(slot, st)
+                if st == start_next and n + 1 < n_blocks:
+                    self.ev_draft.record(main)
+                    ret.wait_event(self.ev_draft)
+                    with torch.cuda.stream(ret):
+                        self.retrieve((n + 1) % 2)
+                        self.ev_ready[(n + 1) % 2].record(ret)
+        main.wait_stream(ret)
+        return self.out
