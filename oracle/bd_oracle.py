@@ -71,37 +71,59 @@ def _i64(x):
 # Mask
 # ---------------------------------------------------------------------------
 
-def eq6_mask(C: int, q: int, bl: int, o) -> np.ndarray:
+MASK_MODES = ("block_causal", "isolated", "shared_first")
+
+
+def eq6_mask(C: int, q: int, bl: int, o, mode: str = "block_causal") -> np.ndarray:
     """Per-row block-diagonal mask over a cache of capacity ``C``.
 
     FlowBlock review, Eq. (6) (paper Eq. 5): query ``i`` of row ``b`` sees
     key ``j`` when ``j < o_b`` (the row's own frozen prefix) or when
     ``t <= j < t + (s+1)*bl`` with ``t = C - q`` the shared physical tail
     where the window's present KV lives and ``s = floor(i / bl)`` the
-    query's window slot.
+    query's window slot.  Other ``mode`` values replace the tail part by
+    ``window_visible``'s other modes (the prefix part is unchanged).
 
     Returns a bool array ``[B, q, C]``.
     """
     o = _i64(o)
     t = C - q
-    i = np.arange(q)[:, None]
     j = np.arange(C)[None, :]
-    s = i // bl
-    own_tail = (j >= t) & (j < t + (s + 1) * bl)          # [q, C]
+    own_tail = np.zeros((q, C), bool)
+    own_tail[:, t:] = window_visible(q, bl, mode)          # [q, C]
     own_prefix = j[None, :, :] < o[:, None, None]          # [B, 1, C]
     return own_prefix | own_tail[None, :, :]
 
 
-def window_visible(q: int, bl: int) -> np.ndarray:
-    """Window part of Eq. (6) in window coordinates ``w = j - t``.
+def window_visible(q: int, bl: int, mode: str = "block_causal") -> np.ndarray:
+    """Window part of the mask in window coordinates ``w = j - t``; the
+    window holds ``q / bl`` blocks (groups) of ``bl`` queries and keys.
 
-    Query ``i`` sees window key ``w`` when ``w < (floor(i/bl) + 1) * bl``:
-    bidirectional inside its own block and causal over earlier window
-    blocks (FlowBlock review, W-shaped block-causal mask).  ``[q, q]`` bool.
+    ``block_causal`` (FlowBlock review Eq. (6)): query ``i`` sees window key
+    ``w`` when ``w < (floor(i/bl) + 1) * bl``: bidirectional inside its own
+    block and causal over earlier window blocks (W-shaped mask).
+
+    ``isolated`` (HERALD Sec. IV-B2): the denoising group and the draft
+    group run in one forward pass; each sees the prefix and its own group
+    (bidirectionally) but not the other: ``floor(w/bl) == floor(i/bl)``.
+
+    ``shared_first`` (Flash-dLLM's verify pass; reading of a garbled
+    passage): block 0 holds the tracked context, the later blocks are views
+    of the search positions; the context does not see the views and the
+    views do not see each other, each view sees the context:
+    ``floor(w/bl) == floor(i/bl)`` or ``floor(w/bl) == 0``.
+
+    Returns ``[q, q]`` bool.
     """
-    i = np.arange(q)[:, None]
-    w = np.arange(q)[None, :]
-    return w < (i // bl + 1) * bl
+    if mode not in MASK_MODES:
+        raise ValueError(f"unknown mask mode {mode!r}")
+    gi = np.arange(q)[:, None] // bl
+    gw = np.arange(q)[None, :] // bl
+    if mode == "block_causal":
+        return gw <= gi
+    if mode == "isolated":
+        return gw == gi
+    return (gw == gi) | (gw == 0)
 
 
 # ---------------------------------------------------------------------------
@@ -124,7 +146,7 @@ def _softmax_attend(logits: np.ndarray, vals: np.ndarray):
 
 
 def block_attention(Q, PK, PV, p_len, WK, WV, bl: int, sm_scale: float,
-                    rows=None):
+                    rows=None, mode: str = "block_causal"):
     """Block-diffusion attention in prefix/window form.
 
     For row ``b``, query ``i`` and query head ``hq`` (KV head ``h = hq//G``)
@@ -134,7 +156,8 @@ def block_attention(Q, PK, PV, p_len, WK, WV, bl: int, sm_scale: float,
     (the window is the cache tail ``[t, C)``); with ``PK`` a compact pool of
     selected entries and ``p_len = k_b`` it is HERALD's denoising attention
     over the critical KV cache (Sec. III-C, IV-B1), where the block attends
-    bidirectionally in-block and to the cached prefix (Sec. II-A).
+    bidirectionally in-block and to the cached prefix (Sec. II-A).  ``mode``
+    picks the window mask (``window_visible``).
 
     Q: [B, q, Hq, d]; PK, PV: [B, P, Hkv, d]; WK, WV: [B, q, Hkv, d].
     Returns ``O [B, q, Hq, d]`` and ``LSE [B, Hq, q]`` in float64; rows not
@@ -147,7 +170,7 @@ def block_attention(Q, PK, PV, p_len, WK, WV, bl: int, sm_scale: float,
     G = Hq // Hkv
     assert G * Hkv == Hq
     rows = range(B) if rows is None else [int(r) for r in _i64(rows)]
-    wvis = window_visible(q, bl)                             # [q, q]
+    wvis = window_visible(q, bl, mode)                       # [q, q]
     O = np.full((B, q, Hq, d), np.nan)
     LSE = np.full((B, Hq, q), np.nan)
     for b in rows:
@@ -164,7 +187,7 @@ def block_attention(Q, PK, PV, p_len, WK, WV, bl: int, sm_scale: float,
     return O, LSE
 
 
-def cache_attention_eq6(Q, Kc, Vc, o, bl: int, sm_scale: float):
+def cache_attention_eq6(Q, Kc, Vc, o, bl: int, sm_scale: float, mode: str = "block_causal"):
     """Attention over the whole pre-allocated cache under the Eq. (6) mask.
 
     FlowBlock review Eq. (6): the keys are the cache positions ``j`` of
@@ -176,7 +199,7 @@ def cache_attention_eq6(Q, Kc, Vc, o, bl: int, sm_scale: float):
     B, q, Hq, d = Q.shape
     C, Hkv = Kc.shape[1], Kc.shape[2]
     G = Hq // Hkv
-    M = eq6_mask(C, q, bl, o)
+    M = eq6_mask(C, q, bl, o, mode)
     O = np.empty((B, q, Hq, d))
     LSE = np.empty((B, Hq, q))
     for b in range(B):

@@ -225,3 +225,69 @@ def test_free_retire_shift_equivalence():
     Q2 = np.concatenate([Q[:, bl:], _rand(rs, B, bl, Hq, d)], axis=1)
     O_after, _ = orc.cache_attention_eq6(Q2, K2, V2, o2, bl, 0.35)
     np.testing.assert_allclose(O_after[:, :bl], O_before[:, bl:], rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# window mask modes (HERALD Sec. IV-B2 isolated groups; Flash-dLLM verify
+# views with a shared first block)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", ["isolated", "shared_first"])
+def test_mode_attention_vs_sdpa(mode):
+    rs = np.random.default_rng(31)
+    B, Hq, Hkv, d, bl, W, P = 2, 8, 2, 16, 4, 3, 9
+    q = W * bl
+    Q = _rand(rs, B, q, Hq, d)
+    PK, PV = _rand(rs, B, P, Hkv, d), _rand(rs, B, P, Hkv, d)
+    WK, WV = _rand(rs, B, q, Hkv, d), _rand(rs, B, q, Hkv, d)
+    p_len = np.array([P, 0])
+    O, _ = orc.block_attention(Q, PK, PV, p_len, WK, WV, bl, 0.3, mode=mode)
+    for b in range(B):
+        Pb = int(p_len[b])
+        keys = np.concatenate([PK[b, :Pb], WK[b]], 0)
+        vals = np.concatenate([PV[b, :Pb], WV[b]], 0)
+        mask = np.zeros((q, Pb + q), bool)
+        mask[:, :Pb] = True
+        for i in range(q):
+            g = i // bl
+            mask[i, Pb + g * bl:Pb + (g + 1) * bl] = True
+            if mode == "shared_first":
+                mask[i, Pb:Pb + bl] = True
+        np.testing.assert_allclose(O[b], _sdpa(Q[b], keys, vals, mask, 0.3), rtol=1e-12, atol=1e-12)
+
+
+def test_isolated_groups_equal_separate_forwards():
+    """HERALD's fused draft/denoise forward: each group's output equals a
+    forward of that group alone (W = 1) over the same prefix."""
+    rs = np.random.default_rng(32)
+    B, Hq, Hkv, d, bl, W, P = 2, 4, 2, 8, 8, 2, 13
+    q = W * bl
+    Q = _rand(rs, B, q, Hq, d)
+    PK, PV = _rand(rs, B, P, Hkv, d), _rand(rs, B, P, Hkv, d)
+    WK, WV = _rand(rs, B, q, Hkv, d), _rand(rs, B, q, Hkv, d)
+    p_len = np.array([P, 5])
+    O, L = orc.block_attention(Q, PK, PV, p_len, WK, WV, bl, 0.4, mode="isolated")
+    for g in range(W):
+        sl = slice(g * bl, (g + 1) * bl)
+        Og, Lg = orc.block_attention(Q[:, sl], PK, PV, p_len, WK[:, sl], WV[:, sl], bl, 0.4)
+        np.testing.assert_allclose(O[:, sl], Og, rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(L[:, :, sl], Lg, rtol=1e-13, atol=1e-14)
+
+
+def test_shared_first_views_equal_two_block_forwards():
+    """Each view block j >= 1 gives what the block-causal W = 2 forward of
+    (block 0, block j) gives for its second block; block 0 what it gives alone."""
+    rs = np.random.default_rng(33)
+    B, Hq, Hkv, d, bl, W, P = 1, 4, 1, 8, 4, 4, 6
+    q = W * bl
+    Q = _rand(rs, B, q, Hq, d)
+    PK, PV = _rand(rs, B, P, Hkv, d), _rand(rs, B, P, Hkv, d)
+    WK, WV = _rand(rs, B, q, Hkv, d), _rand(rs, B, q, Hkv, d)
+    p_len = np.array([P])
+    O, _ = orc.block_attention(Q, PK, PV, p_len, WK, WV, bl, 0.5, mode="shared_first")
+    O0, _ = orc.block_attention(Q[:, :bl], PK, PV, p_len, WK[:, :bl], WV[:, :bl], bl, 0.5)
+    np.testing.assert_allclose(O[:, :bl], O0, rtol=1e-13, atol=1e-14)
+    for j in range(1, W):
+        idx = np.r_[0:bl, j * bl:(j + 1) * bl]
+        Oj, _ = orc.block_attention(Q[:, idx], PK, PV, p_len, WK[:, idx], WV[:, idx], bl, 0.5)
+        np.testing.assert_allclose(O[:, j * bl:(j + 1) * bl], Oj[:, bl:], rtol=1e-13, atol=1e-14)

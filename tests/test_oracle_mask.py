@@ -112,3 +112,57 @@ def test_window_visible_matches_eq6_tail():
         C = q + 10
         M = orc.eq6_mask(C, q, bl, np.array([0]))[0]
         assert np.array_equal(orc.window_visible(q, bl), M[:, C - q:])
+
+
+# ---------------------------------------------------------------------------
+# the two other window masks: HERALD's isolated draft/denoise groups (Sec.
+# IV-B2) and Flash-dLLM's verify views (block 0 shared)
+# ---------------------------------------------------------------------------
+
+def _groups_by_rule(q, bl, mode):
+    """Enumerate (query group, key group) pairs in words: isolated groups see
+    only themselves; with a shared first group every group also sees group
+    0, and group 0 sees only itself."""
+    M = np.zeros((q, q), bool)
+    for i in range(q):
+        for w in range(q):
+            gi, gw = i // bl, w // bl
+            if mode == "isolated":
+                M[i, w] = gi == gw
+            else:
+                M[i, w] = gi == gw or gw == 0
+    return M
+
+
+@pytest.mark.parametrize("mode", ["isolated", "shared_first"])
+@pytest.mark.parametrize("q,bl", [(64, 32), (96, 32), (12, 4), (5, 5)])
+def test_other_window_modes_by_rule(mode, q, bl):
+    np.testing.assert_array_equal(orc.window_visible(q, bl, mode), _groups_by_rule(q, bl, mode))
+
+
+def test_other_modes_special_cases():
+    # one block: every mode is plain bidirectional attention over the block
+    for mode in orc.MASK_MODES:
+        assert orc.window_visible(32, 32, mode).all()
+    # two blocks: the shared-first views equal the block-causal mask
+    np.testing.assert_array_equal(orc.window_visible(64, 32, "shared_first"),
+                                  orc.window_visible(64, 32, "block_causal"))
+    # isolated is block-diagonal: its complement within block-causal is the strict lower blocks
+    bc, iso = orc.window_visible(96, 32, "block_causal"), orc.window_visible(96, 32, "isolated")
+    assert (iso <= bc).all() and iso.sum() == 3 * 32 * 32
+    with pytest.raises(ValueError):
+        orc.window_visible(64, 32, "causal")
+
+
+@pytest.mark.parametrize("mode", ["isolated", "shared_first"])
+def test_cache_mask_other_modes(mode):
+    """In the cache form the prefix part is unchanged and the tail carries
+    the window mode; rows [o_b, t) stay invisible."""
+    C, q, bl = 200, 96, 32
+    t = C - q
+    o = np.array([0, 40, t])
+    M = orc.eq6_mask(C, q, bl, o, mode)
+    W = _groups_by_rule(q, bl, mode)
+    for b, ob in enumerate(o):
+        assert M[b][:, :ob].all() and not M[b][:, ob:t].any()
+        np.testing.assert_array_equal(M[b][:, t:], W)
