@@ -477,7 +477,7 @@ def main():
                       "mb": round(work["scatter_bytes"] / 1e6, 2)}
 
     traffic = traffic_for_attention()
-    roof = {"bound": "mfma", "kernel": "attn_mfma_kernel<8, 4> (dense and sparse rows, one launch)",
+    roof = {"bound": "mfma", "kernel": "attn_mfma_kernel<8, 4, false> (dense and sparse rows, one launch)",
             "achieved": round(tf_a, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tf_a / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
             "algorithmic_bytes": attn_bytes,

@@ -73,6 +73,23 @@ typedef enum {
   BD_REP_ROW = 1   /* one query row (HERALD's block-centre [MASK] query) */
 } bd_rep_mode;
 
+/* Window part of the attention mask.  The window holds q / bl blocks
+ * (groups) of bl queries and their keys; prefix keys are always visible.
+ * Query i (group floor(i/bl)) sees window key w (group floor(w/bl)) when
+ *   BD_MASK_BLOCK_CAUSAL  group(w) <= group(i)      FlowBlock review Eq. (6)
+ *   BD_MASK_ISOLATED      group(w) == group(i)      HERALD Sec. IV-B2: the
+ *                         denoising and draft groups of one forward see the
+ *                         prefix but not each other
+ *   BD_MASK_SHARED_FIRST  group(w) == group(i) or group(w) == 0
+ *                         Flash-dLLM's verify pass: block 0 holds the
+ *                         tracked context, later blocks are views that see
+ *                         it but not each other, and it sees none of them */
+typedef enum {
+  BD_MASK_BLOCK_CAUSAL = 0,
+  BD_MASK_ISOLATED = 1,
+  BD_MASK_SHARED_FIRST = 2
+} bd_mask_mode;
+
 /* Library version string, e.g. "libbdattn 0.1.0 gfx950". */
 const char *bd_version(void);
 
@@ -242,6 +259,24 @@ int bd_attn_packed(int dtype, int B, int Hq, int Hkv, int d, int q, int bl,
                    void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * bd_attn_packed_masked: bd_attn_packed with the window mask chosen by
+ * mask_mode (bd_mask_mode): BD_MASK_BLOCK_CAUSAL is bd_attn_packed;
+ * BD_MASK_ISOLATED is HERALD's fused draft/denoise forward (Sec. IV-B2);
+ * BD_MASK_SHARED_FIRST is Flash-dLLM's verify views.  Every query still sees
+ * its whole prefix and its own block.  Other arguments, layouts and errors as
+ * bd_attn_packed; an unknown mode returns BD_ERR_INVALID_ARG.
+ */
+int bd_attn_packed_masked(int dtype, int B, int Hq, int Hkv, int d, int q,
+                          int bl, int mask_mode,
+                          const int32_t *row_ids, int n_rows, const void *q_ptr,
+                          const int64_t q_strides[3], const void *pk, const void *pv,
+                          const int64_t p_strides[3], int p_cap,
+                          const int32_t *p_len, int p_max, const void *wk,
+                          const void *wv, const int64_t w_strides[3], float sm_scale,
+                          void *out, const int64_t out_strides[3], float *lse,
+                          void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * bd_attn_packed_dual: bd_attn_packed over two row lists in one launch,
  * each list with its own prefix source.  The rows of list a attend over
  * pk_a/pv_a with lengths p_len_a, the rows of list b over pk_b/pv_b with
@@ -285,12 +320,14 @@ int bd_attn_packed_dual(int dtype, int B, int Hq, int Hkv, int d, int q,
  * bd_mask_materialize: test hook for the attention mask.  Writes
  * out[b, i, j] = 1 if query i of row b sees cache position j under
  * FlowBlock review Eq. (6) (j < o_b, or t <= j < t + (floor(i/bl)+1)*bl
- * with t = C - q), else 0, for j < C.  out is device uint8 [B, q, C],
- * contiguous.  It evaluates the same device predicate the attention kernels
- * use.  Rows with o_b outside [0, t] are written all 0xFF.
+ * with t = C - q; with another bd_mask_mode the tail part follows that
+ * mode), else 0, for j < C.  out is device uint8 [B, q, C], contiguous.  It
+ * evaluates the same device predicate the attention kernels use.  Rows with
+ * o_b outside [0, t] are written all 0xFF.  Unknown modes return
+ * BD_ERR_INVALID_ARG.
  */
-int bd_mask_materialize(int B, int C, int q, int bl, const int32_t *o,
-                        uint8_t *out, void *stream);
+int bd_mask_materialize(int B, int C, int q, int bl, int mask_mode,
+                        const int32_t *o, uint8_t *out, void *stream);
 
 #ifdef __cplusplus
 }

@@ -20,6 +20,9 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "bdattn.h")
 BD_OK, BD_ERR_INVALID_ARG, BD_ERR_UNSUPPORTED, BD_ERR_HIP, BD_ERR_WORKSPACE = 0, 1, 2, 3, 4
 BD_BF16, BD_F32 = 0, 1
 BD_REP_MEAN, BD_REP_ROW = 0, 1
+BD_MASK_BLOCK_CAUSAL, BD_MASK_ISOLATED, BD_MASK_SHARED_FIRST = 0, 1, 2
+MASK_MODES = {"block_causal": BD_MASK_BLOCK_CAUSAL, "isolated": BD_MASK_ISOLATED,
+              "shared_first": BD_MASK_SHARED_FIRST}
 
 _DTYPE = {torch.bfloat16: BD_BF16, torch.float32: BD_F32}
 
@@ -50,7 +53,10 @@ _SIGS = {
                                  _vp, _i, _vp, _vp, _vp, _i, _vp, _i,
                                  _vp, _i, _vp, _vp, _vp, _i, _vp, _i,
                                  _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _sz, _vp]),
-    "bd_mask_materialize": (_i, [_i, _i, _i, _i, _vp, _vp, _vp]),
+    "bd_attn_packed_masked": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _vp, _i, _vp, _vp, _vp, _vp,
+                                   _vp, _i, _vp, _i, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp,
+                                   _vp, _sz, _vp]),
+    "bd_mask_materialize": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp]),
 }
 
 _lib = None
@@ -225,8 +231,9 @@ def attn_workspace_size(dtype, B, Hq, Hkv, d, q, n_rows, p_max) -> int:
 
 
 def attn_packed(q, pk, pv, p_len, p_max: int, wk, wv, bl: int, sm_scale: float, out=None,
-                lse=None, row_ids=None, ws=None):
-    """Packed block-diffusion attention; returns out [B, q, Hq, d]."""
+                lse=None, row_ids=None, ws=None, mask_mode: str = "block_causal"):
+    """Packed block-diffusion attention; returns out [B, q, Hq, d].  Any
+    ``mask_mode`` other than "block_causal" calls bd_attn_packed_masked."""
     q = _dev(q, "q")
     pk, pv, wk, wv = (_dev(x, n) for x, n in ((pk, "pk"), (pv, "pv"), (wk, "wk"), (wv, "wv")))
     if pv.stride() != pk.stride() or wv.stride() != wk.stride():
@@ -243,11 +250,15 @@ def attn_packed(q, pk, pv, p_len, p_max: int, wk, wv, bl: int, sm_scale: float, 
         ws = workspace(need, q.device)
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
         raise ValueError("lse must be contiguous float32 [B, Hq, q]")
-    _check(lib().bd_attn_packed(_DTYPE[q.dtype], B, Hq, Hkv, d, nqry, bl, _ptr(rid), n_rows,
-                                _ptr(q), _strides(q, 3), _ptr(pk), _ptr(pv), _strides(pk, 3),
-                                pk.shape[1], _ptr(p_len), p_max, _ptr(wk), _ptr(wv),
-                                _strides(wk, 3), float(sm_scale), _ptr(out), _strides(out, 3),
-                                _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(), _stream()))
+    tail = (_ptr(rid), n_rows, _ptr(q), _strides(q, 3), _ptr(pk), _ptr(pv), _strides(pk, 3),
+            pk.shape[1], _ptr(p_len), p_max, _ptr(wk), _ptr(wv), _strides(wk, 3),
+            float(sm_scale), _ptr(out), _strides(out, 3), _ptr(lse), _ptr(ws),
+            0 if ws is None else ws.numel(), _stream())
+    if mask_mode == "block_causal":
+        _check(lib().bd_attn_packed(_DTYPE[q.dtype], B, Hq, Hkv, d, nqry, bl, *tail))
+    else:
+        _check(lib().bd_attn_packed_masked(_DTYPE[q.dtype], B, Hq, Hkv, d, nqry, bl,
+                                           MASK_MODES[mask_mode], *tail))
     return out
 
 
@@ -292,8 +303,9 @@ def attn_packed_dual(q, src_a, src_b, wk, wv, bl: int, sm_scale: float, out=None
     return out
 
 
-def mask_materialize(B: int, C: int, q: int, bl: int, o):
+def mask_materialize(B: int, C: int, q: int, bl: int, o, mask_mode: str = "block_causal"):
     o = _i32(o, "o")
     out = torch.empty((B, q, C), dtype=torch.uint8, device=o.device)
-    _check(lib().bd_mask_materialize(B, C, q, bl, _ptr(o), _ptr(out), _stream()))
+    _check(lib().bd_mask_materialize(B, C, q, bl, MASK_MODES[mask_mode], _ptr(o), _ptr(out),
+                                     _stream()))
     return out

@@ -239,7 +239,7 @@ struct PrefixArg {
 
 // Shared body of bd_attn_packed (one source) and bd_attn_packed_dual (two).
 int attn_entry(const char *fn, int dtype, int B, int Hq, int Hkv, int d, int q, int bl,
-               const void *q_ptr, const int64_t q_strides[3], const PrefixArg &pa,
+               int mask_mode, const void *q_ptr, const int64_t q_strides[3], const PrefixArg &pa,
                const PrefixArg *pb, const void *wk, const void *wv, const int64_t w_strides[3],
                float sm_scale, void *out, const int64_t out_strides[3], float *lse,
                void *workspace, size_t ws_bytes, void *stream) {
@@ -253,6 +253,8 @@ int attn_entry(const char *fn, int dtype, int B, int Hq, int Hkv, int d, int q, 
       return fail(BD_ERR_INVALID_ARG, "%s: negative row count, capacity or p_max", fn);
   }
   if (Hq % Hkv != 0) return fail(BD_ERR_INVALID_ARG, "%s: Hq %% Hkv != 0", fn);
+  if (mask_mode != BD_MASK_BLOCK_CAUSAL && mask_mode != BD_MASK_ISOLATED && mask_mode != BD_MASK_SHARED_FIRST)
+    return fail(BD_ERR_INVALID_ARG, "%s: unknown mask mode %d", fn, mask_mode);
   if (!pb && !pa.rows && pa.n != B)
     return fail(BD_ERR_INVALID_ARG, "%s: n_rows must equal B when row_ids is NULL", fn);
   if (pb && ((pa.n > 0 && !pa.rows) || (pb->n > 0 && !pb->rows)))
@@ -286,6 +288,7 @@ int attn_entry(const char *fn, int dtype, int B, int Hq, int Hkv, int d, int q, 
     return fail(BD_ERR_INVALID_ARG, "%s: key row strides above 32 MB are not supported", fn);
   AttnArgs a;
   a.dtype = dtype; a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.d = d; a.q = q; a.bl = bl;
+  a.mask_mode = mask_mode;
   a.n_rows = n_rows;
   a.Q = q_ptr; a.wk = wk; a.wv = wv; a.out = out; a.lse = lse;
   memcpy(a.qs, q_strides, sizeof(a.qs));
@@ -336,8 +339,22 @@ int bd_attn_packed(int dtype, int B, int Hq, int Hkv, int d, int q, int bl, cons
                    float sm_scale, void *out, const int64_t out_strides[3], float *lse,
                    void *workspace, size_t ws_bytes, void *stream) {
   const PrefixArg pa{row_ids, n_rows, pk, pv, p_strides, p_cap, p_len, p_max};
-  return attn_entry("bd_attn_packed", dtype, B, Hq, Hkv, d, q, bl, q_ptr, q_strides, pa, nullptr, wk,
-                    wv, w_strides, sm_scale, out, out_strides, lse, workspace, ws_bytes, stream);
+  return attn_entry("bd_attn_packed", dtype, B, Hq, Hkv, d, q, bl, BD_MASK_BLOCK_CAUSAL, q_ptr,
+                    q_strides, pa, nullptr, wk, wv, w_strides, sm_scale, out, out_strides, lse,
+                    workspace, ws_bytes, stream);
+}
+
+int bd_attn_packed_masked(int dtype, int B, int Hq, int Hkv, int d, int q, int bl, int mask_mode,
+                          const int32_t *row_ids, int n_rows, const void *q_ptr,
+                          const int64_t q_strides[3], const void *pk, const void *pv,
+                          const int64_t p_strides[3], int p_cap, const int32_t *p_len, int p_max,
+                          const void *wk, const void *wv, const int64_t w_strides[3],
+                          float sm_scale, void *out, const int64_t out_strides[3], float *lse,
+                          void *workspace, size_t ws_bytes, void *stream) {
+  const PrefixArg pa{row_ids, n_rows, pk, pv, p_strides, p_cap, p_len, p_max};
+  return attn_entry("bd_attn_packed_masked", dtype, B, Hq, Hkv, d, q, bl, mask_mode, q_ptr,
+                    q_strides, pa, nullptr, wk, wv, w_strides, sm_scale, out, out_strides, lse,
+                    workspace, ws_bytes, stream);
 }
 
 int bd_attn_packed_dual(int dtype, int B, int Hq, int Hkv, int d, int q, int bl, const void *q_ptr,
@@ -351,18 +368,21 @@ int bd_attn_packed_dual(int dtype, int B, int Hq, int Hkv, int d, int q, int bl,
                         void *stream) {
   const PrefixArg pa{rows_a, n_a, pk_a, pv_a, pa_strides, pa_cap, p_len_a, p_max_a};
   const PrefixArg pb{rows_b, n_b, pk_b, pv_b, pb_strides, pb_cap, p_len_b, p_max_b};
-  return attn_entry("bd_attn_packed_dual", dtype, B, Hq, Hkv, d, q, bl, q_ptr, q_strides, pa, &pb,
+  return attn_entry("bd_attn_packed_dual", dtype, B, Hq, Hkv, d, q, bl, BD_MASK_BLOCK_CAUSAL, q_ptr, q_strides, pa, &pb,
                     wk, wv, w_strides, sm_scale, out, out_strides, lse, workspace, ws_bytes, stream);
 }
 
-int bd_mask_materialize(int B, int C, int q, int bl, const int32_t *o, uint8_t *out, void *stream) {
+int bd_mask_materialize(int B, int C, int q, int bl, int mask_mode, const int32_t *o, uint8_t *out,
+                        void *stream) {
   g_err[0] = 0;
   if (B < 0 || C < 0 || q < 0 || bl <= 0 || q > C)
     return fail(BD_ERR_INVALID_ARG, "bd_mask_materialize: bad sizes");
+  if (mask_mode != BD_MASK_BLOCK_CAUSAL && mask_mode != BD_MASK_ISOLATED && mask_mode != BD_MASK_SHARED_FIRST)
+    return fail(BD_ERR_INVALID_ARG, "bd_mask_materialize: unknown mask mode %d", mask_mode);
   if (B == 0 || C == 0 || q == 0) return BD_OK;
   if (!o || !out) return fail(BD_ERR_INVALID_ARG, "bd_mask_materialize: null pointer");
   if (B > 65535 || q > 65535) return fail(BD_ERR_INVALID_ARG, "bd_mask_materialize: too large");
-  return hip_status(launch_mask(B, C, q, bl, o, out, (hipStream_t)stream), "bd_mask_materialize launch");
+  return hip_status(launch_mask(B, C, q, bl, mask_mode, o, out, (hipStream_t)stream), "bd_mask_materialize launch");
 }
 
 }  // extern "C"

@@ -150,7 +150,9 @@ __device__ inline bool decode_item(const AttnArgs &a, int bid, Item &it) {
   return true;
 }
 
-template <int NW, int G>
+// WM: a window mask other than block-causal (a.mask_mode); a separate
+// instance, so the block-causal kernel carries none of its code.
+template <int NW, int G, bool WM>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) {
   using S = Shape<NW, G>;
   __shared__ __attribute__((aligned(16))) bf16 Ks[2][kKTile];
@@ -178,6 +180,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
   const int qi = i0 + qb * 32 + ln;
   const bool qok = qi < a.q;
   const int lim = window_limit(qok ? qi : ilast, a.bl, a.q);
+  // other window masks: window keys in [w_shared, w_floor) are not visible
+  const int w_floor = WM ? window_floor(qok ? qi : ilast, a.bl, a.mask_mode) : 0;
+  const int w_shared = WM ? window_shared(a.bl, a.mask_mode) : 0;
 
   // ---- Q operands (B of S^T = K Q^T): lane holds Q[qi][ks*16 + hh*8 .. +8]
   bf16x8 qop[kD / 16];
@@ -334,6 +339,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (kt * 32 + (r >> 2) * 8 + (r & 3) >= thr) s[kt][r] = -INFINITY;
+      if (WM && win) {
+        const int lo_t = w_floor - base - hh * 4, sh_t = w_shared - base - hh * 4;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kk = kt * 32 + (r >> 2) * 8 + (r & 3);
+            if (kk < lo_t && kk >= sh_t) s[kt][r] = -INFINITY;
+          }
+      }
     }
     // column max of the tile; the reference max is raised only when the
     // tile's max exceeds it by more than 2^8
@@ -579,6 +594,8 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a) {
   const int ilast = min(u * kQT + kQT, a.q) - 1;
   const int win_len = window_limit(ilast, a.bl, a.q);
   const int lim_i = window_limit(q_ok ? qi : ilast, a.bl, a.q);
+  const int w_floor = window_floor(q_ok ? qi : ilast, a.bl, a.mask_mode);
+  const int w_shared = window_shared(a.bl, a.mask_mode);
 
   float qv[DL], o[DL];
   const T *qp = reinterpret_cast<const T *>(a.Q) + (int64_t)b * a.qs[0] + (int64_t)qi * a.qs[1] +
@@ -649,6 +666,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a) {
       dot += __shfl_xor(dot, 2);
       dot += __shfl_xor(dot, 4);
       if (base + key >= vlim) continue;  // uniform over the 8 lanes of a query
+      if (win && base + key < w_floor && base + key >= w_shared) continue;
       const float sc = dot * a.scale2;
       const float m_new = fmaxf(m_run, sc);
       const float alpha = exp2f(m_run - m_new);
@@ -736,6 +754,7 @@ AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int d, int q, int n_rows, 
 
 template <int NW, int G>
 static hipError_t launch_mfma(const AttnArgs &a, hipStream_t s) {
+  const bool wm = a.mask_mode != BD_MASK_BLOCK_CAUSAL;
   using S = Shape<NW, G>;
   const int64_t n_groups = (int64_t)a.n_rows * a.Hkv;
   const int64_t per_group = (int64_t)a.nqt * a.n_split;
@@ -745,7 +764,10 @@ static hipError_t launch_mfma(const AttnArgs &a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((attn_mfma_kernel<NW, G>), dim3((unsigned)grid), dim3(S::NT), 0, s, a);
+  if (wm)
+    hipLaunchKernelGGL((attn_mfma_kernel<NW, G, true>), dim3((unsigned)grid), dim3(S::NT), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_mfma_kernel<NW, G, false>), dim3((unsigned)grid), dim3(S::NT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split <= 1) return e;
   const int64_t cgrid = n_groups * a.nqt * (S::NCOL / 8);

@@ -33,9 +33,24 @@ __host__ __device__ inline int window_limit(int i, int bl, int q) {
   return lim < q ? lim : q;
 }
 
-__host__ __device__ inline bool cache_visible(int i, int j, int ob, int t, int bl, int q) {
+// Other window masks (bd_mask_mode): query i sees window key w when
+// w < window_limit(i) and (w < window_shared or w >= window_floor(i)): the
+// block-causal mask has floor 0; isolated groups start at their own block;
+// a shared first block stays visible to every group.
+__host__ __device__ inline int window_floor(int i, int bl, int mode) {
+  return mode == BD_MASK_BLOCK_CAUSAL ? 0 : (i / bl) * bl;
+}
+__host__ __device__ inline int window_shared(int bl, int mode) {
+  return mode == BD_MASK_SHARED_FIRST ? bl : 0;
+}
+
+__host__ __device__ inline bool window_visible(int i, int w, int bl, int q, int mode) {
+  return w < window_limit(i, bl, q) && (w < window_shared(bl, mode) || w >= window_floor(i, bl, mode));
+}
+
+__host__ __device__ inline bool cache_visible(int i, int j, int ob, int t, int bl, int q, int mode) {
   if (j < ob) return true;
-  return j >= t && (j - t) < window_limit(i, bl, q);
+  return j >= t && window_visible(i, j - t, bl, q, mode);
 }
 
 __host__ __device__ inline int clampi(int v, int lo, int hi) {
@@ -77,12 +92,13 @@ struct GatherArgs {
 };
 hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
 
-hipError_t launch_mask(int B, int C, int q, int bl, const int32_t *o, uint8_t *out,
+hipError_t launch_mask(int B, int C, int q, int bl, int mode, const int32_t *o, uint8_t *out,
                        hipStream_t s);
 
 struct AttnArgs {
   int dtype;  // BD_BF16 / BD_F32
   int B, Hq, Hkv, G, d, q, bl, n_rows, p_cap, p_max;
+  int mask_mode;  // bd_mask_mode of the window part
   const void *Q;
   int64_t qs[3];
   const void *pk, *pv;

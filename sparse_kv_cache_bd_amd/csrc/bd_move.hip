@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs a, int vpr)
   }
 }
 
-__global__ __launch_bounds__(kThreads) void mask_kernel(int B, int C, int q, int bl,
+__global__ __launch_bounds__(kThreads) void mask_kernel(int B, int C, int q, int bl, int mode,
                                                         const int32_t *o, uint8_t *out) {
   const int b = blockIdx.z;
   const int i = blockIdx.y;
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void mask_kernel(int B, int C, int q, int
   if (ob < 0 || ob > t)
     v = 0xFF;
   else
-    v = cache_visible(i, j, ob, t, bl, q) ? 1 : 0;
+    v = cache_visible(i, j, ob, t, bl, q, mode) ? 1 : 0;
   out[((int64_t)b * q + i) * C + j] = v;
 }
 
@@ -140,10 +140,10 @@ hipError_t launch_gather(const GatherArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_mask(int B, int C, int q, int bl, const int32_t *o, uint8_t *out,
+hipError_t launch_mask(int B, int C, int q, int bl, int mode, const int32_t *o, uint8_t *out,
                        hipStream_t s) {
   dim3 grid((unsigned)cdiv(C, kThreads), (unsigned)q, (unsigned)B);
-  hipLaunchKernelGGL(mask_kernel, grid, dim3(kThreads), 0, s, B, C, q, bl, o, out);
+  hipLaunchKernelGGL(mask_kernel, grid, dim3(kThreads), 0, s, B, C, q, bl, mode, o, out);
   return hipGetLastError();
 }
 

@@ -24,7 +24,7 @@ def L():
 
 def test_exports_every_header_function(L):
     names = bd.header_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(L, n), n
 
@@ -214,6 +214,31 @@ def test_attn_validation(L, kw, code):
     assert _attn(L, **kw) == code
 
 
+def _attn_masked(L, mode, **kw):
+    a = dict(dtype=bd.BD_BF16, B=2, Hq=32, Hkv=8, d=128, q=64, bl=32, rid=None, n_rows=2,
+             Q=FAKE, qs=I3(64 * 4096, 4096, 128), pk=FAKE, pv=FAKE2, ps=I3(1 << 22, 1024, 128),
+             pcap=4096, plen=FAKE, pmax=4000, wk=FAKE, wv=FAKE2, wsd=I3(1 << 22, 1024, 128),
+             scale=0.088, out=FAKE2, os=I3(64 * 4096, 4096, 128), lse=None, ws=FAKE)
+    a.update(kw)
+    need = bd.attn_workspace_size(a["dtype"], a["B"], a["Hq"], a["Hkv"], a["d"], a["q"],
+                                  a["n_rows"], a["pmax"])
+    return L.bd_attn_packed_masked(a["dtype"], a["B"], a["Hq"], a["Hkv"], a["d"], a["q"], a["bl"],
+                                   mode, a["rid"], a["n_rows"], a["Q"], a["qs"], a["pk"], a["pv"],
+                                   a["ps"], a["pcap"], a["plen"], a["pmax"], a["wk"], a["wv"],
+                                   a["wsd"], a["scale"], a["out"], a["os"], a["lse"], a["ws"], need,
+                                   None)
+
+
+def test_attn_masked_validation(L):
+    for mode in (-1, 3, 99):
+        assert _attn_masked(L, mode) == bd.BD_ERR_INVALID_ARG
+        assert "mask mode" in bd.last_error()
+    # the other checks are those of bd_attn_packed
+    assert _attn_masked(L, bd.BD_MASK_ISOLATED, Hq=30) == bd.BD_ERR_INVALID_ARG
+    assert _attn_masked(L, bd.BD_MASK_SHARED_FIRST, Q=MISALIGNED) == bd.BD_ERR_INVALID_ARG
+    assert _attn_masked(L, bd.BD_MASK_ISOLATED, B=0, n_rows=0) == bd.BD_OK
+
+
 def test_attn_empty_is_ok(L):
     assert _attn(L, B=0, n_rows=0) == bd.BD_OK
     assert _attn(L, q=0) == bd.BD_OK
@@ -268,7 +293,8 @@ def test_attn_dual_empty_and_one_list(L):
 
 
 def test_mask_validation(L):
-    assert L.bd_mask_materialize(2, 100, 200, 32, FAKE, FAKE2, None) == bd.BD_ERR_INVALID_ARG
-    assert L.bd_mask_materialize(2, 100, 64, 0, FAKE, FAKE2, None) == bd.BD_ERR_INVALID_ARG
-    assert L.bd_mask_materialize(2, 100, 64, 32, None, FAKE2, None) == bd.BD_ERR_INVALID_ARG
-    assert L.bd_mask_materialize(0, 100, 64, 32, None, None, None) == bd.BD_OK
+    assert L.bd_mask_materialize(2, 100, 200, 32, 0, FAKE, FAKE2, None) == bd.BD_ERR_INVALID_ARG
+    assert L.bd_mask_materialize(2, 100, 64, 0, 0, FAKE, FAKE2, None) == bd.BD_ERR_INVALID_ARG
+    assert L.bd_mask_materialize(2, 100, 64, 32, 0, None, FAKE2, None) == bd.BD_ERR_INVALID_ARG
+    assert L.bd_mask_materialize(2, 100, 64, 32, 3, FAKE, FAKE2, None) == bd.BD_ERR_INVALID_ARG
+    assert L.bd_mask_materialize(0, 100, 64, 32, 0, None, None, None) == bd.BD_OK
