@@ -49,6 +49,8 @@ __all__ = [
     "topk_select",
     "gather",
     "kv_scatter",
+    "rope",
+    "qkv_rope",
 ]
 
 
@@ -394,3 +396,52 @@ def kv_scatter(present, data, o, t: int, q: int, rows=None):
         ob = int(o[b])
         data[:, b, ob:ob + q] = src[:, b]
     return data
+
+
+# ---------------------------------------------------------------------------
+# Fused producer: QKV projection, rotary embedding, cache write
+# ---------------------------------------------------------------------------
+
+def rope(x, pos, base: float = 10000.0):
+    """Rotary positional embedding of head vectors at absolute positions.
+
+    HERALD Eq. (1) writes the rotation R_{theta,p} applied to a query or key
+    at position p; FlowBlock's packed windows use absolute positions.  The
+    pages fix neither the frequencies nor the pairing; the reading is the
+    usual one: dimension j < d/2 pairs with j + d/2 and turns by the angle
+    ``p * base**(-2j/d)``.  x: ``[..., n, d]`` with ``pos`` ``[n]``.
+    """
+    x = _f64(x)
+    d = x.shape[-1]
+    h = d // 2
+    ang = np.asarray(pos, dtype=np.float64)[:, None] * base ** (-2.0 * np.arange(h) / d)[None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = x[..., :h], x[..., h:]
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+
+
+def qkv_rope(X, Wqkv, rope_pos, Hq: int, Hkv: int, base: float = 10000.0):
+    """Flash-dLLM's fused cache producer (Flash-Cache): the projection of the
+    window's hidden states, RoPE on queries and keys, and the keys and values
+    that the cache write stores.
+
+    X: ``[B, q, Dm]``; Wqkv: ``[(Hq + 2*Hkv) * d, Dm]`` (rows: the query heads,
+    then the key heads, then the value heads); window token ``i`` of row ``b``
+    sits at absolute position ``rope_pos[b] + i``.  Returns Q ``[B, q, Hq, d]``,
+    K and V ``[B, q, Hkv, d]`` in float64.
+    """
+    X = _f64(X)
+    W = _f64(Wqkv)
+    rope_pos = _i64(rope_pos)
+    B, q, Dm = X.shape
+    d = W.shape[0] // (Hq + 2 * Hkv)
+    Q = np.empty((B, q, Hq, d))
+    K = np.empty((B, q, Hkv, d))
+    V = np.empty((B, q, Hkv, d))
+    for b in range(B):
+        Y = (X[b] @ W.T).reshape(q, Hq + 2 * Hkv, d)          # [q, heads, d]
+        pos = int(rope_pos[b]) + np.arange(q)
+        Q[b] = np.stack([rope(Y[:, hq], pos, base) for hq in range(Hq)], axis=1)
+        K[b] = np.stack([rope(Y[:, Hq + h], pos, base) for h in range(Hkv)], axis=1)
+        V[b] = Y[:, Hq + Hkv:]
+    return Q, K, V
