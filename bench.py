@@ -233,6 +233,34 @@ def select_multi_sweep(bd, wl, Kc, s_len, k_sel, sel_bytes, ms_rep, dev, reps):
     return res
 
 
+def bench_producer(bd, dev, reps):
+    """Flash-dLLM's fused cache producer (QKV projection + RoPE + cache write)
+    at the serving-mix shape: 64 rows x 128 window tokens, hidden 4096 (32
+    query heads x 128), 32/8 heads; keys and values written at the window
+    tail of a [64, 16640, 8, 128] cache.  Synthetic N(0,1) hidden states and
+    N(0,1)/sqrt(4096) weights."""
+    import torch
+    B, q, Dm, Hq, Hkv, d, C = 64, 128, 4096, 32, 8, 128, 16640
+    g = torch.Generator(device=dev).manual_seed(0)
+    X = torch.randn((B, q, Dm), generator=g, device=dev).bfloat16()
+    W = (torch.randn(((Hq + 2 * Hkv) * d, Dm), generator=g, device=dev) / math.sqrt(Dm)).bfloat16()
+    Kc = torch.zeros((B, C, Hkv, d), dtype=torch.bfloat16, device=dev)
+    Vc = torch.zeros_like(Kc)
+    Qo = torch.empty((B, q, Hq, d), dtype=torch.bfloat16, device=dev)
+    rope_pos = torch.randint(1024, 16384, (B,), generator=g, device=dev).to(torch.int32)
+    dst = torch.full((B,), C - q, dtype=torch.int32, device=dev)
+    ms = time_calls(lambda: bd.qkv_rope_write(X, W, rope_pos, Hq, Hkv, Qo, Kc, Vc, dst), reps)
+    flop = 2 * B * q * Dm * (Hq + 2 * Hkv) * d
+    nbytes = (B * q * Dm + (Hq + 2 * Hkv) * d * Dm + B * q * (Hq + 2 * Hkv) * d) * 2
+    res = {"tokens": B * q, "hidden": Dm, "heads": [Hq, Hkv], "us": round(ms * 1e3, 2),
+           "TFLOP/s": _rate(flop, ms, 1e12),
+           "frac_mfma_peak": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "gflop": round(flop / 1e9, 1), "min_mb": round(nbytes / 1e6, 1)}
+    del X, W, Kc, Vc, Qo
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_configs(dev, reps: int = 10):
     """The other synthetic workloads, each in the launch configuration its
     parity test checks: per-operation times and rates, warm (back-to-back
@@ -348,6 +376,7 @@ def bench_configs(dev, reps: int = 10):
             out[name]["select_multi_sweep"] = sweep
         del Kc, Vc, pool_k, pool_v, ws, ws_a
         torch.cuda.empty_cache()
+    out["producer_serving_mix"] = bench_producer(bd, dev, reps)
     del flush
     torch.cuda.empty_cache()
     return out

@@ -17,6 +17,9 @@
  *   bd_kv_scatter   write-back of the window's KV to its absolute positions
  *                   (FlowBlock review, Eq. (7) = paper Eq. 6).
  *
+ * bd_qkv_rope_write produces the window's queries, keys and values from its
+ * hidden states (projection + RoPE + cache write in one kernel).
+ *
  * bd_attn_packed_dual runs bd_attn_packed for two row lists with different
  * prefix sources (cache rows and pool rows) in one launch.  bd_select_multi
  * is the exact selection in which every block query ranks the prefix (the
@@ -315,6 +318,43 @@ int bd_attn_packed_dual(int dtype, int B, int Hq, int Hkv, int d, int q,
                         const int64_t w_strides[3], float sm_scale, void *out,
                         const int64_t out_strides[3], float *lse,
                         void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * bd_qkv_rope_write: Flash-dLLM's fused cache producer (Flash-Cache): the
+ * projection of the window's hidden states onto the query, key and value
+ * heads, the rotary embedding of queries and keys at absolute positions
+ * (HERALD Eq. (1); FlowBlock's packed windows use absolute-position RoPE),
+ * and the write of keys and values into the cache, with no intermediate
+ * tensor in memory.
+ *
+ * For row b < B, window token i < q (absolute position
+ * p = rope_pos[b] + i) and head n < Hq + 2*Hkv (the Hq query heads, then the
+ * Hkv key heads, then the Hkv value heads):
+ *   y[n, :] = sum_e x[b, i, e] * w[n*d + :, e]          (fp32 accumulation)
+ *   query and key heads: y[j], y[j + d/2] (j < d/2) rotate by the angle
+ *   p * rope_base^(-2j/d):  y'[j] = y[j] cos - y[j+d/2] sin,
+ *                           y'[j+d/2] = y[j+d/2] cos + y[j] sin
+ *   q_out[b, i, n]                 = y'  (query heads)
+ *   k_cache[b, dst_pos[b] + i, n-Hq] = y'  (key heads)
+ *   v_cache[b, dst_pos[b] + i, n-Hq-Hkv] = y  (value heads)
+ * all rounded once to bf16.  dst_pos[b] = C - q writes the window tail that
+ * bd_attn_packed reads; dst_pos[b] = o_b writes straight to the Eq. (7)
+ * position.  Cache positions outside [0, c_cap) are not written.
+ *
+ *   x         [B, q, Dm] bf16, strides x_strides {row, token}; Dm contiguous.
+ *   w         [(Hq + 2*Hkv) * d, Dm] bf16, contiguous (a linear layer's weight).
+ *   rope_pos, dst_pos  device int32 [B].
+ *   q_out     [B, q, Hq, d] bf16, strides q_strides.
+ *   k_cache, v_cache   [B, c_cap, Hkv, d] bf16, shared strides c_strides.
+ *
+ * Built for dtype BD_BF16 with d == 128 and Dm a multiple of 32.
+ */
+int bd_qkv_rope_write(int dtype, int B, int q, int Dm, int Hq, int Hkv, int d,
+                      const void *x, const int64_t x_strides[2], const void *w,
+                      const int32_t *rope_pos, float rope_base, void *q_out,
+                      const int64_t q_strides[3], void *k_cache, void *v_cache,
+                      const int64_t c_strides[3], int c_cap,
+                      const int32_t *dst_pos, void *stream);
 
 /*
  * bd_mask_materialize: test hook for the attention mask.  Writes

@@ -26,6 +26,7 @@ MASK_MODES = {"block_causal": BD_MASK_BLOCK_CAUSAL, "isolated": BD_MASK_ISOLATED
 
 _DTYPE = {torch.bfloat16: BD_BF16, torch.float32: BD_F32}
 
+_c_i64_2 = ctypes.c_int64 * 2
 _c_i64_3 = ctypes.c_int64 * 3
 _c_i64_4 = ctypes.c_int64 * 4
 _vp = ctypes.c_void_p
@@ -57,6 +58,8 @@ _SIGS = {
                                    _vp, _i, _vp, _i, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp,
                                    _vp, _sz, _vp]),
     "bd_mask_materialize": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp]),
+    "bd_qkv_rope_write": (_i, [_i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, ctypes.c_float,
+                               _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp]),
 }
 
 _lib = None
@@ -125,7 +128,7 @@ def _strides(t: torch.Tensor, n: int):
         raise ValueError("the head dimension must be contiguous")
     st = list(t.stride()[:-1])
     assert len(st) == n, (t.shape, n)
-    return (_c_i64_3 if n == 3 else _c_i64_4)(*st)
+    return {2: _c_i64_2, 3: _c_i64_3, 4: _c_i64_4}[n](*st)
 
 
 def _i32(t, name):
@@ -301,6 +304,27 @@ def attn_packed_dual(q, src_a, src_b, wk, wv, bl: int, sm_scale: float, out=None
         _ptr(wk), _ptr(wv), _strides(wk, 3), float(sm_scale), _ptr(out), _strides(out, 3),
         _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(), _stream()))
     return out
+
+
+def qkv_rope_write(x, w, rope_pos, Hq: int, Hkv: int, q_out, k_cache, v_cache, dst_pos,
+                   rope_base: float = 10000.0):
+    """Fused QKV projection + RoPE + cache write.  x [B, q, Dm]; w
+    [(Hq + 2 Hkv) * d, Dm]; q_out [B, q, Hq, d]; k_cache / v_cache
+    [B, C, Hkv, d] (shared strides).  Returns q_out."""
+    x, w = _dev(x, "x"), _dev(w, "w")
+    q_out, k_cache, v_cache = _dev(q_out, "q_out"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache")
+    if k_cache.stride() != v_cache.stride():
+        raise ValueError("k_cache and v_cache must share strides")
+    if not w.is_contiguous():
+        raise ValueError("w must be contiguous")
+    B, nq, Dm = x.shape
+    d = q_out.shape[3]
+    rope_pos, dst_pos = _i32(rope_pos, "rope_pos"), _i32(dst_pos, "dst_pos")
+    _check(lib().bd_qkv_rope_write(_DTYPE[x.dtype], B, nq, Dm, Hq, Hkv, d, _ptr(x), _strides(x, 2),
+                                   _ptr(w), _ptr(rope_pos), float(rope_base), _ptr(q_out),
+                                   _strides(q_out, 3), _ptr(k_cache), _ptr(v_cache),
+                                   _strides(k_cache, 3), k_cache.shape[1], _ptr(dst_pos), _stream()))
+    return q_out
 
 
 def mask_materialize(B: int, C: int, q: int, bl: int, o, mask_mode: str = "block_causal"):

@@ -1,5 +1,6 @@
 // Public C-ABI of libbdattn: argument validation (before any HIP call) and
 // dispatch to the kernel launchers.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -370,6 +371,39 @@ int bd_attn_packed_dual(int dtype, int B, int Hq, int Hkv, int d, int q, int bl,
   const PrefixArg pb{rows_b, n_b, pk_b, pv_b, pb_strides, pb_cap, p_len_b, p_max_b};
   return attn_entry("bd_attn_packed_dual", dtype, B, Hq, Hkv, d, q, bl, BD_MASK_BLOCK_CAUSAL, q_ptr, q_strides, pa, &pb,
                     wk, wv, w_strides, sm_scale, out, out_strides, lse, workspace, ws_bytes, stream);
+}
+
+int bd_qkv_rope_write(int dtype, int B, int q, int Dm, int Hq, int Hkv, int d, const void *x,
+                      const int64_t x_strides[2], const void *w, const int32_t *rope_pos,
+                      float rope_base, void *q_out, const int64_t q_strides[3], void *k_cache,
+                      void *v_cache, const int64_t c_strides[3], int c_cap, const int32_t *dst_pos,
+                      void *stream) {
+  g_err[0] = 0;
+  if (dtype != BD_BF16) return fail(BD_ERR_UNSUPPORTED, "bd_qkv_rope_write: only BD_BF16 is built");
+  if (d != 128) return fail(BD_ERR_UNSUPPORTED, "bd_qkv_rope_write: only d == 128 is built");
+  if (B < 0 || q < 0 || Dm <= 0 || Hq <= 0 || Hkv <= 0 || c_cap < 0)
+    return fail(BD_ERR_INVALID_ARG, "bd_qkv_rope_write: negative or zero size");
+  if (Dm % 32 != 0) return fail(BD_ERR_UNSUPPORTED, "bd_qkv_rope_write: Dm must be a multiple of 32");
+  if (!(rope_base > 1.f) || rope_base > 1e30f)
+    return fail(BD_ERR_INVALID_ARG, "bd_qkv_rope_write: rope_base must be > 1");
+  if ((int64_t)B * q > ((int64_t)1 << 24) || Hq + 2 * Hkv > 65535)
+    return fail(BD_ERR_INVALID_ARG, "bd_qkv_rope_write: too large for one launch");
+  if (B == 0 || q == 0) return BD_OK;
+  if (!x || !w || !rope_pos || !q_out || !k_cache || !v_cache || !dst_pos || !x_strides ||
+      !q_strides || !c_strides)
+    return fail(BD_ERR_INVALID_ARG, "bd_qkv_rope_write: null pointer");
+  if (!strides_ok(x_strides, 2, 2) || !strides_ok(q_strides, 3, 2) || !strides_ok(c_strides, 3, 2))
+    return fail(BD_ERR_INVALID_ARG, "bd_qkv_rope_write: strides must be >= 0 and 16-byte multiples");
+  if (!aligned16(x) || !aligned16(w) || !aligned16(q_out) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(BD_ERR_INVALID_ARG, "bd_qkv_rope_write: base pointers must be 16-byte aligned");
+  ProduceArgs a;
+  a.B = B; a.q = q; a.Dm = Dm; a.Hq = Hq; a.Hkv = Hkv; a.c_cap = c_cap;
+  a.x = (const bf16 *)x; a.xs[0] = x_strides[0]; a.xs[1] = x_strides[1];
+  a.w = (const bf16 *)w; a.rope_pos = rope_pos; a.dst_pos = dst_pos;
+  for (int j = 0; j < 64; ++j) a.inv_freq[j] = pow((double)rope_base, -2.0 * j / 128.0);
+  a.qo = (bf16 *)q_out; memcpy(a.qos, q_strides, sizeof(a.qos));
+  a.kc = (bf16 *)k_cache; a.vc = (bf16 *)v_cache; memcpy(a.cs, c_strides, sizeof(a.cs));
+  return hip_status(launch_produce(a, (hipStream_t)stream), "bd_qkv_rope_write launch");
 }
 
 int bd_mask_materialize(int B, int C, int q, int bl, int mask_mode, const int32_t *o, uint8_t *out,

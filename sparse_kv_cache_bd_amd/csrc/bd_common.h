@@ -155,4 +155,20 @@ hipError_t launch_select(const SelectArgs &a, hipStream_t s);
 size_t select_multi_workspace(int B, int Hkv, int s_max);
 hipError_t launch_select_multi(const SelectArgs &a, hipStream_t s);
 
+// Fused cache producer: QKV projection + RoPE + cache write (d = 128, bf16).
+struct ProduceArgs {
+  int B, q, Dm, Hq, Hkv, c_cap;
+  const bf16 *x;
+  int64_t xs[2];            // {row, token}
+  const bf16 *w;            // [(Hq + 2 Hkv) * 128, Dm], contiguous
+  const int32_t *rope_pos;  // absolute position of window token 0, per row
+  const int32_t *dst_pos;   // cache position of window token 0, per row
+  double inv_freq[64];      // rope_base^(-2j/128), j < 64
+  bf16 *qo;
+  int64_t qos[3];
+  bf16 *kc, *vc;
+  int64_t cs[3];
+};
+hipError_t launch_produce(const ProduceArgs &a, hipStream_t s);
+
 }  // namespace bd

@@ -1,0 +1,137 @@
+// Fused cache producer (Flash-dLLM, Flash-Cache): the projection of the
+// window's hidden states onto the query, key and value heads, the rotary
+// embedding of queries and keys at their absolute positions (HERALD Eq. (1);
+// FlowBlock's packed windows use absolute positions), and the write of keys
+// and values into the cache, with no intermediate tensor in HBM.
+//
+// One block computes one head (128 output features) for 256 window tokens:
+// Y^T = W_head X^T with v_mfma_f32_32x32x16_bf16, features on M and tokens
+// on N, so a lane ends with 16 features of one token; dimension j and its
+// rotary partner j + 64 sit in the same lane and register (M blocks mb and
+// mb + 2).  Eight waves (two per SIMD) each own 32 tokens and all 128
+// features.  Tiles of 32 hidden elements of W and X are double-buffered in
+// LDS, the next tile's global loads in flight during the MFMAs of the
+// current one, one barrier per tile.  The rotation angle is formed and
+// reduced to [-pi, pi] in double precision (positions reach 1e5 and more;
+// the inverse frequencies come from the host in double), its sine and cosine
+// taken in fp32 and applied to the fp32 accumulators; results are rounded to
+// bf16 once.
+#include "bd_common.h"
+
+namespace bd {
+
+namespace {
+
+constexpr int kPD = 128;               // head dim
+constexpr int kPTok = 256;             // tokens per block
+constexpr int kPBK = 32;               // hidden elements per staged tile
+constexpr int kPStr = kPBK + 8;        // LDS row stride (elements)
+
+__global__ __launch_bounds__(512, 1) void produce_kernel(ProduceArgs a) {
+  const int head = blockIdx.x;
+  const int t0 = blockIdx.y * kPTok;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hh = lane >> 5, ln = lane & 31;
+  const int n_tok = a.B * a.q;
+  __shared__ __attribute__((aligned(16))) bf16 Ws[2][kPD * kPStr];
+  __shared__ __attribute__((aligned(16))) bf16 Xs[2][kPTok * kPStr];
+
+  // staging: piece p of a tile is row p / 4, hidden elements 8 * (p % 4)..+8;
+  // a thread stages W row tid/4 and X rows tid/4 and tid/4 + 128 (tokens
+  // past the end re-read the last token; their results are not stored)
+  const int srow = tid >> 2, kq = (tid & 3) * 8;
+  const bf16 *wrow = a.w + ((int64_t)head * kPD + srow) * a.Dm + kq;
+  auto xrow = [&](int r) {
+    const int T = min(t0 + r, n_tok - 1);
+    const int b = T / a.q, i = T - b * a.q;
+    return a.x + (int64_t)b * a.xs[0] + (int64_t)i * a.xs[1] + kq;
+  };
+  const bf16 *xr0 = xrow(srow), *xr1 = xrow(srow + 128);
+  bf16x8 wv, xv0, xv1;
+  auto load = [&](int k0) {
+    wv = *reinterpret_cast<const bf16x8 *>(wrow + k0);
+    xv0 = *reinterpret_cast<const bf16x8 *>(xr0 + k0);
+    xv1 = *reinterpret_cast<const bf16x8 *>(xr1 + k0);
+  };
+  auto store = [&](int buf) {
+    *reinterpret_cast<bf16x8 *>(&Ws[buf][srow * kPStr + kq]) = wv;
+    *reinterpret_cast<bf16x8 *>(&Xs[buf][srow * kPStr + kq]) = xv0;
+    *reinterpret_cast<bf16x8 *>(&Xs[buf][(srow + 128) * kPStr + kq]) = xv1;
+  };
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x16{};
+  const int nit = a.Dm / kPBK;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int it = 0; it < nit; ++it) {
+    const int buf = it & 1;
+    const bool more = it + 1 < nit;
+    if (more) load((it + 1) * kPBK);
+#pragma unroll
+    for (int ks = 0; ks < kPBK / 16; ++ks) {
+      const bf16x8 xf = *reinterpret_cast<const bf16x8 *>(&Xs[buf][(wave * 32 + ln) * kPStr + ks * 16 + hh * 8]);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const bf16x8 wf = *reinterpret_cast<const bf16x8 *>(&Ws[buf][(mb * 32 + ln) * kPStr + ks * 16 + hh * 8]);
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, xf, acc[mb], 0, 0, 0);
+      }
+    }
+    if (more) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds features mb*32 + (r/4)*8 + hh*4 + r%4 of token T
+  const int T = t0 + wave * 32 + ln;
+  if (T >= n_tok) return;
+  const int b = T / a.q, i = T - b * a.q;
+  const int kind = head < a.Hq ? 0 : (head < a.Hq + a.Hkv ? 1 : 2);   // q, k, v
+  if (kind < 2) {
+    const double pos = (double)a.rope_pos[b] + (double)i;
+    constexpr double kTwoPi = 6.283185307179586476925;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int f = mb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+        // angle in double, reduced to [-pi, pi] in double, then sin / cos in fp32
+        const double ang = pos * a.inv_freq[f];
+        const double red = __builtin_fma(-__builtin_rint(ang * (1.0 / kTwoPi)), kTwoPi, ang);
+        float s, c;
+        __sincosf((float)red, &s, &c);
+        const float lo = acc[mb][r], hi = acc[mb + 2][r];
+        acc[mb][r] = lo * c - hi * s;
+        acc[mb + 2][r] = hi * c + lo * s;
+      }
+  }
+  bf16 *dst;
+  if (kind == 0) {
+    dst = a.qo + (int64_t)b * a.qos[0] + (int64_t)i * a.qos[1] + (int64_t)head * a.qos[2];
+  } else {
+    const int p = a.dst_pos[b] + i;
+    if (p < 0 || p >= a.c_cap) return;   // outside the cache: not written
+    const int h = kind == 1 ? head - a.Hq : head - a.Hq - a.Hkv;
+    dst = (kind == 1 ? a.kc : a.vc) + (int64_t)b * a.cs[0] + (int64_t)p * a.cs[1] + (int64_t)h * a.cs[2];
+  }
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      bf16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (bf16)acc[mb][r4 * 4 + e];
+      *reinterpret_cast<bf16x4 *>(dst + mb * 32 + r4 * 8 + hh * 4) = v;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_produce(const ProduceArgs &a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.Hq + 2 * a.Hkv), (unsigned)cdiv((int64_t)a.B * a.q, kPTok));
+  hipLaunchKernelGGL(produce_kernel, grid, dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace bd

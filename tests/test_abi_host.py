@@ -24,7 +24,7 @@ def L():
 
 def test_exports_every_header_function(L):
     names = bd.header_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     for n in names:
         assert hasattr(L, n), n
 
@@ -298,3 +298,32 @@ def test_mask_validation(L):
     assert L.bd_mask_materialize(2, 100, 64, 32, 0, None, FAKE2, None) == bd.BD_ERR_INVALID_ARG
     assert L.bd_mask_materialize(2, 100, 64, 32, 3, FAKE, FAKE2, None) == bd.BD_ERR_INVALID_ARG
     assert L.bd_mask_materialize(0, 100, 64, 32, 0, None, None, None) == bd.BD_OK
+
+
+def _produce(L, **kw):
+    a = dict(dtype=bd.BD_BF16, B=2, q=64, Dm=256, Hq=8, Hkv=2, d=128, x=FAKE,
+             xs=(ctypes.c_int64 * 2)(64 * 256, 256), w=FAKE2, rope_pos=FAKE, base=10000.0,
+             qo=FAKE, qs=I3(64 * 1024, 1024, 128), kc=FAKE, vc=FAKE2, cs=I3(1 << 20, 256, 128),
+             cap=4096, dst=FAKE)
+    a.update(kw)
+    return L.bd_qkv_rope_write(a["dtype"], a["B"], a["q"], a["Dm"], a["Hq"], a["Hkv"], a["d"],
+                               a["x"], a["xs"], a["w"], a["rope_pos"], a["base"], a["qo"],
+                               a["qs"], a["kc"], a["vc"], a["cs"], a["cap"], a["dst"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=bd.BD_F32), bd.BD_ERR_UNSUPPORTED),
+    (dict(d=64), bd.BD_ERR_UNSUPPORTED),
+    (dict(Dm=100), bd.BD_ERR_UNSUPPORTED),                 # not a multiple of 32
+    (dict(Dm=0), bd.BD_ERR_INVALID_ARG),
+    (dict(base=1.0), bd.BD_ERR_INVALID_ARG),
+    (dict(base=float("nan")), bd.BD_ERR_INVALID_ARG),
+    (dict(w=None), bd.BD_ERR_INVALID_ARG),
+    (dict(dst=None), bd.BD_ERR_INVALID_ARG),
+    (dict(x=MISALIGNED), bd.BD_ERR_INVALID_ARG),
+    (dict(cs=I3(1 << 20, 250, 128)), bd.BD_ERR_INVALID_ARG),   # row stride not 16 B
+    (dict(B=0), bd.BD_OK),
+    (dict(q=0, x=None), bd.BD_OK),
+])
+def test_producer_validation(L, kw, code):
+    assert _produce(L, **kw) == code
