@@ -383,7 +383,7 @@ int bd_qkv_rope_write(int dtype, int B, int q, int Dm, int Hq, int Hkv, int d, c
   if (d != 128) return fail(BD_ERR_UNSUPPORTED, "bd_qkv_rope_write: only d == 128 is built");
   if (B < 0 || q < 0 || Dm <= 0 || Hq <= 0 || Hkv <= 0 || c_cap < 0)
     return fail(BD_ERR_INVALID_ARG, "bd_qkv_rope_write: negative or zero size");
-  if (Dm % 32 != 0) return fail(BD_ERR_UNSUPPORTED, "bd_qkv_rope_write: Dm must be a multiple of 32");
+  if (Dm % 64 != 0) return fail(BD_ERR_UNSUPPORTED, "bd_qkv_rope_write: Dm must be a multiple of 64");
   if (!(rope_base > 1.f) || rope_base > 1e30f)
     return fail(BD_ERR_INVALID_ARG, "bd_qkv_rope_write: rope_base must be > 1");
   if ((int64_t)B * q > ((int64_t)1 << 24) || Hq + 2 * Hkv > 65535)

@@ -8,10 +8,10 @@
 // Y^T = W_head X^T with v_mfma_f32_32x32x16_bf16, features on M and tokens
 // on N, so a lane ends with 16 features of one token; dimension j and its
 // rotary partner j + 64 sit in the same lane and register (M blocks mb and
-// mb + 2).  Eight waves (two per SIMD) each own 32 tokens and all 128
-// features.  Tiles of 32 hidden elements of W and X are double-buffered in
-// LDS, the next tile's global loads in flight during the MFMAs of the
-// current one, one barrier per tile.  The rotation angle is formed and
+// mb + 2).  Eight waves each own 32 tokens and all 128 features; two
+// blocks share a CU.  Tiles of 32 hidden elements of W and X are
+// double-buffered in LDS and staged through two register sets, so a tile's
+// global loads have two tiles of MFMAs to land; one barrier per tile.  The rotation angle is formed and
 // reduced to [-pi, pi] in double precision (positions reach 1e5 and more;
 // the inverse frequencies come from the host in double), its sine and cosine
 // taken in fp32 and applied to the fp32 accumulators; results are rounded to
@@ -47,29 +47,27 @@ __global__ __launch_bounds__(512, 1) void produce_kernel(ProduceArgs a) {
     return a.x + (int64_t)b * a.xs[0] + (int64_t)i * a.xs[1] + kq;
   };
   const bf16 *xr0 = xrow(srow), *xr1 = xrow(srow + 128);
-  bf16x8 wv, xv0, xv1;
-  auto load = [&](int k0) {
-    wv = *reinterpret_cast<const bf16x8 *>(wrow + k0);
-    xv0 = *reinterpret_cast<const bf16x8 *>(xr0 + k0);
-    xv1 = *reinterpret_cast<const bf16x8 *>(xr1 + k0);
+  // two register sets: tile it+2 is loaded while tile it is computed and
+  // tile it+1 goes from registers to LDS (loads are unconditional, clamped
+  // to the last tile, so every wait count is static)
+  bf16x8 rw[2], rx0[2], rx1[2];
+  const int nit = a.Dm / kPBK;   // even: the loop body handles two tiles
+  auto load = [&](int tile, int set) {
+    const int k0 = min(tile, nit - 1) * kPBK;
+    rw[set] = *reinterpret_cast<const bf16x8 *>(wrow + k0);
+    rx0[set] = *reinterpret_cast<const bf16x8 *>(xr0 + k0);
+    rx1[set] = *reinterpret_cast<const bf16x8 *>(xr1 + k0);
   };
-  auto store = [&](int buf) {
-    *reinterpret_cast<bf16x8 *>(&Ws[buf][srow * kPStr + kq]) = wv;
-    *reinterpret_cast<bf16x8 *>(&Xs[buf][srow * kPStr + kq]) = xv0;
-    *reinterpret_cast<bf16x8 *>(&Xs[buf][(srow + 128) * kPStr + kq]) = xv1;
+  auto store = [&](int buf, int set) {
+    *reinterpret_cast<bf16x8 *>(&Ws[buf][srow * kPStr + kq]) = rw[set];
+    *reinterpret_cast<bf16x8 *>(&Xs[buf][srow * kPStr + kq]) = rx0[set];
+    *reinterpret_cast<bf16x8 *>(&Xs[buf][(srow + 128) * kPStr + kq]) = rx1[set];
   };
 
   f32x16 acc[4];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x16{};
-  const int nit = a.Dm / kPBK;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int it = 0; it < nit; ++it) {
-    const int buf = it & 1;
-    const bool more = it + 1 < nit;
-    if (more) load((it + 1) * kPBK);
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < kPBK / 16; ++ks) {
       const bf16x8 xf = *reinterpret_cast<const bf16x8 *>(&Xs[buf][(wave * 32 + ln) * kPStr + ks * 16 + hh * 8]);
@@ -79,7 +77,20 @@ __global__ __launch_bounds__(512, 1) void produce_kernel(ProduceArgs a) {
         acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, xf, acc[mb], 0, 0, 0);
       }
     }
-    if (more) store(buf ^ 1);
+  };
+  load(0, 0);
+  store(0, 0);
+  load(1, 1);
+  load(2, 0);
+  __syncthreads();
+  for (int it = 0; it < nit; it += 2) {
+    compute(0);          // tile it
+    store(1, 1);         // tile it + 1
+    load(it + 3, 1);
+    __syncthreads();
+    compute(1);          // tile it + 1
+    store(0, 0);         // tile it + 2
+    load(it + 4, 0);
     __syncthreads();
   }
 

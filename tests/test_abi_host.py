@@ -314,7 +314,7 @@ def _produce(L, **kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=bd.BD_F32), bd.BD_ERR_UNSUPPORTED),
     (dict(d=64), bd.BD_ERR_UNSUPPORTED),
-    (dict(Dm=100), bd.BD_ERR_UNSUPPORTED),                 # not a multiple of 32
+    (dict(Dm=96), bd.BD_ERR_UNSUPPORTED),                  # not a multiple of 64
     (dict(Dm=0), bd.BD_ERR_INVALID_ARG),
     (dict(base=1.0), bd.BD_ERR_INVALID_ARG),
     (dict(base=float("nan")), bd.BD_ERR_INVALID_ARG),
