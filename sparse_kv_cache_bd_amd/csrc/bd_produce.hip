@@ -25,7 +25,13 @@ namespace {
 constexpr int kPD = 128;               // head dim
 constexpr int kPTok = 256;             // tokens per block
 constexpr int kPBK = 32;               // hidden elements per staged tile
-constexpr int kPStr = kPBK + 8;        // LDS row stride (elements)
+constexpr int kPStr = kPBK;            // LDS row stride (elements): 64 bytes
+
+// LDS element offset of 16-byte chunk c (0..3) of staged row `row`: the chunk
+// index is XORed with bits 2-3 of the row, so 16 lanes writing 4 rows x 4
+// chunks, and 16 lanes reading one chunk of 16 consecutive rows, each touch
+// 16 distinct 4-bank groups of the 64 LDS banks.
+__device__ inline int lds_off(int row, int c) { return row * kPStr + ((c ^ ((row >> 2) & 3)) << 3); }
 
 __global__ __launch_bounds__(512, 1) void produce_kernel(ProduceArgs a) {
   const int head = blockIdx.x;
@@ -39,7 +45,7 @@ __global__ __launch_bounds__(512, 1) void produce_kernel(ProduceArgs a) {
   // staging: piece p of a tile is row p / 4, hidden elements 8 * (p % 4)..+8;
   // a thread stages W row tid/4 and X rows tid/4 and tid/4 + 128 (tokens
   // past the end re-read the last token; their results are not stored)
-  const int srow = tid >> 2, kq = (tid & 3) * 8;
+  const int srow = tid >> 2, kc = tid & 3, kq = kc * 8;
   const bf16 *wrow = a.w + ((int64_t)head * kPD + srow) * a.Dm + kq;
   auto xrow = [&](int r) {
     const int T = min(t0 + r, n_tok - 1);
@@ -59,9 +65,9 @@ __global__ __launch_bounds__(512, 1) void produce_kernel(ProduceArgs a) {
     rx1[set] = *reinterpret_cast<const bf16x8 *>(xr1 + k0);
   };
   auto store = [&](int buf, int set) {
-    *reinterpret_cast<bf16x8 *>(&Ws[buf][srow * kPStr + kq]) = rw[set];
-    *reinterpret_cast<bf16x8 *>(&Xs[buf][srow * kPStr + kq]) = rx0[set];
-    *reinterpret_cast<bf16x8 *>(&Xs[buf][(srow + 128) * kPStr + kq]) = rx1[set];
+    *reinterpret_cast<bf16x8 *>(&Ws[buf][lds_off(srow, kc)]) = rw[set];
+    *reinterpret_cast<bf16x8 *>(&Xs[buf][lds_off(srow, kc)]) = rx0[set];
+    *reinterpret_cast<bf16x8 *>(&Xs[buf][lds_off(srow + 128, kc)]) = rx1[set];
   };
 
   f32x16 acc[4];
@@ -70,10 +76,10 @@ __global__ __launch_bounds__(512, 1) void produce_kernel(ProduceArgs a) {
   auto compute = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < kPBK / 16; ++ks) {
-      const bf16x8 xf = *reinterpret_cast<const bf16x8 *>(&Xs[buf][(wave * 32 + ln) * kPStr + ks * 16 + hh * 8]);
+      const bf16x8 xf = *reinterpret_cast<const bf16x8 *>(&Xs[buf][lds_off(wave * 32 + ln, ks * 2 + hh)]);
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
-        const bf16x8 wf = *reinterpret_cast<const bf16x8 *>(&Ws[buf][(mb * 32 + ln) * kPStr + ks * 16 + hh * 8]);
+        const bf16x8 wf = *reinterpret_cast<const bf16x8 *>(&Ws[buf][lds_off(mb * 32 + ln, ks * 2 + hh)]);
         acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, xf, acc[mb], 0, 0, 0);
       }
     }
