@@ -33,7 +33,7 @@ constexpr int kPStr = kPBK;            // LDS row stride (elements): 64 bytes
 // 16 distinct 4-bank groups of the 64 LDS banks.
 __device__ inline int lds_off(int row, int c) { return row * kPStr + ((c ^ ((row >> 2) & 3)) << 3); }
 
-__global__ __launch_bounds__(512, 1) void produce_kernel(ProduceArgs a) {
+__global__ __launch_bounds__(256, 2) void produce_kernel(ProduceArgs a) {
   const int head = blockIdx.x;
   const int t0 = blockIdx.y * kPTok;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -42,46 +42,59 @@ __global__ __launch_bounds__(512, 1) void produce_kernel(ProduceArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 Ws[2][kPD * kPStr];
   __shared__ __attribute__((aligned(16))) bf16 Xs[2][kPTok * kPStr];
 
-  // staging: piece p of a tile is row p / 4, hidden elements 8 * (p % 4)..+8;
-  // a thread stages W row tid/4 and X rows tid/4 and tid/4 + 128 (tokens
-  // past the end re-read the last token; their results are not stored)
+  // staging: piece p of a tile is row p / 4, 16-byte chunk p % 4; a thread
+  // stages W rows tid/4 + 64 u (u < 2) and X rows tid/4 + 64 u (u < 4);
+  // tokens past the end re-read the last token (their results are not stored)
   const int srow = tid >> 2, kc = tid & 3, kq = kc * 8;
   const bf16 *wrow = a.w + ((int64_t)head * kPD + srow) * a.Dm + kq;
-  auto xrow = [&](int r) {
-    const int T = min(t0 + r, n_tok - 1);
+  const int64_t wstep = (int64_t)64 * a.Dm;
+  const bf16 *xr[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int T = min(t0 + srow + 64 * u, n_tok - 1);
     const int b = T / a.q, i = T - b * a.q;
-    return a.x + (int64_t)b * a.xs[0] + (int64_t)i * a.xs[1] + kq;
-  };
-  const bf16 *xr0 = xrow(srow), *xr1 = xrow(srow + 128);
+    xr[u] = a.x + (int64_t)b * a.xs[0] + (int64_t)i * a.xs[1] + kq;
+  }
   // two register sets: tile it+2 is loaded while tile it is computed and
   // tile it+1 goes from registers to LDS (loads are unconditional, clamped
   // to the last tile, so every wait count is static)
-  bf16x8 rw[2], rx0[2], rx1[2];
+  bf16x8 rw[2][2], rx[2][4];
   const int nit = a.Dm / kPBK;   // even: the loop body handles two tiles
   auto load = [&](int tile, int set) {
     const int k0 = min(tile, nit - 1) * kPBK;
-    rw[set] = *reinterpret_cast<const bf16x8 *>(wrow + k0);
-    rx0[set] = *reinterpret_cast<const bf16x8 *>(xr0 + k0);
-    rx1[set] = *reinterpret_cast<const bf16x8 *>(xr1 + k0);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) rw[set][u] = *reinterpret_cast<const bf16x8 *>(wrow + u * wstep + k0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) rx[set][u] = *reinterpret_cast<const bf16x8 *>(xr[u] + k0);
   };
   auto store = [&](int buf, int set) {
-    *reinterpret_cast<bf16x8 *>(&Ws[buf][lds_off(srow, kc)]) = rw[set];
-    *reinterpret_cast<bf16x8 *>(&Xs[buf][lds_off(srow, kc)]) = rx0[set];
-    *reinterpret_cast<bf16x8 *>(&Xs[buf][lds_off(srow + 128, kc)]) = rx1[set];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) *reinterpret_cast<bf16x8 *>(&Ws[buf][lds_off(srow + 64 * u, kc)]) = rw[set][u];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) *reinterpret_cast<bf16x8 *>(&Xs[buf][lds_off(srow + 64 * u, kc)]) = rx[set][u];
   };
 
-  f32x16 acc[4];
+  // acc[nb][mb]: token block nb (32 tokens) x feature block mb (32 features)
+  f32x16 acc[2][4];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x16{};
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = f32x16{};
   auto compute = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < kPBK / 16; ++ks) {
-      const bf16x8 xf = *reinterpret_cast<const bf16x8 *>(&Xs[buf][lds_off(wave * 32 + ln, ks * 2 + hh)]);
+      bf16x8 xf[2], wf[4];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const bf16x8 wf = *reinterpret_cast<const bf16x8 *>(&Ws[buf][lds_off(mb * 32 + ln, ks * 2 + hh)]);
-        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, xf, acc[mb], 0, 0, 0);
-      }
+      for (int nb = 0; nb < 2; ++nb)
+        xf[nb] = *reinterpret_cast<const bf16x8 *>(&Xs[buf][lds_off(wave * 64 + nb * 32 + ln, ks * 2 + hh)]);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+        wf[mb] = *reinterpret_cast<const bf16x8 *>(&Ws[buf][lds_off(mb * 32 + ln, ks * 2 + hh)]);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[mb], xf[nb], acc[nb][mb], 0, 0, 0);
     }
   };
   load(0, 0);
@@ -101,53 +114,56 @@ __global__ __launch_bounds__(512, 1) void produce_kernel(ProduceArgs a) {
   }
 
   // ---- epilogue: lane holds features mb*32 + (r/4)*8 + hh*4 + r%4 of token T
-  const int T = t0 + wave * 32 + ln;
-  if (T >= n_tok) return;
-  const int b = T / a.q, i = T - b * a.q;
   const int kind = head < a.Hq ? 0 : (head < a.Hq + a.Hkv ? 1 : 2);   // q, k, v
-  if (kind < 2) {
-    const double pos = (double)a.rope_pos[b] + (double)i;
-    constexpr double kTwoPi = 6.283185307179586476925;
+  constexpr double kTwoPi = 6.283185307179586476925;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+  for (int nb = 0; nb < 2; ++nb) {
+    const int T = t0 + wave * 64 + nb * 32 + ln;
+    if (T >= n_tok) continue;
+    const int b = T / a.q, i = T - b * a.q;
+    if (kind < 2) {
+      const double pos = (double)a.rope_pos[b] + (double)i;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int f = mb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-        // angle in double, reduced to [-pi, pi] in double, then sin / cos in fp32
-        const double ang = pos * a.inv_freq[f];
-        const double red = __builtin_fma(-__builtin_rint(ang * (1.0 / kTwoPi)), kTwoPi, ang);
-        float s, c;
-        __sincosf((float)red, &s, &c);
-        const float lo = acc[mb][r], hi = acc[mb + 2][r];
-        acc[mb][r] = lo * c - hi * s;
-        acc[mb + 2][r] = hi * c + lo * s;
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int f = mb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+          // angle in double, reduced to [-pi, pi] in double, then sin / cos in fp32
+          const double ang = pos * a.inv_freq[f];
+          const double red = __builtin_fma(-__builtin_rint(ang * (1.0 / kTwoPi)), kTwoPi, ang);
+          float s, c;
+          __sincosf((float)red, &s, &c);
+          const float lo = acc[nb][mb][r], hi = acc[nb][mb + 2][r];
+          acc[nb][mb][r] = lo * c - hi * s;
+          acc[nb][mb + 2][r] = hi * c + lo * s;
+        }
+    }
+    bf16 *dst;
+    if (kind == 0) {
+      dst = a.qo + (int64_t)b * a.qos[0] + (int64_t)i * a.qos[1] + (int64_t)head * a.qos[2];
+    } else {
+      const int p = a.dst_pos[b] + i;
+      if (p < 0 || p >= a.c_cap) continue;   // outside the cache: not written
+      const int h = kind == 1 ? head - a.Hq : head - a.Hq - a.Hkv;
+      dst = (kind == 1 ? a.kc : a.vc) + (int64_t)b * a.cs[0] + (int64_t)p * a.cs[1] + (int64_t)h * a.cs[2];
+    }
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (bf16)acc[nb][mb][r4 * 4 + e];
+        *reinterpret_cast<bf16x4 *>(dst + mb * 32 + r4 * 8 + hh * 4) = v;
       }
   }
-  bf16 *dst;
-  if (kind == 0) {
-    dst = a.qo + (int64_t)b * a.qos[0] + (int64_t)i * a.qos[1] + (int64_t)head * a.qos[2];
-  } else {
-    const int p = a.dst_pos[b] + i;
-    if (p < 0 || p >= a.c_cap) return;   // outside the cache: not written
-    const int h = kind == 1 ? head - a.Hq : head - a.Hq - a.Hkv;
-    dst = (kind == 1 ? a.kc : a.vc) + (int64_t)b * a.cs[0] + (int64_t)p * a.cs[1] + (int64_t)h * a.cs[2];
-  }
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      bf16x4 v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (bf16)acc[mb][r4 * 4 + e];
-      *reinterpret_cast<bf16x4 *>(dst + mb * 32 + r4 * 8 + hh * 4) = v;
-    }
 }
 
 }  // namespace
 
 hipError_t launch_produce(const ProduceArgs &a, hipStream_t s) {
   const dim3 grid((unsigned)(a.Hq + 2 * a.Hkv), (unsigned)cdiv((int64_t)a.B * a.q, kPTok));
-  hipLaunchKernelGGL(produce_kernel, grid, dim3(512), 0, s, a);
+  hipLaunchKernelGGL(produce_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
