@@ -21,9 +21,11 @@
 //          and invalidate the L2 of the XCD on every block.)
 //   topk   exact radix select of the k-th largest score on its fp32 bit
 //          pattern (non-negative floats order like their bit patterns;
-//          digits of 11, 11 and 10 bits), then an ordered compaction: every
+//          digits of 11, 11 and 10 bits; the first digit's histogram is
+//          built by the score pass), then an ordered compaction: every
 //          score above the threshold plus the lowest-position ties,
-//          ascending, -1 padding.  Rows of up to kLdsKeys scores: one block
+//          ascending, -1 padding (one prefix sum per chunk when every tie is
+//          kept).  Rows of up to kLdsKeys scores: one block
 //          per (row, KV head) with the scores read once into LDS.  Longer
 //          rows: blocks of kCK scores; the score pass histograms the first
 //          digit, two passes the others, then per-block counts and an
@@ -45,6 +47,7 @@ constexpr int kBins = 2048;        // radix digit bins (11 bits)
 constexpr int kThreads = 256;
 constexpr int kTopkThreads = 1024;
 constexpr int kPerThread = 16;     // consecutive scores per thread in the compaction
+constexpr int kRankU = 8;          // keys per thread per histogram round
 constexpr int kLdsKeys = 32768;    // longest score row ranked by one block from LDS
 constexpr int kCK = 4096;          // scores per block of the multi-block ranking path
 constexpr int kZStr = kTS + 16;    // LDS row stride of the scan's z staging (floats)
@@ -70,7 +73,7 @@ SelLayout sel_layout(int B, int Hq, int Hkv, int d, int s_max) {
   L.z = take((size_t)B * Hq * (size_t)L.zs * 4);
   L.part = take((size_t)B * Hq * L.nch_scan * 2 * 4);
   L.scores = take(P * (size_t)s_max * 4);
-  L.hist = L.multi ? take(P * 3 * kBins * 4) : 0;
+  L.hist = take(P * 3 * kBins * 4);
   L.ccount = L.multi ? take(P * L.nch_topk * 2 * 4) : 0;
   L.total = off;
   return L;
@@ -79,7 +82,7 @@ SelLayout sel_layout(int B, int Hq, int Hkv, int d, int s_max) {
 struct SelPtrs {
   bf16 *qhi, *qlo;
   float *z, *part, *scores;
-  uint32_t *hist, *ccount;   // multi-block ranking: digit histograms, per-chunk counts
+  uint32_t *hist, *ccount;   // digit histograms (digit 0 for every row); per-chunk counts
   int nch_scan, zs, nch_topk;
   bool multi;
 };
@@ -185,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void sel_prep_kernel(SelectArgs a, SelPtr
     w.qhi[((int64_t)b * a.Hq + hq) * kSD + t] = hi;
     w.qlo[((int64_t)b * a.Hq + hq) * kSD + t] = lo;
   }
-  if (w.multi) {  // this row's digit histograms (Hkv x 3 x kBins words)
+  {  // this row's digit histograms (Hkv x 3 x kBins words)
     const int words = a.Hkv * 3 * kBins;
     uint32_t *hist = w.hist + (size_t)b * words;
     for (int e = hq * kThreads + t; e < words; e += a.Hq * kThreads) hist[e] = 0;
@@ -387,8 +390,7 @@ __global__ __launch_bounds__(kThreads) void sel_score_kernel(SelectArgs a, SelPt
     }
   }
   __shared__ uint32_t hist[kBins];
-  if (w.multi)
-    for (int e = threadIdx.x; e < kBins; e += kThreads) hist[e] = 0;
+  for (int e = threadIdx.x; e < kBins; e += kThreads) hist[e] = 0;
   __syncthreads();
   const int s = c * kScoreTok + threadIdx.x * per;
   const bool full = s + per <= S;
@@ -426,7 +428,7 @@ __global__ __launch_bounds__(kThreads) void sel_score_kernel(SelectArgs a, SelPt
     for (int r = 0; r < per; ++r)
       if (s + r < S) op[r] = acc[r];
   }
-  if (w.multi) {  // first radix digit (bits 31..21) of the scores just written
+  {  // first radix digit (bits 31..21) of the scores just written
 #pragma unroll
     for (int r = 0; r < per; ++r) hist_add(hist, __float_as_uint(acc[r]) >> 21, s + r < S);
     __syncthreads();
@@ -481,32 +483,72 @@ __device__ inline void find_digit(const uint32_t *cnt_of, int nb, uint32_t krem,
 __device__ inline int cpos(int s) { return s + (s >> 4); }
 
 __device__ inline void topk_body(const uint32_t *keys, int S, int keff, int32_t *out, uint32_t *hist,
-                                 int *sh) {
+                                 int *sh, const uint32_t *hist0) {
   uint32_t prefix = 0, krem = (uint32_t)keff;
+  int total_eq = 0;  // scores equal to the threshold (the last digit's count)
+  {  // digit 0: the histogram the score pass built while writing the scores
+    uint32_t D;
+    find_digit(hist0, kBins, krem, sh, D, krem);
+    prefix = D << 21;
+  }
 #pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+  for (int pass = 1; pass < 3; ++pass) {
+    const int shift = pass == 1 ? 10 : 0;
     const uint32_t dmask = pass == 2 ? 1023u : 2047u;
     const int hi_shift = shift + (pass == 2 ? 10 : 11);  // bits above this digit
     for (int e = threadIdx.x; e < kBins; e += kTopkThreads) hist[e] = 0;
     __syncthreads();
-    for (int s0 = 0; s0 < S; s0 += kTopkThreads) {
-      const int s = s0 + threadIdx.x;
-      const uint32_t key = s < S ? keys[cpos(s)] : 0u;
-      if (pass == 0) {
-        // the first digit is dominated by the exponent: aggregate per wave
-        hist_add(hist, (key >> shift) & dmask, s < S);
-      } else if (s < S && (key >> hi_shift) == (prefix >> hi_shift)) {
-        atomicAdd(&hist[(key >> shift) & dmask], 1u);
+    // kRankU keys per thread per round: their LDS reads are issued together,
+    // then the histogram updates (the reads' latencies overlap)
+    for (int s0 = 0; s0 < S; s0 += kTopkThreads * kRankU) {
+      uint32_t kk[kRankU];
+#pragma unroll
+      for (int u = 0; u < kRankU; ++u) {
+        const int s = s0 + u * kTopkThreads + threadIdx.x;
+        kk[u] = s < S ? keys[cpos(s)] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < kRankU; ++u) {
+        const int s = s0 + u * kTopkThreads + threadIdx.x;
+        if (s < S && (kk[u] >> hi_shift) == (prefix >> hi_shift)) atomicAdd(&hist[(kk[u] >> shift) & dmask], 1u);
       }
     }
     __syncthreads();
     uint32_t D;
     find_digit(hist, pass == 2 ? 1024 : kBins, krem, sh, D, krem);
     prefix |= D << shift;
+    if (pass == 2) total_eq = (int)hist[D];
   }
   const uint32_t thr = prefix;
   const int need_eq = (int)krem;
+
+  if (need_eq == total_eq) {
+    // every score equal to the threshold is kept (the usual case): the kept
+    // set is the scores >= thr, one prefix sum per chunk
+    int sel_base = 0;
+    for (int c0 = 0; c0 < S; c0 += kTopkThreads * kPerThread) {
+      const int sb = c0 + threadIdx.x * kPerThread;
+      uint32_t selbits = 0;
+      int n_sel = 0;
+#pragma unroll
+      for (int e = 0; e < kPerThread; ++e) {
+        const int s = sb + e;
+        const bool sel = s < S && keys[cpos(s)] >= thr;
+        selbits |= (uint32_t)sel << e;
+        n_sel += sel;
+      }
+      int tot_sel;
+      int pos = sel_base + block_excl_scan(n_sel, sh, tot_sel);
+#pragma unroll
+      for (int e = 0; e < kPerThread; ++e)
+        if (selbits & (1u << e)) {
+          if (pos < keff) out[pos] = sb + e;
+          ++pos;
+        }
+      sel_base += tot_sel;
+    }
+    return;
+  }
 
   // ordered compaction: kPerThread consecutive scores per thread per chunk
   int sel_base = 0, eq_base = 0;  // selections / ties before the current chunk
@@ -584,7 +626,7 @@ __global__ __launch_bounds__(kTopkThreads) void sel_topk_kernel(SelectArgs a, Se
     }
   }
   __syncthreads();
-  topk_body(cache, S, keff, out, hist, sh);
+  topk_body(cache, S, keff, out, hist, sh, w.hist + (size_t)p * 3 * kBins);
 }
 
 // ------------------------------------------------------ multi-block ranking
@@ -785,7 +827,7 @@ MultiLayout multi_layout(int B, int Hkv, int s_max) {
   L.part = take(P * kMCols * (size_t)L.nch * 2 * 4);
   L.mp = take(P * kMCols * 4);
   L.scores = take(P * (size_t)s_max * 4);
-  L.hist = L.multi ? take(P * 3 * kBins * 4) : 0;
+  L.hist = take(P * 3 * kBins * 4);
   L.ccount = L.multi ? take(P * L.nch_topk * 2 * 4) : 0;
   L.total = off;
   return L;
@@ -943,7 +985,7 @@ __global__ __launch_bounds__(kMCols) void selm_merge_kernel(SelectArgs a, MultiP
     }
     w.mp[((int64_t)b * a.Hkv + h) * kMCols + col] = M + __log2f(Lsum);
   }
-  if (w.multi) {
+  {
     uint32_t *hist = w.hist + ((size_t)b * a.Hkv + h) * 3 * kBins;
     for (int e = threadIdx.x; e < 3 * kBins; e += kMCols) hist[e] = 0;
   }
@@ -963,8 +1005,7 @@ __global__ __launch_bounds__(kThreads, 2) void selm_score_kernel(SelectArgs a, M
   stage_columns(a, b, h, ncol, ncb * 16, qs);
   for (int col = tid; col < kMCols; col += kThreads)
     mps[col] = col < ncol ? w.mp[((int64_t)b * a.Hkv + h) * kMCols + col] : INFINITY;
-  if (w.multi)
-    for (int e = tid; e < kBins; e += kThreads) hist[e] = 0;
+  for (int e = tid; e < kBins; e += kThreads) hist[e] = 0;
   __syncthreads();
 
   const int s0 = c * kMTok, s_end = min(s0 + kMTok, S);
@@ -1008,7 +1049,7 @@ __global__ __launch_bounds__(kThreads, 2) void selm_score_kernel(SelectArgs a, M
     const float v = grp == 0 ? acc[0] : (grp == 1 ? acc[1] : (grp == 2 ? acc[2] : acc[3]));
     const int tok = t0 + lane;
     if (tok < S) orow[tok] = v;
-    if (w.multi) hist_add(hist, __float_as_uint(v) >> 21, tok < S);
+    hist_add(hist, __float_as_uint(v) >> 21, tok < S);
   };
   if (ng > 0) {
     bf16x8 ka[4][4], kb2[4][4];
@@ -1021,7 +1062,7 @@ __global__ __launch_bounds__(kThreads, 2) void selm_score_kernel(SelectArgs a, M
     if (2 < ng) compute(2, ka);
     if (3 < ng) compute(3, kb2);
   }
-  if (w.multi) {  // first radix digit of the scores just written
+  {  // first radix digit of the scores just written
     __syncthreads();
     uint32_t *gh = w.hist + ((size_t)b * a.Hkv + h) * 3 * kBins;
     for (int e = tid; e < kBins; e += kThreads)
