@@ -33,45 +33,50 @@ constexpr int kPStr = kPBK;            // LDS row stride (elements): 64 bytes
 // 16 distinct 4-bank groups of the 64 LDS banks.
 __device__ inline int lds_off(int row, int c) { return row * kPStr + ((c ^ ((row >> 2) & 3)) << 3); }
 
-__global__ __launch_bounds__(256, 2) void produce_kernel(ProduceArgs a) {
-  const int head = blockIdx.x;
+__global__ __launch_bounds__(512, 1) void produce_kernel(ProduceArgs a) {
+  const int nheads = a.Hq + 2 * a.Hkv;
   const int t0 = blockIdx.y * kPTok;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave_all = tid >> 6;
+  const int hsel = wave_all >> 2, wave = wave_all & 3;   // head of the pair, token quarter
+  const int head = min(2 * (int)blockIdx.x + hsel, nheads - 1);
+  const bool head_ok = 2 * (int)blockIdx.x + hsel < nheads;
   const int hh = lane >> 5, ln = lane & 31;
   const int n_tok = a.B * a.q;
-  __shared__ __attribute__((aligned(16))) bf16 Ws[2][kPD * kPStr];
+  __shared__ __attribute__((aligned(16))) bf16 Ws[2][2 * kPD * kPStr];
   __shared__ __attribute__((aligned(16))) bf16 Xs[2][kPTok * kPStr];
 
   // staging: piece p of a tile is row p / 4, 16-byte chunk p % 4; a thread
   // stages W rows tid/4 + 64 u (u < 2) and X rows tid/4 + 64 u (u < 4);
   // tokens past the end re-read the last token (their results are not stored)
-  const int srow = tid >> 2, kc = tid & 3, kq = kc * 8;
-  const bf16 *wrow = a.w + ((int64_t)head * kPD + srow) * a.Dm + kq;
-  const int64_t wstep = (int64_t)64 * a.Dm;
-  const bf16 *xr[4];
+  const int srow = tid >> 2, kc = tid & 3, kq = kc * 8;   // srow < 128
+  // W rows srow and srow + 128 of the pair's 256 (a missing second head
+  // re-reads the last head; its results are not stored)
+  const bf16 *wrow0 = a.w + ((int64_t)(2 * blockIdx.x) * kPD + srow) * a.Dm + kq;
+  const bf16 *wrow1 = a.w + ((int64_t)min(2 * (int)blockIdx.x + 1, nheads - 1) * kPD + srow) * a.Dm + kq;
+  const bf16 *xr[2];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int T = min(t0 + srow + 64 * u, n_tok - 1);
+  for (int u = 0; u < 2; ++u) {
+    const int T = min(t0 + srow + 128 * u, n_tok - 1);
     const int b = T / a.q, i = T - b * a.q;
     xr[u] = a.x + (int64_t)b * a.xs[0] + (int64_t)i * a.xs[1] + kq;
   }
   // two register sets: tile it+2 is loaded while tile it is computed and
   // tile it+1 goes from registers to LDS (loads are unconditional, clamped
   // to the last tile, so every wait count is static)
-  bf16x8 rw[2][2], rx[2][4];
+  bf16x8 rw[2][2], rx[2][2];
   const int nit = a.Dm / kPBK;   // even: the loop body handles two tiles
   auto load = [&](int tile, int set) {
     const int k0 = min(tile, nit - 1) * kPBK;
+    rw[set][0] = *reinterpret_cast<const bf16x8 *>(wrow0 + k0);
+    rw[set][1] = *reinterpret_cast<const bf16x8 *>(wrow1 + k0);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) rw[set][u] = *reinterpret_cast<const bf16x8 *>(wrow + u * wstep + k0);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) rx[set][u] = *reinterpret_cast<const bf16x8 *>(xr[u] + k0);
+    for (int u = 0; u < 2; ++u) rx[set][u] = *reinterpret_cast<const bf16x8 *>(xr[u] + k0);
   };
   auto store = [&](int buf, int set) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) *reinterpret_cast<bf16x8 *>(&Ws[buf][lds_off(srow + 64 * u, kc)]) = rw[set][u];
+    for (int u = 0; u < 2; ++u) *reinterpret_cast<bf16x8 *>(&Ws[buf][lds_off(srow + 128 * u, kc)]) = rw[set][u];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) *reinterpret_cast<bf16x8 *>(&Xs[buf][lds_off(srow + 64 * u, kc)]) = rx[set][u];
+    for (int u = 0; u < 2; ++u) *reinterpret_cast<bf16x8 *>(&Xs[buf][lds_off(srow + 128 * u, kc)]) = rx[set][u];
   };
 
   // acc[nb][mb]: token block nb (32 tokens) x feature block mb (32 features)
@@ -89,7 +94,7 @@ __global__ __launch_bounds__(256, 2) void produce_kernel(ProduceArgs a) {
         xf[nb] = *reinterpret_cast<const bf16x8 *>(&Xs[buf][lds_off(wave * 64 + nb * 32 + ln, ks * 2 + hh)]);
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
-        wf[mb] = *reinterpret_cast<const bf16x8 *>(&Ws[buf][lds_off(mb * 32 + ln, ks * 2 + hh)]);
+        wf[mb] = *reinterpret_cast<const bf16x8 *>(&Ws[buf][lds_off(hsel * kPD + mb * 32 + ln, ks * 2 + hh)]);
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -114,6 +119,7 @@ __global__ __launch_bounds__(256, 2) void produce_kernel(ProduceArgs a) {
   }
 
   // ---- epilogue: lane holds features mb*32 + (r/4)*8 + hh*4 + r%4 of token T
+  if (!head_ok) return;
   const int kind = head < a.Hq ? 0 : (head < a.Hq + a.Hkv ? 1 : 2);   // q, k, v
   constexpr double kTwoPi = 6.283185307179586476925;
 #pragma unroll
@@ -162,8 +168,8 @@ __global__ __launch_bounds__(256, 2) void produce_kernel(ProduceArgs a) {
 }  // namespace
 
 hipError_t launch_produce(const ProduceArgs &a, hipStream_t s) {
-  const dim3 grid((unsigned)(a.Hq + 2 * a.Hkv), (unsigned)cdiv((int64_t)a.B * a.q, kPTok));
-  hipLaunchKernelGGL(produce_kernel, grid, dim3(256), 0, s, a);
+  const dim3 grid((unsigned)cdiv(a.Hq + 2 * a.Hkv, 2), (unsigned)cdiv((int64_t)a.B * a.q, kPTok));
+  hipLaunchKernelGGL(produce_kernel, grid, dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

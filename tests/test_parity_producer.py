@@ -60,6 +60,7 @@ def _run(bd, X, W, rope_pos, dst_pos, Hq, Hkv, C, base=10000.0):
     (3, 40, 256, 8, 2, [0, 1000, 131000]),      # one ragged token tile, large positions
     (2, 200, 512, 4, 4, [17, 4096]),            # tiles spanning rows
     (5, 64, 128, 16, 2, [5, 9, 33, 70000, 1]),  # G = 8
+    (3, 40, 128, 1, 1, [2, 50, 7]),             # three heads: an odd head count
 ])
 def test_producer_small(bd, B, q, Dm, Hq, Hkv, rope_pos):
     note(f"producer B={B} q={q} Dm={Dm} Hq={Hq} Hkv={Hkv}")
