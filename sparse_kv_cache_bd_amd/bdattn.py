@@ -138,6 +138,26 @@ def _i32(t, name):
     return t
 
 
+def _buf(t, name, shape, dtype):
+    """An output or per-row buffer the C-ABI indexes as contiguous memory:
+    checked here so that a wrong shape raises instead of writing out of
+    bounds on the GPU."""
+    if t is None:
+        return None
+    t = _dev(t, name)
+    if t.dtype != dtype or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)}")
+    return t
+
+
+def _rows(t, name, B):
+    t = _i32(t, name)
+    if t.numel() < B:
+        raise ValueError(f"{name} must hold at least {B} entries")
+    return t
+
+
 def workspace(nbytes: int, device=None) -> torch.Tensor | None:
     """Caller-owned workspace (256-byte aligned: torch allocations are)."""
     if nbytes <= 0:
@@ -158,7 +178,7 @@ def kv_scatter(present_k, present_v, data_k, data_v, o, t: int, q: int, row_ids=
     if pv is not None and (pv.stride() != pk.stride() or dv.stride() != dk.stride()):
         raise ValueError("K and V tensors must share strides")
     L, B, Pcap, Hkv, d = pk.shape
-    o = _i32(o, "o")
+    o = _rows(o, "o", B)
     rid = _i32(row_ids, "row_ids") if row_ids is not None else None
     n_rows = B if rid is None else rid.numel()
     _check(lib().bd_kv_scatter(_DTYPE[pk.dtype], B, Hkv, d, q, L, _ptr(pk), _ptr(pv),
@@ -172,9 +192,11 @@ def gather(k_src, v_src, idx, k_cnt, k_pool, v_pool):
     vs, vp = _dev(v_src, "v_src"), _dev(v_pool, "v_pool")
     if vs is not None and (vs.stride() != ks.stride() or vp.stride() != kp.stride()):
         raise ValueError("K and V tensors must share strides")
-    idx = _i32(idx, "idx")
-    k_cnt = _i32(k_cnt, "k_cnt")
     B, S, Hkv, d = ks.shape
+    idx = _i32(idx, "idx")
+    if idx.dim() != 3 or tuple(idx.shape[:2]) != (B, Hkv):
+        raise ValueError(f"idx must be [{B}, {Hkv}, k_max]")
+    k_cnt = _rows(k_cnt, "k_cnt", B)
     k_max = idx.shape[2]
     _check(lib().bd_gather(_DTYPE[ks.dtype], B, Hkv, d, _ptr(ks), _ptr(vs), _strides(ks, 3), S,
                            _ptr(idx), k_max, _ptr(k_cnt), _ptr(kp), _ptr(vp), _strides(kp, 3),
@@ -191,9 +213,11 @@ def select(q, k, s_len, s_max: int, k_sel, k_max: int, sm_scale: float, rep_mode
     q, k = _dev(q, "q"), _dev(k, "k")
     B, nq, Hq, d = q.shape
     Hkv = k.shape[2]
-    s_len, k_sel = _i32(s_len, "s_len"), _i32(k_sel, "k_sel")
+    s_len, k_sel = _rows(s_len, "s_len", B), _rows(k_sel, "k_sel", B)
     if idx_out is None:
         idx_out = torch.empty((B, Hkv, k_max), dtype=torch.int32, device=q.device)
+    idx_out = _buf(idx_out, "idx_out", (B, Hkv, k_max), torch.int32)
+    score_out = _buf(score_out, "score_out", (B, Hkv, s_max), torch.float32)
     need = select_workspace_size(B, Hq, Hkv, d, s_max, k_max)
     if ws is None:
         ws = workspace(need, q.device)
@@ -215,9 +239,11 @@ def select_multi(q, k, s_len, s_max: int, k_sel, k_max: int, sm_scale: float, id
     q, k = _dev(q, "q"), _dev(k, "k")
     B, nq, Hq, d = q.shape
     Hkv = k.shape[2]
-    s_len, k_sel = _i32(s_len, "s_len"), _i32(k_sel, "k_sel")
+    s_len, k_sel = _rows(s_len, "s_len", B), _rows(k_sel, "k_sel", B)
     if idx_out is None:
         idx_out = torch.empty((B, Hkv, k_max), dtype=torch.int32, device=q.device)
+    idx_out = _buf(idx_out, "idx_out", (B, Hkv, k_max), torch.int32)
+    score_out = _buf(score_out, "score_out", (B, Hkv, s_max), torch.float32)
     need = select_multi_workspace_size(B, Hq, Hkv, d, nq, s_max, k_max)
     if ws is None:
         ws = workspace(need, q.device)
@@ -243,16 +269,17 @@ def attn_packed(q, pk, pv, p_len, p_max: int, wk, wv, bl: int, sm_scale: float, 
         raise ValueError("K and V tensors must share strides")
     B, nqry, Hq, d = q.shape
     Hkv = pk.shape[2]
-    p_len = _i32(p_len, "p_len")
+    p_len = _rows(p_len, "p_len", B)
     rid = _i32(row_ids, "row_ids") if row_ids is not None else None
     n_rows = B if rid is None else rid.numel()
     if out is None:
         out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q's shape and dtype")
     need = attn_workspace_size(q.dtype, B, Hq, Hkv, d, nqry, n_rows, p_max)
     if ws is None:
         ws = workspace(need, q.device)
-    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
-        raise ValueError("lse must be contiguous float32 [B, Hq, q]")
+    lse = _buf(lse, "lse", (B, Hq, nqry), torch.float32)
     tail = (_ptr(rid), n_rows, _ptr(q), _strides(q, 3), _ptr(pk), _ptr(pv), _strides(pk, 3),
             pk.shape[1], _ptr(p_len), p_max, _ptr(wk), _ptr(wv), _strides(wk, 3),
             float(sm_scale), _ptr(out), _strides(out, 3), _ptr(lse), _ptr(ws),
@@ -287,16 +314,17 @@ def attn_packed_dual(q, src_a, src_b, wk, wv, bl: int, sm_scale: float, out=None
         pk, pv = _dev(pk, "pk_" + tag), _dev(pv, "pv_" + tag)
         if pv.stride() != pk.stride():
             raise ValueError("K and V tensors must share strides")
-        srcs.append((_i32(rows, "rows_" + tag), pk, pv, _i32(p_len, "p_len_" + tag), int(p_max)))
+        srcs.append((_i32(rows, "rows_" + tag), pk, pv, _rows(p_len, "p_len_" + tag, B), int(p_max)))
     (ra, pka, pva, pla, pma), (rb, pkb, pvb, plb, pmb) = srcs
     Hkv = pka.shape[2]
     if out is None:
         out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q's shape and dtype")
     need = attn_dual_workspace_size(q.dtype, B, Hq, Hkv, d, nqry, ra.numel(), pma, rb.numel(), pmb)
     if ws is None:
         ws = workspace(need, q.device)
-    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
-        raise ValueError("lse must be contiguous float32 [B, Hq, q]")
+    lse = _buf(lse, "lse", (B, Hq, nqry), torch.float32)
     _check(lib().bd_attn_packed_dual(
         _DTYPE[q.dtype], B, Hq, Hkv, d, nqry, bl, _ptr(q), _strides(q, 3),
         _ptr(ra), ra.numel(), _ptr(pka), _ptr(pva), _strides(pka, 3), pka.shape[1], _ptr(pla), pma,
@@ -319,7 +347,14 @@ def qkv_rope_write(x, w, rope_pos, Hq: int, Hkv: int, q_out, k_cache, v_cache, d
         raise ValueError("w must be contiguous")
     B, nq, Dm = x.shape
     d = q_out.shape[3]
-    rope_pos, dst_pos = _i32(rope_pos, "rope_pos"), _i32(dst_pos, "dst_pos")
+    if tuple(w.shape) != ((Hq + 2 * Hkv) * d, Dm):
+        raise ValueError(f"w must be [{(Hq + 2 * Hkv) * d}, {Dm}]")
+    if tuple(q_out.shape) != (B, nq, Hq, d):
+        raise ValueError(f"q_out must be [{B}, {nq}, {Hq}, {d}]")
+    if k_cache.dim() != 4 or k_cache.shape[0] != B or tuple(k_cache.shape[2:]) != (Hkv, d) or \
+            k_cache.shape != v_cache.shape:
+        raise ValueError(f"k_cache / v_cache must be [{B}, C, {Hkv}, {d}]")
+    rope_pos, dst_pos = _rows(rope_pos, "rope_pos", B), _rows(dst_pos, "dst_pos", B)
     _check(lib().bd_qkv_rope_write(_DTYPE[x.dtype], B, nq, Dm, Hq, Hkv, d, _ptr(x), _strides(x, 2),
                                    _ptr(w), _ptr(rope_pos), float(rope_base), _ptr(q_out),
                                    _strides(q_out, 3), _ptr(k_cache), _ptr(v_cache),
@@ -328,7 +363,7 @@ def qkv_rope_write(x, w, rope_pos, Hq: int, Hkv: int, q_out, k_cache, v_cache, d
 
 
 def mask_materialize(B: int, C: int, q: int, bl: int, o, mask_mode: str = "block_causal"):
-    o = _i32(o, "o")
+    o = _rows(o, "o", B)
     out = torch.empty((B, q, C), dtype=torch.uint8, device=o.device)
     _check(lib().bd_mask_materialize(B, C, q, bl, MASK_MODES[mask_mode], _ptr(o), _ptr(out),
                                      _stream()))
