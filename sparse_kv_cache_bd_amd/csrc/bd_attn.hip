@@ -483,49 +483,50 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int64_t group = unit / a.nqt;
   const int rl = (int)(group / a.Hkv);
   const int h = (int)(group - (int64_t)rl * a.Hkv);
-  const RowRef rr = row_ref(a, rl);
-  const int b = rr.b;
-  if (b < 0 || b >= a.B) return;
-  const int P = prefix_len(a, rr);
-  const int nc = P > 0 ? (int)cdiv(P, a.chunk) : 1;
-  if (nc == 1) return;  // written directly by the attention kernel
   const int cg = col / 32;
   const int g = cg / S::QB;
   const int qb = cg - g * S::QB;
   const int qi = u * S::NQ + qb * 32 + (col & 31);
   if (qi >= a.q) return;
   const int64_t prow0 = unit * a.n_split * S::NCOL + col;
-  // the partials of 8 chunks are loaded together (8 loads in flight), then
-  // merged in chunk order
+  // the partials of the first U chunks are requested before the row lookup
+  // (row id, then prefix length), so the two latencies overlap; chunks past
+  // the row's count hold stale data and are never used
   constexpr int U = 8;
-  float M = -INFINITY;
-  for (int c0 = 0; c0 < nc; c0 += U) {
-    float mu[U];
+  float2 ml[U];
+  f32x4 po[U];
+  auto load = [&](int c0, int lim) {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      mu[u] = c0 + u < nc ? a.part_ml[(prow0 + (int64_t)(c0 + u) * S::NCOL) * 2] : -INFINITY;
-#pragma unroll
-    for (int u = 0; u < U; ++u) M = fmaxf(M, mu[u]);
-  }
-  float L = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int c0 = 0; c0 < nc; c0 += U) {
-    float2 ml[U];
-    f32x4 po[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (c0 + u < nc) {
-        const int64_t prow = prow0 + (int64_t)(c0 + u) * S::NCOL;
-        ml[u] = *reinterpret_cast<const float2 *>(a.part_ml + prow * 2);
-        po[u] = *reinterpret_cast<const f32x4 *>(a.part_o + prow * kD + d4 * 4);
+    for (int v = 0; v < U; ++v) {
+      if (c0 + v < lim) {
+        const int64_t prow = prow0 + (int64_t)(c0 + v) * S::NCOL;
+        ml[v] = *reinterpret_cast<const float2 *>(a.part_ml + prow * 2);
+        po[v] = *reinterpret_cast<const f32x4 *>(a.part_o + prow * kD + d4 * 4);
       }
     }
+  };
+  load(0, a.n_split);
+  const RowRef rr = row_ref(a, rl);
+  const int b = rr.b;
+  if (b < 0 || b >= a.B) return;
+  const int P = prefix_len(a, rr);
+  const int nc = P > 0 ? (int)cdiv(P, a.chunk) : 1;
+  if (nc == 1) return;  // written directly by the attention kernel
+  // online merge in chunk order (every chunk holds visible prefix keys, so
+  // each partial max is finite)
+  float M = -INFINITY, L = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < nc; c0 += U) {
+    if (c0 > 0) load(c0, nc);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (c0 + u < nc) {
-        const float w = __builtin_amdgcn_exp2f(ml[u].x - M);
-        L += ml[u].y * w;
-        acc += po[u] * w;
+    for (int v = 0; v < U; ++v) {
+      if (c0 + v < nc) {
+        const float mn = fmaxf(M, ml[v].x);
+        const float sa = __builtin_amdgcn_exp2f(M - mn);
+        const float sb = __builtin_amdgcn_exp2f(ml[v].x - mn);
+        L = L * sa + ml[v].y * sb;
+        acc = acc * sa + po[v] * sb;
+        M = mn;
       }
     }
   }
