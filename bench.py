@@ -56,9 +56,18 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def attention_flops(p_len, rows, q, bl, Hq, d):
+def window_keys(i, q, bl, mode="block_causal"):
+    """Window keys query i sees under each window mask."""
+    lim = min(q, (i // bl + 1) * bl)
+    if mode == "block_causal":
+        return lim
+    own = lim - (i // bl) * bl
+    return own if (mode == "isolated" or i < bl) else own + bl
+
+
+def attention_flops(p_len, rows, q, bl, Hq, d, mode="block_causal"):
     """4*d FLOPs per visible (query, key) pair per query head."""
-    win = sum(min(q, (i // bl + 1) * bl) for i in range(q))
+    win = sum(window_keys(i, q, bl, mode) for i in range(q))
     return sum(4 * d * Hq * (q * int(p_len[b]) + win) for b in rows)
 
 
@@ -288,6 +297,17 @@ def bench_configs(dev, reps: int = 10):
         step = BlockDiffusionStep(Kc, Vc, Q, o, wl.bl, wl.sm_scale, p_max_dense=int(wl.o.max()))
         ms_a = time_calls(step.attn_dense, reps)
         ms_s = time_calls(step.scatter, reps)
+        # the other window masks on the same rows (HERALD's isolated
+        # draft/denoise groups; Flash-dLLM's verify views)
+        modes = {}
+        if wl.W > 1:
+            for mode in ("isolated", "shared_first"):
+                out_m = torch.empty_like(Q)
+                fm = lambda: bd.attn_packed(Q, Kc, Vc, o, int(wl.o.max()), step.wk, step.wv, wl.bl,
+                                            wl.sm_scale, out=out_m, ws=step.ws_dense, mask_mode=mode)
+                ms_m = time_calls(fm, reps)
+                fl = attention_flops(wl.o, range(wl.B), wl.q, wl.bl, wl.Hq, wl.d, mode)
+                modes[mode] = {"us": round(ms_m * 1e3, 2), "TFLOP/s": _rate(fl, ms_m, 1e12)}
         ms_ac, q_ac = cold(step.attn_dense)
         ms_sc, q_sc = cold(step.scatter)
         flop = attention_flops(wl.o, range(wl.B), wl.q, wl.bl, wl.Hq, wl.d)
@@ -305,6 +325,8 @@ def bench_configs(dev, reps: int = 10):
                      "attainable_TFLOP/s": round(att, 1),
                      "scatter_us": round(ms_s * 1e3, 2), "scatter_GB/s": _rate(sbytes, ms_s, 1e9),
                      "scatter_cold_us": q_sc, "scatter_cold_GB/s": _rate(sbytes, ms_sc, 1e9)}
+        if modes:
+            out[name]["attn_other_masks"] = modes
         del step, Kc, Vc, Q, o
 
     for name in ("sparse_32k", "sparse_128k"):
@@ -335,6 +357,17 @@ def bench_configs(dev, reps: int = 10):
                 bd.attn_packed(steps_q[st], pool_k, pool_v, k_sel, k_max, wk, wv, wl.bl,
                                wl.sm_scale, out=outb, ws=ws_a)
         ms_att = time_calls(steps, max(2, reps // 2))
+        # the same T steps captured once in a HIP graph and replayed (the
+        # step kernels are short: launch gaps are a visible share)
+        graph = torch.cuda.CUDAGraph()
+        steps()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            steps()
+        graph.replay()
+        torch.cuda.synchronize()
+        ms_att_graph = time_calls(graph.replay, max(2, reps // 2))
+        del graph
         wk0, wv0 = steps_kv[0]
         ms_attc, q_attc = cold(lambda: bd.attn_packed(steps_q[0], pool_k, pool_v, k_sel, k_max, wk0, wv0,
                                                       wl.bl, wl.sm_scale, out=outb, ws=ws_a))
@@ -364,6 +397,7 @@ def bench_configs(dev, reps: int = 10):
                      "gather_us": round(ms_gat * 1e3, 2), "gather_GB/s": _rate(gat_bytes, ms_gat, 1e9),
                      "gather_cold_us": q_gatc, "gather_cold_GB/s": _rate(gat_bytes, ms_gatc, 1e9),
                      "attn_us_per_step": round(ms_att * 1e3 / wl.T, 2),
+                     "attn_us_per_step_graph": round(ms_att_graph * 1e3 / wl.T, 2),
                      "attn_TFLOP/s": _rate(flop, ms_att, 1e12),
                      "attn_cold_us_per_step": q_attc,
                      "attn_cold_frac_attainable": round(flop1 / (ms_attc * 1e-3) / 1e12 / att, 4),

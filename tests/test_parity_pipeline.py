@@ -56,3 +56,44 @@ def test_overlapped_equals_sequential(bd, T, n_blocks):
     ref, _ = orc.block_attention(wl.extra["step_q"][T - 1], seq.pools[last][0].cpu(),
                                  seq.pools[last][1].cpu(), wl.k_sel, wk, wv, wl.bl, wl.sm_scale)
     check_attention(out_s, ref, torch.bfloat16, label="pipeline")
+
+
+def test_denoising_steps_in_a_hip_graph(bd):
+    """The T denoising attentions over one pool captured in a HIP graph: every
+    replay (with eager work and synchronisations between replays) gives the
+    eager outputs bit for bit."""
+    note("denoising steps in a HIP graph")
+    wl = synth.sparse_32k(B=2, S=8192, T=3)
+    Kc, Vc = wl.Kc.cuda(), wl.Vc.cuda()
+    idx = bd.select(wl.Qsel.cuda(), Kc, wl.s_len.cuda(), wl.s_max, wl.k_sel.cuda(), wl.k_max,
+                    wl.sm_scale)
+    pk = torch.zeros((wl.B, wl.k_max, wl.Hkv, wl.d), dtype=torch.bfloat16, device="cuda")
+    pv = torch.zeros_like(pk)
+    k_sel = wl.k_sel.cuda()
+    bd.gather(Kc, Vc, idx, k_sel, pk, pv)
+    steps_q = [x.cuda() for x in wl.extra["step_q"]]
+    steps_kv = [(a.cuda(), b.cuda()) for a, b in wl.extra["step_kv"]]
+    outs = [torch.empty_like(steps_q[0]) for _ in range(wl.T)]
+    ws = bd.workspace(bd.attn_workspace_size(torch.bfloat16, wl.B, wl.Hq, wl.Hkv, wl.d, wl.q,
+                                             wl.B, wl.k_max), "cuda")
+
+    def steps():
+        for st in range(wl.T):
+            wk, wv = steps_kv[st]
+            bd.attn_packed(steps_q[st], pk, pv, k_sel, wl.k_max, wk, wv, wl.bl, wl.sm_scale,
+                           out=outs[st], ws=ws)
+    steps()
+    torch.cuda.synchronize()
+    want = [o.clone() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        steps()
+    for rep in range(3):
+        for o in outs:
+            o.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for st in range(wl.T):
+            assert torch.equal(outs[st], want[st]), f"replay {rep}, step {st}"
+        bd.select(wl.Qsel.cuda(), Kc, wl.s_len.cuda(), wl.s_max, k_sel, wl.k_max, wl.sm_scale)
