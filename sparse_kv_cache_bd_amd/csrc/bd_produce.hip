@@ -4,18 +4,19 @@
 // FlowBlock's packed windows use absolute positions), and the write of keys
 // and values into the cache, with no intermediate tensor in HBM.
 //
-// One block computes one head (128 output features) for 256 window tokens:
-// Y^T = W_head X^T with v_mfma_f32_32x32x16_bf16, features on M and tokens
-// on N, so a lane ends with 16 features of one token; dimension j and its
-// rotary partner j + 64 sit in the same lane and register (M blocks mb and
-// mb + 2).  Eight waves each own 32 tokens and all 128 features; two
-// blocks share a CU.  Tiles of 32 hidden elements of W and X are
+// One block computes two heads (2 x 128 output features) for 256 window
+// tokens: Y^T = W_head X^T with v_mfma_f32_32x32x16_bf16, features on M and
+// tokens on N, so a lane ends with 16 features of one token; dimension j and
+// its rotary partner j + 64 sit in the same lane and register (M blocks mb
+// and mb + 2).  Eight waves: four per head, each owning 64 tokens and the
+// head's 128 features (8 MFMAs per 6 fragment reads); every staged X tile
+// feeds both heads.  Tiles of 32 hidden elements of W and X are
 // double-buffered in LDS and staged through two register sets, so a tile's
-// global loads have two tiles of MFMAs to land; one barrier per tile.  The rotation angle is formed and
-// reduced to [-pi, pi] in double precision (positions reach 1e5 and more;
-// the inverse frequencies come from the host in double), its sine and cosine
-// taken in fp32 and applied to the fp32 accumulators; results are rounded to
-// bf16 once.
+// global loads have two tiles of MFMAs to land; one barrier per tile.  The
+// rotation angle is formed and reduced to [-pi, pi] in double precision
+// (positions reach 1e5 and more; the inverse frequencies come from the host
+// in double), its sine and cosine taken in fp32 and applied to the fp32
+// accumulators; results are rounded to bf16 once.
 #include "bd_common.h"
 
 namespace bd {
@@ -46,8 +47,9 @@ __global__ __launch_bounds__(512, 1) void produce_kernel(ProduceArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 Xs[2][kPTok * kPStr];
 
   // staging: piece p of a tile is row p / 4, 16-byte chunk p % 4; a thread
-  // stages W rows tid/4 + 64 u (u < 2) and X rows tid/4 + 64 u (u < 4);
-  // tokens past the end re-read the last token (their results are not stored)
+  // stages W rows tid/4 and tid/4 + 128 (the pair's two heads) and X rows
+  // tid/4 and tid/4 + 128; tokens past the end re-read the last token (their
+  // results are not stored)
   const int srow = tid >> 2, kc = tid & 3, kq = kc * 8;   // srow < 128
   // W rows srow and srow + 128 of the pair's 256 (a missing second head
   // re-reads the last head; its results are not stored)
