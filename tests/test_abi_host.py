@@ -327,3 +327,47 @@ def _produce(L, **kw):
 ])
 def test_producer_validation(L, kw, code):
     assert _produce(L, **kw) == code
+
+
+def test_plain_c_client(tmp_path):
+    """The public header is plain C: a C99 program includes it, links the
+    library and gets the documented status codes from host-side validation
+    (no kernel launches)."""
+    import os
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    inc = os.path.dirname(bd.HEADER_PATH)
+    libdir = os.path.dirname(bd.LIB_PATH)
+    src = tmp_path / "client.c"
+    src.write_text(r"""
+#include <stdio.h>
+#include <string.h>
+#include "bdattn.h"
+int main(void) {
+  int64_t s3[3] = {0, 0, 0};
+  if (strncmp(bd_version(), "libbdattn", 9) != 0) return 10;
+  /* unknown dtype: unsupported, before any device work */
+  if (bd_select(7, 1, 8, 2, 128, 0, s3, 1, BD_REP_MEAN, 0, 0, s3, 0, 0, 0, 0, 1, 0.1f, 0, 0, 0, 0,
+                0) != BD_ERR_UNSUPPORTED) return 11;
+  if (strlen(bd_last_error()) == 0) return 12;
+  /* unknown mask mode */
+  if (bd_attn_packed_masked(BD_BF16, 1, 8, 2, 128, 32, 32, 9, 0, 1, 0, s3, 0, 0, s3, 0, 0, 0, 0, 0,
+                            s3, 0.1f, 0, s3, 0, 0, 0, 0) != BD_ERR_INVALID_ARG) return 13;
+  /* empty calls succeed */
+  if (bd_gather(BD_BF16, 0, 8, 128, 0, 0, s3, 0, 0, 0, 0, 0, 0, s3, 0, 0) != BD_OK) return 14;
+  if (bd_qkv_rope_write(BD_BF16, 0, 32, 128, 4, 2, 128, 0, 0, 0, 0, 10000.f, 0, 0, 0, 0, 0, 0, 0,
+                        0) != BD_OK) return 15;
+  printf("ok\n");
+  return 0;
+}
+""")
+    exe = tmp_path / "client"
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-I", inc, str(src), "-L", libdir,
+                        "-lbdattn", f"-Wl,-rpath,{libdir}", "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", (r.returncode, r.stdout, r.stderr)
