@@ -444,31 +444,43 @@ __global__ __launch_bounds__(kThreads) void sel_score_kernel(SelectArgs a, SelPt
 // of 256 or 1024 threads.
 __device__ inline void find_digit(const uint32_t *cnt_of, int nb, uint32_t krem, int *sh,
                                   uint32_t &D, uint32_t &rem) {
+  (void)sh;
+  // wave 0 alone: lane l sums bins nb-1-l*per .. down (per = nb/64, all its
+  // loads in flight), one wave-level inclusive scan from the highest bins,
+  // and the one lane whose range holds the krem-th count walks its bins
   __shared__ uint32_t sd[2];
-  if (threadIdx.x == 0) {
-    sd[0] = 0;
-    sd[1] = krem;
-  }
-  const int per = nb / (int)blockDim.x;  // 1 to 8 bins per thread, descending
-  const int hi_bin = nb - 1 - threadIdx.x * per;
-  uint32_t cnt[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-  int tsum = 0;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    if (lane == 0) {
+      sd[0] = 0;
+      sd[1] = krem;
+    }
+    const int per = nb >> 6;   // 32 or 16 bins per lane, descending
+    const int hi_bin = nb - 1 - lane * per;
+    uint32_t cnt[32];
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
-    if (e < per) cnt[e] = cnt_of[hi_bin - e];
+    for (int e = 0; e < 32; ++e) cnt[e] = e < per ? cnt_of[hi_bin - e] : 0u;
+    uint32_t tsum = 0;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) tsum += (int)cnt[e];
-  int total;
-  const int before = block_excl_scan(tsum, sh, total);
-  if ((uint32_t)before < krem && krem <= (uint32_t)(before + tsum)) {
-    uint32_t cum = (uint32_t)before;
-    for (int e = 0; e < per; ++e) {
-      if (cum + cnt[e] >= krem) {
-        sd[0] = (uint32_t)(hi_bin - e);
-        sd[1] = krem - cum;
-        break;
+    for (int e = 0; e < 32; ++e) tsum += cnt[e];
+    uint32_t x = tsum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    const uint32_t before = x - tsum;
+    if (before < krem && krem <= x) {
+      uint32_t cum = before;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        if (e < per && cum + cnt[e] >= krem) {
+          sd[0] = (uint32_t)(hi_bin - e);
+          sd[1] = krem - cum;
+          break;
+        }
+        cum += cnt[e];
       }
-      cum += cnt[e];
     }
   }
   __syncthreads();
