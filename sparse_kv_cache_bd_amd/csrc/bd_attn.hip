@@ -450,17 +450,20 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
     if (a.lse && hh == 0)
       a.lse[((int64_t)b * a.Hq + hq) * a.q + qi] = (m_run + __log2f(l_run)) * kLn2;
   } else {
-    // partial rows [unit][chunk][column], unit = (natural row, KV head, query tile)
+    // partials [unit][chunk][column], unit = (natural row, KV head, query
+    // tile).  O of a 32-column group is stored as [dims / 4][column][4]:
+    // lane l's store s (dims 8s + 4hh ..) lands at float (64s + l) * 4, so
+    // each store instruction writes 1 KB contiguous.
     const int64_t unit = ((int64_t)it.rl * a.Hkv + h) * a.nqt + it.u;
     const int col = wave * 32 + ln;
     const int64_t prow = (unit * a.n_split + it.c) * S::NCOL + col;
-    float *po = a.part_o + prow * kD;
+    float *po = a.part_o + (prow - ln) * kD + lane * 4;
 #pragma unroll
     for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
         f32x4 w = {acc[dt][rq * 4 + 0], acc[dt][rq * 4 + 1], acc[dt][rq * 4 + 2], acc[dt][rq * 4 + 3]};
-        *reinterpret_cast<f32x4 *>(po + dt * 32 + rq * 8 + hh * 4) = w;
+        *reinterpret_cast<f32x4 *>(po + (dt * 4 + rq) * 256) = w;
       }
     if (hh == 0) {
       a.part_ml[prow * 2 + 0] = m_run;
@@ -470,15 +473,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
 }
 
 // Merge the split-KV partials: one thread per (column, 4 dims), chunks in a
-// fixed order, so the result does not depend on scheduling.
+// fixed order, so the result does not depend on scheduling.  Eight
+// consecutive threads take eight consecutive columns of the same 4 dims: in
+// the partials' [dims / 4][column][4] order of a column group they read one
+// 128-byte line.
 template <int NW, int G>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   using S = Shape<NW, G>;
   constexpr int CPB = 256 / (kD / 4);  // columns per block: 8
   const int blocks_per_unit = S::NCOL / CPB;
   const int64_t unit = blockIdx.x / blocks_per_unit;
-  const int col = (blockIdx.x - unit * blocks_per_unit) * CPB + threadIdx.x / (kD / 4);
-  const int d4 = threadIdx.x % (kD / 4);
+  const int col = (blockIdx.x - unit * blocks_per_unit) * CPB + (threadIdx.x & (CPB - 1));
+  const int d4 = threadIdx.x / CPB;
   const int u = (int)(unit % a.nqt);
   const int64_t group = unit / a.nqt;
   const int rl = (int)(group / a.Hkv);
@@ -501,7 +507,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
       if (c0 + v < lim) {
         const int64_t prow = prow0 + (int64_t)(c0 + v) * S::NCOL;
         ml[v] = *reinterpret_cast<const float2 *>(a.part_ml + prow * 2);
-        po[v] = *reinterpret_cast<const f32x4 *>(a.part_o + prow * kD + d4 * 4);
+        po[v] = *reinterpret_cast<const f32x4 *>(a.part_o + (prow - (col & 31)) * kD + (d4 * 32 + (col & 31)) * 4);
       }
     }
   };
