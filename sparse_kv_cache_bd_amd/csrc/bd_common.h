@@ -119,7 +119,7 @@ struct AttnArgs {
   int p_cap2, p_max2;
   float scale2;  // sm_scale * log2(e)
   // launch plan (attn_plan)
-  int nw;                 // waves per block of the MFMA path (2 or 4)
+  int nw;                 // waves per block of the MFMA path (4 or 8)
   int nqt, chunk, n_split;
   int *row_order;         // rows by descending prefix length, or NULL (natural order)
   float *part_o, *part_ml;
