@@ -477,7 +477,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
 // consecutive threads take eight consecutive columns of the same 4 dims: in
 // the partials' [dims / 4][column][4] order of a column group they read one
 // 128-byte line.
-template <int NW, int G>
+// U: partials requested per round of loads (8, or 32 for long chunk lists).
+template <int NW, int G, int U>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   using S = Shape<NW, G>;
   constexpr int CPB = 256 / (kD / 4);  // columns per block: 8
@@ -498,7 +499,6 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   // the partials of the first U chunks are requested before the row lookup
   // (row id, then prefix length), so the two latencies overlap; chunks past
   // the row's count hold stale data and are never used
-  constexpr int U = 8;
   float2 ml[U];
   f32x4 po[U];
   auto load = [&](int c0, int lim) {
@@ -778,7 +778,12 @@ static hipError_t launch_mfma(const AttnArgs &a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split <= 1) return e;
   const int64_t cgrid = n_groups * a.nqt * (S::NCOL / 8);
-  hipLaunchKernelGGL((attn_combine_kernel<NW, G>), dim3((unsigned)cgrid), dim3(256), 0, s, a);
+  // one round of loads covers up to 8 chunks; longer lists (pools of
+  // thousands of keys) take 32 per round, fewer dependent round trips
+  if (a.n_split > 8)
+    hipLaunchKernelGGL((attn_combine_kernel<NW, G, 32>), dim3((unsigned)cgrid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_combine_kernel<NW, G, 8>), dim3((unsigned)cgrid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
