@@ -571,7 +571,10 @@ __global__ __launch_bounds__(1024) void attn_order_kernel(AttnArgs a) {
 
 // -------------------------------------------------------------- general path
 // One block per (row, query head, 32-query tile); 8 lanes per query, each
-// lane owning D/8 dimensions.  fp32 arithmetic throughout; used for fp32
+// lane owning D/8 dimensions.  Keys are handled in batches of 8: each lane
+// forms its partial dot products for the 8 keys (independent chains), the 8
+// lanes add them (three butterfly steps per key, the 8 keys interleaved), and
+// the running max and O are updated once per batch.  fp32 arithmetic throughout; used for fp32
 // inputs and for shapes the MFMA path is not built for.
 constexpr int kGenKeys = 32;
 constexpr int kQT = 32;  // queries per block
@@ -580,8 +583,9 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a) {
   constexpr int DL = D / 8;  // dims per lane
   constexpr int EPT = kGenKeys * D / 256;  // tile elements staged per thread
-  __shared__ float Kt[2][kGenKeys][D + 1];
-  __shared__ float Vt_[2][kGenKeys][D + 1];
+  constexpr int KS = D + 4;  // LDS row stride (floats), 16-byte aligned rows
+  __shared__ __attribute__((aligned(16))) float Kt[2][kGenKeys][KS];
+  __shared__ __attribute__((aligned(16))) float Vt_[2][kGenKeys][KS];
   const int tid = threadIdx.x;
   const int ql = tid >> 3;   // query inside tile
   const int sub = tid & 7;   // dimension slice
@@ -663,25 +667,63 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a) {
     const bool win = tile >= npt;
     const int base = win ? (tile - npt) * kGenKeys : tile * kGenKeys;
     const int limit = win ? win_len : P;
-    const int vlim = win ? lim_i : limit;
-    const int nk = min(kGenKeys, limit - base);
-    for (int key = 0; key < nk; ++key) {
-      float dot = 0.f;
+    const int vlim = win ? lim_i : limit;   // keys at or past vlim are not visible
+    // the tile in groups of 8 keys (a runtime loop bounds the registers the
+    // scheduler can fill with LDS reads): scores of the group's keys, every
+    // lane of the query holding all 8
+#pragma unroll 1
+    for (int k0 = 0; k0 < kGenKeys; k0 += 8) {
+      float sc[8];
 #pragma unroll
-      for (int e = 0; e < DL; ++e) dot += qv[e] * Kt[buf][key][sub * DL + e];
-      dot += __shfl_xor(dot, 1);
-      dot += __shfl_xor(dot, 2);
-      dot += __shfl_xor(dot, 4);
-      if (base + key >= vlim) continue;  // uniform over the 8 lanes of a query
-      if (win && base + key < w_floor && base + key >= w_shared) continue;
-      const float sc = dot * a.scale2;
-      const float m_new = fmaxf(m_run, sc);
-      const float alpha = exp2f(m_run - m_new);
-      const float p = exp2f(sc - m_new);
-      l_run = l_run * alpha + p;
+      for (int kk = 0; kk < 8; ++kk) {
+        const float *kr = &Kt[buf][k0 + kk][sub * DL];
+        float dot = 0.f;
 #pragma unroll
-      for (int e = 0; e < DL; ++e) o[e] = o[e] * alpha + p * Vt_[buf][key][sub * DL + e];
-      m_run = m_new;
+        for (int e = 0; e < DL; e += 4) {
+          const f32x4 kv = *reinterpret_cast<const f32x4 *>(kr + e);
+          dot = fmaf(qv[e + 0], kv[0], dot);
+          dot = fmaf(qv[e + 1], kv[1], dot);
+          dot = fmaf(qv[e + 2], kv[2], dot);
+          dot = fmaf(qv[e + 3], kv[3], dot);
+        }
+        sc[kk] = dot;
+      }
+      float gmax = -INFINITY;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        float dot = sc[kk];
+        dot += __shfl_xor(dot, 1);
+        dot += __shfl_xor(dot, 2);
+        dot += __shfl_xor(dot, 4);
+        const int key = base + k0 + kk;
+        bool vis = key < vlim;
+        if (win && key < w_floor && key >= w_shared) vis = false;
+        sc[kk] = vis ? dot * a.scale2 : -INFINITY;
+        gmax = fmaxf(gmax, sc[kk]);
+      }
+      if (gmax > m_run) {
+        // m_run = -inf gives alpha = 0 on an all-zero O and sum
+        const float alpha = __builtin_amdgcn_exp2f(m_run - gmax);
+        l_run *= alpha;
+#pragma unroll
+        for (int e = 0; e < DL; ++e) o[e] *= alpha;
+        m_run = gmax;
+      }
+      const float mref = m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const float p = __builtin_amdgcn_exp2f(sc[kk] - mref);
+        l_run += p;
+        const float *vr = &Vt_[buf][k0 + kk][sub * DL];
+#pragma unroll
+        for (int e = 0; e < DL; e += 4) {
+          const f32x4 vv = *reinterpret_cast<const f32x4 *>(vr + e);
+          o[e + 0] = fmaf(p, vv[0], o[e + 0]);
+          o[e + 1] = fmaf(p, vv[1], o[e + 1]);
+          o[e + 2] = fmaf(p, vv[2], o[e + 2]);
+          o[e + 3] = fmaf(p, vv[3], o[e + 3]);
+        }
+      }
     }
     if (tile + 1 < ntile) lstore(buf ^ 1);
     __syncthreads();
