@@ -168,6 +168,32 @@ def test_pool_form_with_nan_past_budget(bd):
     check_attention(out, ref, torch.bfloat16, label="pool")
 
 
+def test_pool_long_ragged_combine_rounds(bd):
+    """Pool rows of 16000 and 5000 keys with 4 KV heads and q = 32: the plan
+    cuts them into 256-key chunks (63 and 20), so the combine takes its
+    32-partials-per-round form, in two rounds for the long row and one
+    partly filled round for the short one."""
+    note("attn pool long ragged combine rounds")
+    rs = np.random.default_rng(33)
+    B, Hkv, G, d, bl, W = 2, 4, 4, 128, 32, 1
+    q = W * bl
+    kb = [16000, 5000]
+    kmax = max(kb)
+    PK, PV = _pool_case(rs, B, kmax + 8, Hkv, d, kb, torch.bfloat16)
+    wk = torch.from_numpy(rs.standard_normal((B, q, Hkv, d)).astype(np.float32) / math.sqrt(d)).bfloat16()
+    wv = torch.from_numpy(rs.standard_normal((B, q, Hkv, d)).astype(np.float32) / math.sqrt(d)).bfloat16()
+    Q = torch.from_numpy(rs.standard_normal((B, q, G * Hkv, d)).astype(np.float32) / math.sqrt(d)).bfloat16()
+    need = bd.attn_workspace_size(torch.bfloat16, B, G * Hkv, Hkv, d, q, B, kmax)
+    assert need >= B * Hkv * 63 * 128 * d * 4, "plan does not split into 256-key chunks"
+    L = torch.full((B, G * Hkv, q), 5.0, device="cuda")
+    out = bd.attn_packed(Q.cuda(), PK.cuda(), PV.cuda(), torch.tensor(kb, dtype=torch.int32).cuda(), kmax,
+                         wk.cuda(), wv.cuda(), bl, 1.0 / math.sqrt(d), lse=L)
+    torch.cuda.synchronize()
+    ref, ref_lse = orc.block_attention(Q, PK, PV, kb, wk, wv, bl, 1.0 / math.sqrt(d))
+    check_attention(out, ref, torch.bfloat16, label="pool rounds")
+    np.testing.assert_allclose(L.cpu().numpy(), ref_lse, atol=2e-3, rtol=1e-3)
+
+
 @pytest.mark.parametrize("d,G", [(64, 1), (128, 4), (64, 2)])
 def test_fp32_general_path(bd, d, G):
     note(f"attn fp32 d={d} G={G}")
