@@ -574,19 +574,23 @@ __global__ __launch_bounds__(1024) void attn_order_kernel(AttnArgs a) {
 // lane owning D/8 dimensions.  Keys are handled in batches of 8: each lane
 // forms its partial dot products for the 8 keys (independent chains), the 8
 // lanes add them (three butterfly steps per key, the 8 keys interleaved), and
-// the running max and O are updated once per batch.  fp32 arithmetic throughout; used for fp32
+// the running max and O are updated once per batch.  KG key groups of 256
+// threads (launches with fewer blocks than CUs) take tiles kg, kg + KG, ...
+// in lockstep with their own LDS buffers and hand (max, sum, O) to group 0
+// through LDS at the end.  fp32 arithmetic throughout; used for fp32
 // inputs and for shapes the MFMA path is not built for.
 constexpr int kGenKeys = 32;
 constexpr int kQT = 32;  // queries per block
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a) {
+template <typename T, int D, int KG>
+__global__ __launch_bounds__(256 * KG) void attn_generic_kernel(AttnArgs a) {
   constexpr int DL = D / 8;  // dims per lane
   constexpr int EPT = kGenKeys * D / 256;  // tile elements staged per thread
   constexpr int KS = D + 4;  // LDS row stride (floats), 16-byte aligned rows
-  __shared__ __attribute__((aligned(16))) float Kt[2][kGenKeys][KS];
-  __shared__ __attribute__((aligned(16))) float Vt_[2][kGenKeys][KS];
-  const int tid = threadIdx.x;
+  __shared__ __attribute__((aligned(16))) float Kt[KG][2][kGenKeys][KS];
+  __shared__ __attribute__((aligned(16))) float Vt_[KG][2][kGenKeys][KS];
+  const int kg = KG > 1 ? (int)(threadIdx.x >> 8) : 0;  // key group
+  const int tid = threadIdx.x & 255;
   const int ql = tid >> 3;   // query inside tile
   const int sub = tid & 7;   // dimension slice
   const int nqt = a.nqt;
@@ -652,18 +656,22 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a) {
     for (int i = 0; i < EPT; ++i) {
       const int e = tid + 256 * i;
       const int key = e / D, dd = e - key * D;
-      Kt[buf][key][dd] = kreg[i];
-      Vt_[buf][key][dd] = vreg[i];
+      Kt[kg][buf][key][dd] = kreg[i];
+      Vt_[kg][buf][key][dd] = vreg[i];
     }
   };
-  if (ntile > 0) {
-    gload(0);
+  if (kg < ntile) {
+    gload(kg);
     lstore(0);
   }
   __syncthreads();
-  for (int tile = 0; tile < ntile; ++tile) {
-    const int buf = tile & 1;
-    if (tile + 1 < ntile) gload(tile + 1);
+  const int n_steps = (int)cdiv(ntile, KG);
+  for (int step = 0; step < n_steps; ++step) {
+    const int tile = step * KG + kg;
+    const int buf = step & 1;
+    const bool more = tile + KG < ntile;
+    if (more) gload(tile + KG);
+    if (tile < ntile) {
     const bool win = tile >= npt;
     const int base = win ? (tile - npt) * kGenKeys : tile * kGenKeys;
     const int limit = win ? win_len : P;
@@ -676,7 +684,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a) {
       float sc[8];
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        const float *kr = &Kt[buf][k0 + kk][sub * DL];
+        const float *kr = &Kt[kg][buf][k0 + kk][sub * DL];
         float dot = 0.f;
 #pragma unroll
         for (int e = 0; e < DL; e += 4) {
@@ -714,7 +722,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a) {
       for (int kk = 0; kk < 8; ++kk) {
         const float p = __builtin_amdgcn_exp2f(sc[kk] - mref);
         l_run += p;
-        const float *vr = &Vt_[buf][k0 + kk][sub * DL];
+        const float *vr = &Vt_[kg][buf][k0 + kk][sub * DL];
 #pragma unroll
         for (int e = 0; e < DL; e += 4) {
           const f32x4 vv = *reinterpret_cast<const f32x4 *>(vr + e);
@@ -725,8 +733,37 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a) {
         }
       }
     }
-    if (tile + 1 < ntile) lstore(buf ^ 1);
+    }
+    if (more) lstore(buf ^ 1);
     __syncthreads();
+  }
+  if constexpr (KG > 1) {
+    // groups 1.. -> LDS as [group - 1][value][thread] (the tile buffers are
+    // free after the loop's last barrier); group 0 merges them in group order
+    float *xg = &Kt[0][0][0][0];
+    static_assert((KG - 1) * (DL + 2) * 256 <= KG * 2 * kGenKeys * KS, "hand-over area exceeds the K tiles");
+    if (kg > 0) {
+      float *x = xg + (kg - 1) * (DL + 2) * 256 + tid;
+      x[0] = m_run;
+      x[256] = l_run;
+#pragma unroll
+      for (int e = 0; e < DL; ++e) x[(2 + e) * 256] = o[e];
+    }
+    __syncthreads();
+    if (kg > 0) return;
+#pragma unroll
+    for (int g = 1; g < KG; ++g) {
+      const float *x = xg + (g - 1) * (DL + 2) * 256 + tid;
+      const float mg = x[0];
+      const float mm = fmaxf(m_run, mg);
+      // a group with no visible key has max -inf, sum 0 and O 0: weight 0
+      const float w0 = m_run == mm ? 1.f : __builtin_amdgcn_exp2f(m_run - mm);
+      const float w1 = mg == mm ? 1.f : __builtin_amdgcn_exp2f(mg - mm);
+      l_run = l_run * w0 + x[256] * w1;
+#pragma unroll
+      for (int e = 0; e < DL; ++e) o[e] = o[e] * w0 + x[(2 + e) * 256] * w1;
+      m_run = mm;
+    }
   }
   if (!q_ok) return;
   T *op = reinterpret_cast<T *>(a.out) + (int64_t)b * a.os[0] + (int64_t)qi * a.os[1] +
@@ -848,12 +885,26 @@ hipError_t launch_attn(const AttnArgs &a, hipStream_t s) {
     return hipErrorInvalidValue;
   }
   const int64_t grid = (int64_t)a.n_rows * a.Hq * a.nqt;
+  // fewer blocks than CUs: key groups per block (4 at d = 64, 2 at d = 128,
+  // as the LDS allows)
+  const bool few = grid < kCUs;
+  const dim3 g((unsigned)grid);
   if (a.dtype == BD_F32) {
-    if (a.d == 64) hipLaunchKernelGGL((attn_generic_kernel<float, 64>), dim3((unsigned)grid), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((attn_generic_kernel<float, 128>), dim3((unsigned)grid), dim3(256), 0, s, a);
+    if (a.d == 64) {
+      if (few) hipLaunchKernelGGL((attn_generic_kernel<float, 64, 4>), g, dim3(1024), 0, s, a);
+      else hipLaunchKernelGGL((attn_generic_kernel<float, 64, 1>), g, dim3(256), 0, s, a);
+    } else {
+      if (few) hipLaunchKernelGGL((attn_generic_kernel<float, 128, 2>), g, dim3(512), 0, s, a);
+      else hipLaunchKernelGGL((attn_generic_kernel<float, 128, 1>), g, dim3(256), 0, s, a);
+    }
   } else {
-    if (a.d == 64) hipLaunchKernelGGL((attn_generic_kernel<bf16, 64>), dim3((unsigned)grid), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((attn_generic_kernel<bf16, 128>), dim3((unsigned)grid), dim3(256), 0, s, a);
+    if (a.d == 64) {
+      if (few) hipLaunchKernelGGL((attn_generic_kernel<bf16, 64, 4>), g, dim3(1024), 0, s, a);
+      else hipLaunchKernelGGL((attn_generic_kernel<bf16, 64, 1>), g, dim3(256), 0, s, a);
+    } else {
+      if (few) hipLaunchKernelGGL((attn_generic_kernel<bf16, 128, 2>), g, dim3(512), 0, s, a);
+      else hipLaunchKernelGGL((attn_generic_kernel<bf16, 128, 1>), g, dim3(256), 0, s, a);
+    }
   }
   return hipGetLastError();
 }

@@ -205,6 +205,18 @@ def test_fp32_general_path(bd, d, G):
     np.testing.assert_allclose(L.cpu().numpy(), ref_lse, atol=1e-5, rtol=1e-5)
 
 
+def test_fp32_general_path_many_blocks(bd):
+    """256 blocks (8 rows x 32 query heads): the general path with one key
+    group per block; the small launches above take 2 or 4 key groups."""
+    note("attn fp32 general path, 256 blocks")
+    o = [300, 0, 45, 129, 77, 256, 5, 190]
+    Q, K, V, q, t = _cache_case(41, 8, 340, 32, 8, 64, 32, 1, o, dtype=torch.float32)
+    out, L = _run_cache(bd, Q, K, V, o, 32, 0.125, lse=True)
+    ref, ref_lse = orc.cache_attention_eq6(Q, K, V, o, 32, 0.125)
+    check_attention(out, ref, torch.float32, label="fp32 many blocks")
+    np.testing.assert_allclose(L.cpu().numpy(), ref_lse, atol=1e-5, rtol=1e-5)
+
+
 def test_tiny_dense_config(bd):
     """The tiny fp32 configuration: 1 row, 4/4 heads, d = 64, prefix 256,
     W = 1, plus the scatter of the 32 new KV rows."""
