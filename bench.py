@@ -8,12 +8,15 @@ their own cache and of the sparse rows over their pools (one launch for
 both), and the KV write-back scatter of every row.  Inputs are resident in
 HBM before the timed region.
 
-The default 50 untimed warm-up steps (about 30 ms) bring the GPU to its
-steady state: the first few dozen steps of a fresh process run up to 8 %
-slower.  The timed region holds exactly ``--steps`` steps with no event
-between operations; a second pass over the same number of steps records an
-event after every operation for ``breakdown`` (those events add about 8 us
-per step).
+Before the ``--warmup`` steps an untimed settle phase repeats the step for
+a fixed wall time (``--settle-ms``, default 400 ms; reported as
+``settle_ms`` / ``settle_steps``): the first few dozen steps of a fresh
+process run up to 15 % slower than steady state (the attention launch
+448-580 us against 404 us), so a short warm-up alone would time the ramp.
+The timed region holds exactly ``--steps`` steps with no event between
+operations; a second pass over the same number of steps records an event
+after every operation for ``breakdown`` (those events add about 8 us per
+step).
 
 Prints one JSON line.  ``value`` is the whole-step throughput in attention
 TFLOP/s: the algorithmic attention FLOPs of the step (4*d per visible
@@ -420,7 +423,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-ms", type=float, default=400.0,
+                    help="untimed steps for this long before the warm-up steps")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -463,6 +468,16 @@ def main():
                               p_max_dense=dense_pmax, k_max=wl.k_max, s_max=wl.s_max)
     work = step_work(wl)
     log(f"rows={wl.B} dense={step.n_dense} sparse={step.n_sparse} warmup={args.warmup} steps={args.steps}")
+    # settle phase: the step repeated for a fixed wall time (batches of 10
+    # steps, then a synchronisation), so the timed steps start at steady state
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(10):
+            step.run()
+        settle_steps += 10
+        torch.cuda.synchronize()
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
     for _ in range(args.warmup):
         step.run()
     torch.cuda.synchronize()
@@ -559,7 +574,8 @@ def main():
         cpu = cpu_baseline(wl, args.cpu_budget)
 
     res = {"metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+           "steps": args.steps, "warmup": args.warmup, "settle_ms": round(settle_ms, 1),
+           "settle_steps": settle_steps, "ms_per_step": round(ms_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic",
            "config": {"workload": "serving_mix", "rows": wl.B, "dense_rows": n_dense,

@@ -158,6 +158,32 @@ def _rows(t, name, B):
     return t
 
 
+def _kv(t, name, B, Hkv, d, dtype, min_len=0, lead=()):
+    """A K/V-like tensor ``[*lead, >= B, >= min_len, Hkv, d]`` the C-ABI
+    indexes with its own strides: dtype, rank, row count, head count and
+    head dim are checked here, so a mismatched buffer raises instead of
+    being read or written out of bounds."""
+    t = _dev(t, name)
+    n = len(lead) + 4
+    if t.dim() != n:
+        raise ValueError(f"{name} must have {n} dimensions, got shape {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    sh = tuple(t.shape)
+    if sh[:len(lead)] != tuple(lead) or sh[len(lead)] < B or sh[len(lead) + 1] < min_len or \
+            sh[len(lead) + 2:] != (Hkv, d):
+        want = ", ".join([*map(str, lead), f">={B}", f">={min_len}", str(Hkv), str(d)])
+        raise ValueError(f"{name} must be [{want}], got {sh}")
+    return t
+
+
+def _pair(k, v, kname, vname):
+    """K and V of one source share shape and strides (one stride set crosses
+    the C-ABI for both)."""
+    if v is not None and (v.shape != k.shape or v.stride() != k.stride()):
+        raise ValueError(f"{kname} and {vname} must share shape and strides")
+
+
 def workspace(nbytes: int, device=None) -> torch.Tensor | None:
     """Caller-owned workspace (256-byte aligned: torch allocations are)."""
     if nbytes <= 0:
@@ -171,13 +197,18 @@ def kv_scatter(present_k, present_v, data_k, data_v, o, t: int, q: int, row_ids=
     """Eq. (7) write-back.  present_*/data_*: [L, B, P, Hkv, d] or [B, P, Hkv, d]."""
     pk, dk = _dev(present_k, "present_k"), _dev(data_k, "data_k")
     pv, dv = _dev(present_v, "present_v"), _dev(data_v, "data_v")
+    if (pv is None) != (dv is None):
+        raise ValueError("present_v and data_v must both be given or both be None")
     if pk.dim() == 4:
         pk, dk = pk.unsqueeze(0), dk.unsqueeze(0)
         pv = pv.unsqueeze(0) if pv is not None else None
         dv = dv.unsqueeze(0) if dv is not None else None
-    if pv is not None and (pv.stride() != pk.stride() or dv.stride() != dk.stride()):
-        raise ValueError("K and V tensors must share strides")
+    if pk.dim() != 5:
+        raise ValueError("present_k must be [L, B, P, Hkv, d] or [B, P, Hkv, d]")
     L, B, Pcap, Hkv, d = pk.shape
+    dk = _kv(dk, "data_k", B, Hkv, d, pk.dtype, lead=(L,))
+    _pair(pk, pv, "present_k", "present_v")
+    _pair(dk, dv, "data_k", "data_v")
     o = _rows(o, "o", B)
     rid = _i32(row_ids, "row_ids") if row_ids is not None else None
     n_rows = B if rid is None else rid.numel()
@@ -190,14 +221,19 @@ def gather(k_src, v_src, idx, k_cnt, k_pool, v_pool):
     """Pool gather.  *_src: [B, S, Hkv, d]; idx [B, Hkv, k_max]; pools [B, >=k_max, Hkv, d]."""
     ks, kp = _dev(k_src, "k_src"), _dev(k_pool, "k_pool")
     vs, vp = _dev(v_src, "v_src"), _dev(v_pool, "v_pool")
-    if vs is not None and (vs.stride() != ks.stride() or vp.stride() != kp.stride()):
-        raise ValueError("K and V tensors must share strides")
+    if (vs is None) != (vp is None):
+        raise ValueError("v_src and v_pool must both be given or both be None")
+    if ks.dim() != 4:
+        raise ValueError("k_src must be [B, S, Hkv, d]")
     B, S, Hkv, d = ks.shape
     idx = _i32(idx, "idx")
     if idx.dim() != 3 or tuple(idx.shape[:2]) != (B, Hkv):
         raise ValueError(f"idx must be [{B}, {Hkv}, k_max]")
-    k_cnt = _rows(k_cnt, "k_cnt", B)
     k_max = idx.shape[2]
+    kp = _kv(kp, "k_pool", B, Hkv, d, ks.dtype, min_len=k_max)
+    _pair(ks, vs, "k_src", "v_src")
+    _pair(kp, vp, "k_pool", "v_pool")
+    k_cnt = _rows(k_cnt, "k_cnt", B)
     _check(lib().bd_gather(_DTYPE[ks.dtype], B, Hkv, d, _ptr(ks), _ptr(vs), _strides(ks, 3), S,
                            _ptr(idx), k_max, _ptr(k_cnt), _ptr(kp), _ptr(vp), _strides(kp, 3),
                            kp.shape[1], _stream()))
@@ -211,8 +247,11 @@ def select(q, k, s_len, s_max: int, k_sel, k_max: int, sm_scale: float, rep_mode
            rep_row: int = 0, idx_out=None, score_out=None, ws=None):
     """Representative-query top-k.  q [B, nq, Hq, d]; k [B, C, Hkv, d].  Returns idx [B, Hkv, k_max]."""
     q, k = _dev(q, "q"), _dev(k, "k")
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, nq, Hq, d] and k [B, C, Hkv, d]")
     B, nq, Hq, d = q.shape
     Hkv = k.shape[2]
+    k = _kv(k, "k", B, Hkv, d, q.dtype)
     s_len, k_sel = _rows(s_len, "s_len", B), _rows(k_sel, "k_sel", B)
     if idx_out is None:
         idx_out = torch.empty((B, Hkv, k_max), dtype=torch.int32, device=q.device)
@@ -237,8 +276,11 @@ def select_multi(q, k, s_len, s_max: int, k_sel, k_max: int, sm_scale: float, id
     """Exact multi-query top-k: every one of the nq queries of q
     [B, nq, Hq, d] ranks k [B, C, Hkv, d].  Returns idx [B, Hkv, k_max]."""
     q, k = _dev(q, "q"), _dev(k, "k")
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, nq, Hq, d] and k [B, C, Hkv, d]")
     B, nq, Hq, d = q.shape
     Hkv = k.shape[2]
+    k = _kv(k, "k", B, Hkv, d, q.dtype)
     s_len, k_sel = _rows(s_len, "s_len", B), _rows(k_sel, "k_sel", B)
     if idx_out is None:
         idx_out = torch.empty((B, Hkv, k_max), dtype=torch.int32, device=q.device)
@@ -264,11 +306,17 @@ def attn_packed(q, pk, pv, p_len, p_max: int, wk, wv, bl: int, sm_scale: float, 
     """Packed block-diffusion attention; returns out [B, q, Hq, d].  Any
     ``mask_mode`` other than "block_causal" calls bd_attn_packed_masked."""
     q = _dev(q, "q")
-    pk, pv, wk, wv = (_dev(x, n) for x, n in ((pk, "pk"), (pv, "pv"), (wk, "wk"), (wv, "wv")))
-    if pv.stride() != pk.stride() or wv.stride() != wk.stride():
-        raise ValueError("K and V tensors must share strides")
+    if q.dim() != 4:
+        raise ValueError("q must be [B, q, Hq, d]")
     B, nqry, Hq, d = q.shape
-    Hkv = pk.shape[2]
+    pk = _dev(pk, "pk")
+    Hkv = pk.shape[2] if pk.dim() == 4 else -1
+    pk = _kv(pk, "pk", B, Hkv, d, q.dtype)
+    pv = _kv(pv, "pv", B, Hkv, d, q.dtype)
+    wk = _kv(wk, "wk", B, Hkv, d, q.dtype, min_len=nqry)
+    wv = _kv(wv, "wv", B, Hkv, d, q.dtype, min_len=nqry)
+    _pair(pk, pv, "pk", "pv")
+    _pair(wk, wv, "wk", "wv")
     p_len = _rows(p_len, "p_len", B)
     rid = _i32(row_ids, "row_ids") if row_ids is not None else None
     n_rows = B if rid is None else rid.numel()
@@ -305,18 +353,21 @@ def attn_packed_dual(q, src_a, src_b, wk, wv, bl: int, sm_scale: float, out=None
     that list's prefix (e.g. the cache for dense rows, the pool for sparse
     rows).  Returns out [B, q, Hq, d]."""
     q = _dev(q, "q")
-    wk, wv = _dev(wk, "wk"), _dev(wv, "wv")
-    if wv.stride() != wk.stride():
-        raise ValueError("K and V tensors must share strides")
+    if q.dim() != 4:
+        raise ValueError("q must be [B, q, Hq, d]")
     B, nqry, Hq, d = q.shape
+    wk = _dev(wk, "wk")
+    Hkv = wk.shape[2] if wk.dim() == 4 else -1
+    wk = _kv(wk, "wk", B, Hkv, d, q.dtype, min_len=nqry)
+    wv = _kv(wv, "wv", B, Hkv, d, q.dtype, min_len=nqry)
+    _pair(wk, wv, "wk", "wv")
     srcs = []
     for tag, (rows, pk, pv, p_len, p_max) in (("a", src_a), ("b", src_b)):
-        pk, pv = _dev(pk, "pk_" + tag), _dev(pv, "pv_" + tag)
-        if pv.stride() != pk.stride():
-            raise ValueError("K and V tensors must share strides")
+        pk = _kv(pk, "pk_" + tag, B, Hkv, d, q.dtype)
+        pv = _kv(pv, "pv_" + tag, B, Hkv, d, q.dtype)
+        _pair(pk, pv, "pk_" + tag, "pv_" + tag)
         srcs.append((_i32(rows, "rows_" + tag), pk, pv, _rows(p_len, "p_len_" + tag, B), int(p_max)))
     (ra, pka, pva, pla, pma), (rb, pkb, pvb, plb, pmb) = srcs
-    Hkv = pka.shape[2]
     if out is None:
         out = torch.empty_like(q)
     if out.shape != q.shape or out.dtype != q.dtype:
@@ -343,6 +394,11 @@ def qkv_rope_write(x, w, rope_pos, Hq: int, Hkv: int, q_out, k_cache, v_cache, d
     q_out, k_cache, v_cache = _dev(q_out, "q_out"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache")
     if k_cache.stride() != v_cache.stride():
         raise ValueError("k_cache and v_cache must share strides")
+    for t, name in ((w, "w"), (q_out, "q_out"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        if t.dtype != x.dtype:
+            raise ValueError(f"{name} must be {x.dtype} like x, got {t.dtype}")
+    if x.dim() != 3 or q_out.dim() != 4:
+        raise ValueError("x must be [B, q, Dm] and q_out [B, q, Hq, d]")
     if not w.is_contiguous():
         raise ValueError("w must be contiguous")
     B, nq, Dm = x.shape

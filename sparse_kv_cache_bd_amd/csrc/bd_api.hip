@@ -224,27 +224,18 @@ size_t bd_attn_dual_workspace_size(int dtype, int B, int Hq, int Hkv, int d, int
 
 }  // extern "C"
 
-namespace {
+namespace bd {
 
-// One prefix source of an attention call: its row list and the prefix
-// tensors those rows attend over.
-struct PrefixArg {
-  const int32_t *rows;
-  int n;
-  const void *pk, *pv;
-  const int64_t *strides;
-  int cap;
-  const int32_t *p_len;
-  int p_max;
-};
-
-// Shared body of bd_attn_packed (one source) and bd_attn_packed_dual (two).
-int attn_entry(const char *fn, int dtype, int B, int Hq, int Hkv, int d, int q, int bl,
+// Shared body of bd_attn_packed (one source), bd_attn_packed_dual (two) and
+// bd_attn_packed_noalloc: validation before any HIP call, then the argument
+// block and the launch plan.  *launch is false when there is nothing to do.
+int attn_setup(const char *fn, int dtype, int B, int Hq, int Hkv, int d, int q, int bl,
                int mask_mode, const void *q_ptr, const int64_t q_strides[3], const PrefixArg &pa,
                const PrefixArg *pb, const void *wk, const void *wv, const int64_t w_strides[3],
                float sm_scale, void *out, const int64_t out_strides[3], float *lse,
-               void *workspace, size_t ws_bytes, void *stream) {
+               AttnArgs &a, AttnPlan &plan, bool *launch) {
   g_err[0] = 0;
+  *launch = false;
   const int es = esize(dtype);
   if (!es) return fail(BD_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
   if (B < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || q < 0 || bl <= 0)
@@ -287,7 +278,6 @@ int attn_entry(const char *fn, int dtype, int B, int Hq, int Hkv, int d, int q, 
     return fail(BD_ERR_INVALID_ARG, "%s: base pointers must be 16-byte aligned", fn);
   if (w_strides[1] * es * 64 > INT32_MAX)
     return fail(BD_ERR_INVALID_ARG, "%s: key row strides above 32 MB are not supported", fn);
-  AttnArgs a;
   a.dtype = dtype; a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.d = d; a.q = q; a.bl = bl;
   a.mask_mode = mask_mode;
   a.n_rows = n_rows;
@@ -307,24 +297,47 @@ int attn_entry(const char *fn, int dtype, int B, int Hq, int Hkv, int d, int q, 
   for (int i = 0; i < 3; ++i) a.ps2[i] = use_b ? pb->strides[i] : 0;
   a.scale2 = sm_scale * kLog2e;
   const int p_max = a.p_max > a.p_max2 ? a.p_max : a.p_max2;
-  const AttnPlan plan = attn_plan(dtype, B, Hq, Hkv, d, q, n_rows, p_max);
+  plan = attn_plan(dtype, B, Hq, Hkv, d, q, n_rows, p_max);
   a.nw = plan.nw; a.nqt = plan.nqt; a.chunk = plan.chunk; a.n_split = plan.n_split;
   const int64_t grid_units = (8 + (int64_t)n_rows * Hkv) * a.nqt * a.n_split;
   if (grid_units > ((int64_t)1 << 31) - 1 || (int64_t)n_rows * Hq * a.nqt > ((int64_t)1 << 31) - 1)
     return fail(BD_ERR_INVALID_ARG, "%s: problem too large for one launch", fn);
   a.row_order = nullptr;
   a.part_o = a.part_ml = nullptr;
+  *launch = true;
+  return BD_OK;
+}
+
+// Points the plan's scratch parts (row order, split partials) into ws.
+void attn_bind_workspace(AttnArgs &a, const AttnPlan &plan, char *ws) {
+  a.row_order = plan.order ? (int *)(ws + plan.off_order) : nullptr;
+  a.part_o = plan.n_split > 1 ? (float *)(ws + plan.off_part_o) : nullptr;
+  a.part_ml = plan.n_split > 1 ? (float *)(ws + plan.off_part_ml) : nullptr;
+}
+
+int attn_launch_status(hipError_t e, const char *fn) { return hip_status(e, fn); }
+
+}  // namespace bd
+
+namespace {
+
+int attn_entry(const char *fn, int dtype, int B, int Hq, int Hkv, int d, int q, int bl,
+               int mask_mode, const void *q_ptr, const int64_t q_strides[3], const PrefixArg &pa,
+               const PrefixArg *pb, const void *wk, const void *wv, const int64_t w_strides[3],
+               float sm_scale, void *out, const int64_t out_strides[3], float *lse,
+               void *workspace, size_t ws_bytes, void *stream) {
+  AttnArgs a;
+  AttnPlan plan;
+  bool launch;
+  const int st = attn_setup(fn, dtype, B, Hq, Hkv, d, q, bl, mask_mode, q_ptr, q_strides, pa, pb,
+                            wk, wv, w_strides, sm_scale, out, out_strides, lse, a, plan, &launch);
+  if (st != BD_OK || !launch) return st;
   if (plan.ws_bytes > 0) {
     if (!workspace || ws_bytes < plan.ws_bytes)
       return fail(BD_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, plan.ws_bytes);
     if (((uintptr_t)workspace & 255u) != 0)
       return fail(BD_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
-    char *w = (char *)workspace;
-    if (plan.order) a.row_order = (int *)(w + plan.off_order);
-    if (plan.n_split > 1) {
-      a.part_o = (float *)(w + plan.off_part_o);
-      a.part_ml = (float *)(w + plan.off_part_ml);
-    }
+    attn_bind_workspace(a, plan, (char *)workspace);
   }
   return hip_status(launch_attn(a, (hipStream_t)stream), fn);
 }

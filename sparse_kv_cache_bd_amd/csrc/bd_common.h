@@ -134,6 +134,28 @@ struct AttnPlan {
 };
 AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int d, int q, int n_rows, int p_max);
 hipError_t launch_attn(const AttnArgs &a, hipStream_t s);
+
+// One prefix source of an attention call: its row list and the prefix
+// tensors those rows attend over.
+struct PrefixArg {
+  const int32_t *rows;
+  int n;
+  const void *pk, *pv;
+  const int64_t *strides;
+  int cap;
+  const int32_t *p_len;
+  int p_max;
+};
+// Validation (before any HIP call), argument block and plan of one
+// attention call (bd_api.hip); *launch is false when there is nothing to do.
+int attn_setup(const char *fn, int dtype, int B, int Hq, int Hkv, int d, int q, int bl,
+               int mask_mode, const void *q_ptr, const int64_t q_strides[3], const PrefixArg &pa,
+               const PrefixArg *pb, const void *wk, const void *wv, const int64_t w_strides[3],
+               float sm_scale, void *out, const int64_t out_strides[3], float *lse,
+               AttnArgs &a, AttnPlan &plan, bool *launch);
+void attn_bind_workspace(AttnArgs &a, const AttnPlan &plan, char *ws);
+// BD_OK, or BD_ERR_HIP with the message set.
+int attn_launch_status(hipError_t e, const char *fn);
 bool attn_mfma_supported(int dtype, int d, int G);
 bool attn_generic_supported(int dtype, int d);
 

@@ -52,6 +52,9 @@ class BlockDiffusionStep:
         self.s_max = int(s_max)
         self.s_len = s_len.to(self.dev) if s_len is not None else torch.zeros(B, **i32)
         self.k_sel = k_sel.to(self.dev) if k_sel is not None else torch.zeros(B, **i32)
+        # entries a row's pool holds: bd_select keeps min(k_b, S_b) positions
+        # (-1 past them), so a budget above the prefix fills only S_b slots
+        self.k_eff = torch.minimum(self.k_sel, self.s_len).contiguous()
         self.out = torch.zeros_like(Q)
         if self.n_sparse:
             self.idx = torch.empty((B, self.Hkv, self.k_max), **i32)
@@ -79,7 +82,7 @@ class BlockDiffusionStep:
 
     def gather(self):
         if self.n_sparse:
-            bd.gather(self.Kc, self.Vc, self.idx, self.k_sel, self.pool_k, self.pool_v)
+            bd.gather(self.Kc, self.Vc, self.idx, self.k_eff, self.pool_k, self.pool_v)
 
     def attn_dense(self):
         if self.n_dense:
@@ -89,7 +92,7 @@ class BlockDiffusionStep:
 
     def attn_sparse(self):
         if self.n_sparse:
-            bd.attn_packed(self.Q, self.pool_k, self.pool_v, self.k_sel, self.k_max, self.wk,
+            bd.attn_packed(self.Q, self.pool_k, self.pool_v, self.k_eff, self.k_max, self.wk,
                            self.wv, self.bl, self.sm_scale, out=self.out,
                            row_ids=self.sparse_rows, ws=self.ws_sparse)
 
@@ -97,7 +100,7 @@ class BlockDiffusionStep:
         """Attention of every row in one launch."""
         if self.n_dense and self.n_sparse:
             bd.attn_packed_dual(self.Q, (self.dense_rows, self.Kc, self.Vc, self.o, self.p_max_dense),
-                                (self.sparse_rows, self.pool_k, self.pool_v, self.k_sel, self.k_max),
+                                (self.sparse_rows, self.pool_k, self.pool_v, self.k_eff, self.k_max),
                                 self.wk, self.wv, self.bl, self.sm_scale, out=self.out,
                                 ws=self.ws_both)
         else:
@@ -143,6 +146,8 @@ class SparseBlockPipeline:
         self.B, _, self.Hkv, self.d = Kc.shape
         self.Hq = Qsel.shape[2]
         self.s_len, self.k_sel = s_len, k_sel
+        # pool entries per row: min(k_b, S_b) (bd_select pads the rest with -1)
+        self.k_eff = torch.minimum(k_sel, s_len).contiguous()
         self.s_max, self.k_max = int(s_max), int(k_max)
         self.sm_scale, self.bl = sm_scale, bl
         self.steps_q, self.steps_kv = steps_q, steps_kv
@@ -169,13 +174,13 @@ class SparseBlockPipeline:
         pk, pv = self.pools[slot]
         bd.select(self.Qsel, self.Kc, self.s_len, self.s_max, self.k_sel, self.k_max,
                   self.sm_scale, idx_out=self.idx, ws=self.ws_sel)
-        bd.gather(self.Kc, self.Vc, self.idx, self.k_sel, pk, pv)
+        bd.gather(self.Kc, self.Vc, self.idx, self.k_eff, pk, pv)
 
     def denoise(self, slot: int, st: int):
         """Denoising step ``st`` of one block over pool ``slot`` (current stream)."""
         pk, pv = self.pools[slot]
         wk, wv = self.steps_kv[st]
-        bd.attn_packed(self.steps_q[st], pk, pv, self.k_sel, self.k_max, wk, wv, self.bl,
+        bd.attn_packed(self.steps_q[st], pk, pv, self.k_eff, self.k_max, wk, wv, self.bl,
                        self.sm_scale, out=self.out, ws=self.ws_attn)
 
     def run_sequential(self, n_blocks: int):

@@ -15,3 +15,20 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+# Figures a test reports (not gates): printed in the terminal summary, so
+# they show in quiet runs as well.
+REPORTS: list[str] = []
+
+
+@pytest.fixture
+def report():
+    return REPORTS.append
+
+
+def pytest_terminal_summary(terminalreporter):
+    if REPORTS:
+        terminalreporter.section("reported figures")
+        for line in REPORTS:
+            terminalreporter.write_line(line)

@@ -97,3 +97,48 @@ def test_denoising_steps_in_a_hip_graph(bd):
         for st in range(wl.T):
             assert torch.equal(outs[st], want[st]), f"replay {rep}, step {st}"
         bd.select(wl.Qsel.cuda(), Kc, wl.s_len.cuda(), wl.s_max, k_sel, wl.k_max, wl.sm_scale)
+
+
+def test_budget_above_prefix(bd):
+    """A row whose budget exceeds its prefix (k_b > S_b) keeps all S_b
+    positions; its pool holds S_b entries and its attention covers exactly
+    those, never the pool slots past them (which hold stale values)."""
+    from sparse_kv_cache_bd_amd.pipeline import BlockDiffusionStep, SparseBlockPipeline
+    note("pipeline: budget above the prefix")
+    wl = synth.serving_mix(seed=3, B=3, p_lo=200, p_hi=1200, W=2, sparse_above=100)
+    k_sel = wl.k_sel.clone()
+    k_sel[0] = int(wl.s_len[0]) + 77          # more than the row's prefix
+    k_max = int(k_sel.max())
+    Kc, Vc, Q, o = wl.Kc.cuda(), wl.Vc.cuda(), wl.Q.cuda(), wl.o.cuda()
+    step = BlockDiffusionStep(Kc, Vc, Q, o, wl.bl, wl.sm_scale, sparse_rows=wl.sparse_rows,
+                              dense_rows=wl.dense_rows, s_len=wl.s_len, k_sel=k_sel,
+                              p_max_dense=int(wl.o.max()), k_max=k_max, s_max=wl.s_max)
+    step.pool_k.fill_(float("nan"))          # stale pool content must never be read
+    step.pool_v.fill_(float("nan"))
+    step.select()
+    step.gather()
+    step.attn_sparse()
+    torch.cuda.synchronize()
+    k_eff = np.minimum(k_sel.numpy(), wl.s_len.numpy())
+    idx = orc.topk_select(step.scores.cpu().double().numpy(), wl.s_len, k_sel, k_max)
+    assert np.array_equal(step.idx.cpu().numpy(), idx)
+    assert (idx[0, :, :int(wl.s_len[0])] == np.arange(int(wl.s_len[0]))).all()
+    zeros = np.zeros((wl.B, k_max, wl.Hkv, wl.d))
+    pk = orc.gather(wl.Kc.double().numpy(), idx, k_eff, zeros)
+    pv = orc.gather(wl.Vc.double().numpy(), idx, k_eff, zeros)
+    t = wl.t
+    rows = wl.sparse_rows.tolist()
+    ref, _ = orc.block_attention(wl.Q, pk, pv, k_eff, wl.Kc[:, t:], wl.Vc[:, t:], wl.bl,
+                                 wl.sm_scale, rows=rows)
+    check_attention(step.out, ref, torch.bfloat16, rows=rows, label="budget above prefix")
+    # the dual-stream pipeline takes the same pool length
+    sel = torch.tensor(rows, dtype=torch.long)
+    pipe = SparseBlockPipeline(Kc[sel], Vc[sel], Q[sel], wl.s_len[sel].cuda(), k_sel[sel].cuda(),
+                               wl.s_max, k_max, wl.sm_scale, wl.bl, [Q[sel]],
+                               [(Kc[sel][:, t:], Vc[sel][:, t:])])
+    for pk_, pv_ in pipe.pools:
+        pk_.fill_(float("nan"))
+        pv_.fill_(float("nan"))
+    out = pipe.run_sequential(1)
+    torch.cuda.synchronize()
+    check_attention(out, ref[sel.numpy()], torch.bfloat16, label="budget above prefix, pipeline")
