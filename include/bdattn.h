@@ -30,7 +30,8 @@
  * - Memory: every tensor pointer is device memory owned by the caller.  The
  *   library allocates nothing and keeps no state between calls; scratch
  *   space comes from a caller workspace whose size the matching
- *   *_workspace_size function returns.
+ *   *_workspace_size function returns (bd_attn_packed_noalloc instead uses
+ *   one device array the library holds per GPU).
  * - Streams: every call is asynchronous on the given hipStream_t (passed as
  *   void*; NULL is the default stream).  No call synchronises, reads device
  *   memory from the host, or allocates, so calls can be captured in a HIP
@@ -318,6 +319,29 @@ int bd_attn_packed_dual(int dtype, int B, int Hq, int Hkv, int d, int q,
                         const int64_t w_strides[3], float sm_scale, void *out,
                         const int64_t out_strides[3], float *lse,
                         void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * bd_attn_packed_noalloc: bd_attn_packed for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, mask, results and errors
+ * as bd_attn_packed, minus the workspace: the call's scratch (row order and
+ * split-prefix partials, bd_attn_workspace_size(...) bytes) lives in a
+ * device array of BD_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * GPU it runs on until the process ends.  The call allocates nothing and
+ * calls no allocating routine; a call whose scratch would exceed
+ * BD_NOALLOC_SCRATCH_BYTES returns BD_ERR_WORKSPACE before any HIP call.
+ * Every call on one GPU shares that array: calls that overlap on one GPU
+ * (on two streams) race and must not be issued.  The first call on a device
+ * looks up the array's address there (a non-allocating runtime query).
+ */
+#define BD_NOALLOC_SCRATCH_BYTES (32u << 20)
+int bd_attn_packed_noalloc(int dtype, int B, int Hq, int Hkv, int d, int q, int bl,
+                           const int32_t *row_ids, int n_rows, const void *q_ptr,
+                           const int64_t q_strides[3], const void *pk, const void *pv,
+                           const int64_t p_strides[3], int p_cap, const int32_t *p_len,
+                           int p_max, const void *wk, const void *wv,
+                           const int64_t w_strides[3], float sm_scale, void *out,
+                           const int64_t out_strides[3], float *lse, void *stream);
 
 /*
  * bd_qkv_rope_write: Flash-dLLM's fused cache producer (Flash-Cache): the

@@ -54,6 +54,9 @@ _SIGS = {
                                  _vp, _i, _vp, _vp, _vp, _i, _vp, _i,
                                  _vp, _i, _vp, _vp, _vp, _i, _vp, _i,
                                  _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "bd_attn_packed_noalloc": (_i, [_i, _i, _i, _i, _i, _i, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp,
+                                    _i, _vp, _i, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp,
+                                    _vp]),
     "bd_attn_packed_masked": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _vp, _i, _vp, _vp, _vp, _vp,
                                    _vp, _i, _vp, _i, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp,
                                    _vp, _sz, _vp]),
@@ -84,6 +87,13 @@ def lib() -> ctypes.CDLL:
             f.argtypes = args
         _lib = L
     return _lib
+
+
+def noalloc_scratch_bytes() -> int:
+    """BD_NOALLOC_SCRATCH_BYTES as the public header defines it."""
+    with open(HEADER_PATH) as f:
+        m = re.search(r"#define\s+BD_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", f.read())
+    return int(m.group(1)) << int(m.group(2))
 
 
 def header_functions() -> list[str]:
@@ -337,6 +347,38 @@ def attn_packed(q, pk, pv, p_len, p_max: int, wk, wv, bl: int, sm_scale: float, 
     else:
         _check(lib().bd_attn_packed_masked(_DTYPE[q.dtype], B, Hq, Hkv, d, nqry, bl,
                                            MASK_MODES[mask_mode], *tail))
+    return out
+
+
+def attn_packed_noalloc(q, pk, pv, p_len, p_max: int, wk, wv, bl: int, sm_scale: float,
+                        out=None, lse=None, row_ids=None):
+    """bd_attn_packed_noalloc: attn_packed with the scratch in the library's
+    own device array (no workspace; allocates nothing when ``out`` is
+    given).  Returns out [B, q, Hq, d]."""
+    q = _dev(q, "q")
+    if q.dim() != 4:
+        raise ValueError("q must be [B, q, Hq, d]")
+    B, nqry, Hq, d = q.shape
+    pk = _dev(pk, "pk")
+    Hkv = pk.shape[2] if pk.dim() == 4 else -1
+    pk = _kv(pk, "pk", B, Hkv, d, q.dtype)
+    pv = _kv(pv, "pv", B, Hkv, d, q.dtype)
+    wk = _kv(wk, "wk", B, Hkv, d, q.dtype, min_len=nqry)
+    wv = _kv(wv, "wv", B, Hkv, d, q.dtype, min_len=nqry)
+    _pair(pk, pv, "pk", "pv")
+    _pair(wk, wv, "wk", "wv")
+    p_len = _rows(p_len, "p_len", B)
+    rid = _i32(row_ids, "row_ids") if row_ids is not None else None
+    n_rows = B if rid is None else rid.numel()
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q's shape and dtype")
+    lse = _buf(lse, "lse", (B, Hq, nqry), torch.float32)
+    _check(lib().bd_attn_packed_noalloc(
+        _DTYPE[q.dtype], B, Hq, Hkv, d, nqry, bl, _ptr(rid), n_rows, _ptr(q), _strides(q, 3),
+        _ptr(pk), _ptr(pv), _strides(pk, 3), pk.shape[1], _ptr(p_len), p_max, _ptr(wk), _ptr(wv),
+        _strides(wk, 3), float(sm_scale), _ptr(out), _strides(out, 3), _ptr(lse), _stream()))
     return out
 
 

@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbdattn.so")
 
-SOURCES = ["bd_api.hip", "bd_move.hip", "bd_attn.hip", "bd_select.hip", "bd_produce.hip"]
+SOURCES = ["bd_api.hip", "bd_move.hip", "bd_attn.hip", "bd_select.hip", "bd_produce.hip",
+           "bd_noalloc.hip"]
 
 ARCH = "gfx950"
 

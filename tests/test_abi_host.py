@@ -24,7 +24,7 @@ def L():
 
 def test_exports_every_header_function(L):
     names = bd.header_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(L, n), n
 
@@ -212,6 +212,48 @@ def _attn(L, ws_bytes=None, **kw):
 ])
 def test_attn_validation(L, kw, code):
     assert _attn(L, **kw) == code
+
+
+def _attn_noalloc(L, **kw):
+    a = dict(dtype=bd.BD_BF16, B=2, Hq=32, Hkv=8, d=128, q=64, bl=32, rid=None, n_rows=2,
+             Q=FAKE, qs=I3(64 * 4096, 4096, 128), pk=FAKE, pv=FAKE2, ps=I3(1 << 22, 1024, 128),
+             pcap=4096, plen=FAKE, pmax=4000, wk=FAKE, wv=FAKE2, wsd=I3(1 << 22, 1024, 128),
+             scale=0.088, out=FAKE2, os=I3(64 * 4096, 4096, 128), lse=None)
+    a.update(kw)
+    return L.bd_attn_packed_noalloc(a["dtype"], a["B"], a["Hq"], a["Hkv"], a["d"], a["q"], a["bl"],
+                                    a["rid"], a["n_rows"], a["Q"], a["qs"], a["pk"], a["pv"],
+                                    a["ps"], a["pcap"], a["plen"], a["pmax"], a["wk"], a["wv"],
+                                    a["wsd"], a["scale"], a["out"], a["os"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=3), bd.BD_ERR_UNSUPPORTED),
+    (dict(Hq=33), bd.BD_ERR_INVALID_ARG),
+    (dict(n_rows=1), bd.BD_ERR_INVALID_ARG),
+    (dict(plen=None), bd.BD_ERR_INVALID_ARG),
+    (dict(wv=MISALIGNED), bd.BD_ERR_INVALID_ARG),
+    (dict(scale=0.0), bd.BD_ERR_INVALID_ARG),
+    (dict(B=0, n_rows=0), bd.BD_OK),
+    (dict(q=0), bd.BD_OK),
+])
+def test_attn_noalloc_validation(L, kw, code):
+    """The allocation-free variant validates exactly like bd_attn_packed."""
+    assert _attn_noalloc(L, **kw) == code
+    if code != bd.BD_OK:
+        assert bd.last_error().startswith("bd_attn_packed_noalloc")
+
+
+def test_attn_noalloc_rejects_oversized_scratch(L):
+    """A call whose scratch exceeds the library's array is refused with
+    BD_ERR_WORKSPACE before any HIP call (the size comes from the plan)."""
+    cap = bd.noalloc_scratch_bytes()
+    assert cap == 32 << 20
+    # one unit with a 4M-key prefix: the plan cuts 512 chunks of partials
+    kw = dict(B=1, n_rows=1, Hq=4, Hkv=1, q=32, pmax=1 << 22, pcap=1 << 22)
+    need = bd.attn_workspace_size(bd.BD_BF16, 1, 4, 1, 128, 32, 1, 1 << 22)
+    assert need > cap
+    assert _attn_noalloc(L, **kw) == bd.BD_ERR_WORKSPACE
+    assert "scratch" in bd.last_error() and str(need) in bd.last_error()
 
 
 def _attn_masked(L, mode, **kw):
