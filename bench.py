@@ -273,6 +273,48 @@ def bench_producer(bd, dev, reps):
     return res
 
 
+def bench_block_table(bd, wl, Kc, Vc, Q, dense_pmax, ms_packed, reps, page=128):
+    """Flash-dLLM's Scheduled Flash Attention on the serving mix's dense
+    rows: each row's prefix cut into pages of ``page`` keys at shuffled slots
+    of a paged store, one work item per row, dispatched in row order and
+    longest first (the caller's choice), against bd_attn_packed over the
+    same rows (contiguous cache, the library's own longest-first order)."""
+    import torch
+    rows = wl.dense_rows.long().to(Kc.device)
+    P = wl.o.long().to(Kc.device)[rows]
+    n_pg = (P + page - 1) // page
+    total = int(n_pg.sum())
+    row_of = torch.repeat_interleave(rows, n_pg)
+    first = torch.cumsum(n_pg, 0) - n_pg
+    j_of = torch.arange(total, device=Kc.device) - torch.repeat_interleave(first, n_pg)
+    g = torch.Generator(device=Kc.device).manual_seed(0)
+    slot = torch.randperm(total, generator=g, device=Kc.device)
+    pos = (j_of[:, None] * page + torch.arange(page, device=Kc.device)[None, :]).clamp_(max=Kc.shape[1] - 1)
+    KP = torch.empty((total, page, wl.Hkv, wl.d), dtype=Kc.dtype, device=Kc.device)
+    VP = torch.empty_like(KP)
+    KP[slot] = Kc[row_of[:, None], pos]
+    VP[slot] = Vc[row_of[:, None], pos]
+    table = slot.to(torch.int32)
+    items = torch.stack([rows, torch.zeros_like(rows), torch.full_like(rows, wl.q), first, P], 1).to(torch.int32)
+    longest = items[torch.argsort(P, descending=True, stable=True)].contiguous()
+    wk, wv = Kc[:, wl.t:], Vc[:, wl.t:]
+    out = torch.empty_like(Q)
+    ws = bd.workspace(bd.attn_block_table_workspace_size(Q.dtype, wl.Hq, wl.Hkv, wl.d, wl.q,
+                                                         len(items), dense_pmax), Q.device)
+    res = {"rows": len(items), "page": page, "pages": total,
+           "store_mb": round(2 * KP.numel() * 2 / 1e6, 1)}
+    flop = attention_flops(wl.o, wl.dense_rows.tolist(), wl.q, wl.bl, wl.Hq, wl.d)
+    for name, it in (("row_order", items.contiguous()), ("longest_first", longest)):
+        ms = time_calls(lambda: bd.attn_block_table(Q, KP, VP, it, table, dense_pmax, wk, wv, wl.bl,
+                                                    wl.sm_scale, out=out, ws=ws), reps)
+        res[f"{name}_us"] = round(ms * 1e3, 2)
+        res[f"{name}_TFLOP/s"] = _rate(flop, ms, 1e12)
+    res["packed_contiguous_us"] = round(ms_packed * 1e3, 2)
+    del KP, VP
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_configs(dev, reps: int = 10):
     """The other synthetic workloads, each in the launch configuration its
     parity test checks: per-operation times and rates, warm (back-to-back
@@ -562,11 +604,16 @@ def main():
             "intensity_flop_per_byte": round(attn_flop / attn_bytes, 1)}
 
     n_dense, n_sparse = step.n_dense, step.n_sparse
+    block_table = None
+    if not args.skip_configs:
+        log("block table over the dense rows")
+        block_table = bench_block_table(bd, wl, Kc, Vc, Q, dense_pmax, ms_dense, args.steps)
     configs = None
     if not args.skip_configs:
         del step, Kc, Vc, Q, o
         torch.cuda.empty_cache()
         configs = bench_configs(dev)
+        configs["block_table_serving_mix_dense"] = block_table
 
     cpu = None
     if not args.no_cpu_baseline:

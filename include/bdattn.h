@@ -344,6 +344,65 @@ int bd_attn_packed_noalloc(int dtype, int B, int Hq, int Hkv, int d, int q, int 
                            const int64_t out_strides[3], float *lse, void *stream);
 
 /*
+ * bd_attn_block_table: Flash-dLLM's Scheduled Flash Attention (Flash-Cache,
+ * Fig. 3(b)): the batch is cut into work items, and a block table aligns
+ * each item's query block with the key-value blocks it attends over; the
+ * caller controls which blocks are computed and in what order, and adds or
+ * removes items freely between calls.  Here the key-value blocks are pages
+ * of a paged KV store (any page anywhere, in any order), and every item
+ * also attends over its row's window under the FlowBlock mask, so a
+ * contiguous table gives exactly bd_attn_packed (FlowBlock review Eq. (6);
+ * HERALD's denoising attention when the pages hold a gathered pool).
+ *
+ * For each item e = items[n] (n < n_items) with row b = e.row, query
+ * i in [e.q_begin, min(e.q_end, q)) and query head hq (KV head h):
+ *   visible keys = the first L = min(e.kv_len, kv_max) keys of the pages
+ *                  table[e.table_off + j], j < ceil(L / page), in that order
+ *                  (key m of the list is position m % page of page
+ *                  table[e.table_off + m / page]), and the window entries
+ *                  wk/wv[b, w, h] with w < (floor(i / bl) + 1) * bl
+ *   out[b, i, hq, :], lse[b, hq, i] as in bd_attn_packed.
+ *
+ *   items     device bd_attn_item [n_items], dispatched in list order.
+ *             An item whose row is outside [0, B), whose query range is
+ *             empty, or whose pages run past n_table is skipped.  Items
+ *             must cover disjoint (row, query) sets: outputs no item covers
+ *             are not written; two items covering the same output leave one
+ *             of the two results.
+ *   table     device int32 [n_table]: page ids; a page id outside
+ *             [0, n_pages) contributes no keys.
+ *   kv_k/kv_v the paged store [n_pages, page, Hkv, d], strides kv_strides
+ *             {page, pos, head}; page a multiple of 64 keys (one 64-key
+ *             tile never straddles two pages).
+ *   q, wk/wv, out, lse, sm_scale as in bd_attn_packed.
+ *   workspace at least bd_attn_block_table_workspace_size(...) bytes,
+ *             256-byte aligned (split partials when few items).
+ *
+ * Built for BD_BF16 with d == 128 and Hq / Hkv in {1, 2, 4, 8}; other
+ * combinations return BD_ERR_UNSUPPORTED.
+ */
+typedef struct {
+  int32_t row;       /* row b of q, the window and out                     */
+  int32_t q_begin;   /* first window query of the item                     */
+  int32_t q_end;     /* one past its last window query (clamped to q)      */
+  int32_t table_off; /* first entry of the item's pages in the table       */
+  int32_t kv_len;    /* keys on those pages (clamped to [0, kv_max])       */
+} bd_attn_item;
+
+size_t bd_attn_block_table_workspace_size(int dtype, int Hq, int Hkv, int d, int q,
+                                          int n_items, int kv_max);
+int bd_attn_block_table(int dtype, int B, int Hq, int Hkv, int d, int q, int bl,
+                        const bd_attn_item *items, int n_items,
+                        const int32_t *table, int n_table, const void *kv_k,
+                        const void *kv_v, const int64_t kv_strides[3],
+                        int n_pages, int page, int kv_max, const void *q_ptr,
+                        const int64_t q_strides[3], const void *wk,
+                        const void *wv, const int64_t w_strides[3],
+                        float sm_scale, void *out,
+                        const int64_t out_strides[3], float *lse,
+                        void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * bd_qkv_rope_write: Flash-dLLM's fused cache producer (Flash-Cache): the
  * projection of the window's hidden states onto the query, key and value
  * heads, the rotary embedding of queries and keys at absolute positions

@@ -41,6 +41,7 @@ __all__ = [
     "eq6_mask",
     "window_visible",
     "block_attention",
+    "block_table_attention",
     "cache_attention_eq6",
     "rep_query",
     "center_row",
@@ -186,6 +187,55 @@ def block_attention(Q, PK, PV, p_len, WK, WV, bl: int, sm_scale: float,
                 logits = sm_scale * (Q[b, :, hq] @ keys.T)   # [q, P+q]
                 logits = np.where(vis, logits, -np.inf)
                 O[b, :, hq], LSE[b, hq] = _softmax_attend(logits, vals)
+    return O, LSE
+
+
+def block_table_attention(Q, KP, VP, items, table, page: int, WK, WV, bl: int,
+                          sm_scale: float, kv_max: int | None = None):
+    """Attention scheduled by a block table (Flash-dLLM, Scheduled Flash
+    Attention, Fig. 3(b)).
+
+    The batch is cut into work items; the block table aligns each item's
+    query block with the key-value blocks it attends over.  Here the
+    key-value blocks are pages of a paged store ``KP, VP [n_pages, page, Hkv,
+    d]``.  Item ``(row, q_begin, q_end, table_off, kv_len)`` covers queries
+    ``i`` in ``[q_begin, min(q_end, q))`` of ``row``; its keys are the first
+    ``L = min(kv_len, kv_max)`` keys of the pages ``table[table_off + j]``
+    taken in table order (key ``m`` is position ``m % page`` of page
+    ``table[table_off + m // page]``), followed by the row's window keys
+    ``WK[row, w]`` with ``w < (floor(i/bl) + 1) * bl`` (FlowBlock review
+    Eq. (6)'s window part).  A contiguous table over a row's own cache is
+    ``block_attention`` with ``p_len = kv_len``.
+
+    Q: [B, q, Hq, d]; WK, WV: [B, q, Hkv, d]; items: int array [n, 5];
+    table: int array.  Returns ``O [B, q, Hq, d]`` and ``LSE [B, Hq, q]`` in
+    float64, NaN wherever no item writes.
+    """
+    Q = _f64(Q)
+    items = _i64(items).reshape(-1, 5)
+    table = _i64(table)
+    B, q, Hq, d = Q.shape
+    Hkv = KP.shape[2]
+    G = Hq // Hkv
+    wvis = window_visible(q, bl)                              # [q, q]
+    O = np.full((B, q, Hq, d), np.nan)
+    LSE = np.full((B, Hq, q), np.nan)
+    for row, q0, q1, off, n in items:
+        q1 = min(int(q1), q)
+        L = int(n) if kv_max is None else min(int(n), int(kv_max))
+        pages = table[int(off):int(off) + -(-L // page)]
+        qi = np.arange(int(q0), q1)
+        for h in range(Hkv):
+            pk = np.concatenate([_f64(KP[p, :, h]) for p in pages] + [np.zeros((0, d))])[:L]
+            pv = np.concatenate([_f64(VP[p, :, h]) for p in pages] + [np.zeros((0, d))])[:L]
+            keys = np.concatenate([pk, _f64(WK[row, :, h])], axis=0)
+            vals = np.concatenate([pv, _f64(WV[row, :, h])], axis=0)
+            vis = np.concatenate([np.ones((len(qi), L), bool), wvis[qi]], axis=1)
+            for g in range(G):
+                hq = h * G + g
+                logits = sm_scale * (Q[row, qi, hq] @ keys.T)
+                logits = np.where(vis, logits, -np.inf)
+                O[row, qi, hq], LSE[row, hq, qi] = _softmax_attend(logits, vals)
     return O, LSE
 
 

@@ -57,6 +57,10 @@ _SIGS = {
     "bd_attn_packed_noalloc": (_i, [_i, _i, _i, _i, _i, _i, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp,
                                     _i, _vp, _i, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp,
                                     _vp]),
+    "bd_attn_block_table_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "bd_attn_block_table": (_i, [_i, _i, _i, _i, _i, _i, _i, _vp, _i, _vp, _i, _vp, _vp, _vp, _i,
+                                 _i, _i, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp,
+                                 _vp, _sz, _vp]),
     "bd_attn_packed_masked": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _vp, _i, _vp, _vp, _vp, _vp,
                                    _vp, _i, _vp, _i, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp,
                                    _vp, _sz, _vp]),
@@ -379,6 +383,54 @@ def attn_packed_noalloc(q, pk, pv, p_len, p_max: int, wk, wv, bl: int, sm_scale:
         _DTYPE[q.dtype], B, Hq, Hkv, d, nqry, bl, _ptr(rid), n_rows, _ptr(q), _strides(q, 3),
         _ptr(pk), _ptr(pv), _strides(pk, 3), pk.shape[1], _ptr(p_len), p_max, _ptr(wk), _ptr(wv),
         _strides(wk, 3), float(sm_scale), _ptr(out), _strides(out, 3), _ptr(lse), _stream()))
+    return out
+
+
+def attn_block_table_workspace_size(dtype, Hq: int, Hkv: int, d: int, q: int, n_items: int,
+                                    kv_max: int) -> int:
+    return int(lib().bd_attn_block_table_workspace_size(_DTYPE.get(dtype, dtype), Hq, Hkv, d, q,
+                                                        n_items, kv_max))
+
+
+def attn_block_table(q, kv_k, kv_v, items, table, kv_max: int, wk, wv, bl: int,
+                     sm_scale: float, out=None, lse=None, ws=None):
+    """Block-table attention (bd_attn_block_table).  q [B, q, Hq, d]; kv_k /
+    kv_v the paged store [n_pages, page, Hkv, d]; items int32 [n_items, 5]
+    (row, q_begin, q_end, table_off, kv_len) in dispatch order; table int32
+    [n_table] page ids; wk / wv [B, q, Hkv, d].  Outputs no item covers are
+    left as they are in ``out``.  Returns out."""
+    q = _dev(q, "q")
+    if q.dim() != 4:
+        raise ValueError("q must be [B, q, Hq, d]")
+    B, nqry, Hq, d = q.shape
+    kv_k = _dev(kv_k, "kv_k")
+    if kv_k.dim() != 4:
+        raise ValueError("kv_k must be [n_pages, page, Hkv, d]")
+    n_pages, page, Hkv = kv_k.shape[0], kv_k.shape[1], kv_k.shape[2]
+    kv_k = _kv(kv_k, "kv_k", n_pages, Hkv, d, q.dtype)
+    kv_v = _kv(kv_v, "kv_v", n_pages, Hkv, d, q.dtype)
+    _pair(kv_k, kv_v, "kv_k", "kv_v")
+    wk = _kv(wk, "wk", B, Hkv, d, q.dtype, min_len=nqry)
+    wv = _kv(wv, "wv", B, Hkv, d, q.dtype, min_len=nqry)
+    _pair(wk, wv, "wk", "wv")
+    items = _i32(items, "items")
+    if items.dim() != 2 or items.shape[1] != 5:
+        raise ValueError("items must be int32 [n_items, 5]")
+    table = _i32(table, "table")
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q's shape and dtype")
+    lse = _buf(lse, "lse", (B, Hq, nqry), torch.float32)
+    n_items = items.shape[0]
+    need = attn_block_table_workspace_size(q.dtype, Hq, Hkv, d, nqry, n_items, kv_max)
+    if ws is None:
+        ws = workspace(need, q.device)
+    _check(lib().bd_attn_block_table(
+        _DTYPE[q.dtype], B, Hq, Hkv, d, nqry, bl, _ptr(items), n_items, _ptr(table), table.numel(),
+        _ptr(kv_k), _ptr(kv_v), _strides(kv_k, 3), n_pages, page, int(kv_max), _ptr(q),
+        _strides(q, 3), _ptr(wk), _ptr(wv), _strides(wk, 3), float(sm_scale), _ptr(out),
+        _strides(out, 3), _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(), _stream()))
     return out
 
 

@@ -304,6 +304,10 @@ int attn_setup(const char *fn, int dtype, int B, int Hq, int Hkv, int d, int q, 
     return fail(BD_ERR_INVALID_ARG, "%s: problem too large for one launch", fn);
   a.row_order = nullptr;
   a.part_o = a.part_ml = nullptr;
+  a.items = nullptr;
+  a.table = nullptr;
+  a.n_table = 0;
+  a.page = 0;
   *launch = true;
   return BD_OK;
 }
@@ -384,6 +388,75 @@ int bd_attn_packed_dual(int dtype, int B, int Hq, int Hkv, int d, int q, int bl,
   const PrefixArg pb{rows_b, n_b, pk_b, pv_b, pb_strides, pb_cap, p_len_b, p_max_b};
   return attn_entry("bd_attn_packed_dual", dtype, B, Hq, Hkv, d, q, bl, BD_MASK_BLOCK_CAUSAL, q_ptr, q_strides, pa, &pb,
                     wk, wv, w_strides, sm_scale, out, out_strides, lse, workspace, ws_bytes, stream);
+}
+
+size_t bd_attn_block_table_workspace_size(int dtype, int Hq, int Hkv, int d, int q, int n_items,
+                                          int kv_max) {
+  if (Hq <= 0 || Hkv <= 0 || d <= 0 || q <= 0 || n_items <= 0 || kv_max < 0) return 0;
+  return attn_plan(dtype, 1, Hq, Hkv, d, q, n_items, kv_max, true).ws_bytes;
+}
+
+int bd_attn_block_table(int dtype, int B, int Hq, int Hkv, int d, int q, int bl,
+                        const bd_attn_item *items, int n_items, const int32_t *table, int n_table,
+                        const void *kv_k, const void *kv_v, const int64_t kv_strides[3],
+                        int n_pages, int page, int kv_max, const void *q_ptr,
+                        const int64_t q_strides[3], const void *wk, const void *wv,
+                        const int64_t w_strides[3], float sm_scale, void *out,
+                        const int64_t out_strides[3], float *lse, void *workspace, size_t ws_bytes,
+                        void *stream) {
+  static const char *fn = "bd_attn_block_table";
+  g_err[0] = 0;
+  const int es = esize(dtype);
+  if (!es) return fail(BD_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || q < 0 || bl <= 0 || n_items < 0 || n_table < 0 ||
+      n_pages < 0 || kv_max < 0)
+    return fail(BD_ERR_INVALID_ARG, "%s: negative or zero size", fn);
+  if (Hq % Hkv != 0) return fail(BD_ERR_INVALID_ARG, "%s: Hq %% Hkv != 0", fn);
+  if (!attn_mfma_supported(dtype, d, Hq / Hkv))
+    return fail(BD_ERR_UNSUPPORTED, "%s: built for bf16, d = 128, Hq/Hkv in {1, 2, 4, 8}", fn);
+  if (page <= 0 || page % 64 != 0)
+    return fail(BD_ERR_INVALID_ARG, "%s: page %d must be a positive multiple of 64 keys", fn, page);
+  if (n_items > INT32_MAX / 2) return fail(BD_ERR_INVALID_ARG, "%s: too many items", fn);
+  if (B == 0 || n_items == 0 || q == 0) return BD_OK;
+  if (!items || !q_ptr || !wk || !wv || !out || !q_strides || !w_strides || !out_strides || !kv_strides)
+    return fail(BD_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (kv_max > 0 && (!table || !kv_k || !kv_v)) return fail(BD_ERR_INVALID_ARG, "%s: null page table or store", fn);
+  if (!(sm_scale > 0.f) || sm_scale > 1e30f) return fail(BD_ERR_INVALID_ARG, "%s: bad sm_scale", fn);
+  if (!strides_ok(kv_strides, 3, es) || !strides_ok(q_strides, 3, es) || !strides_ok(w_strides, 3, es) ||
+      !strides_ok(out_strides, 3, es))
+    return fail(BD_ERR_INVALID_ARG, "%s: strides must be >= 0 and 16-byte multiples", fn);
+  if (!aligned16(q_ptr) || !aligned16(wk) || !aligned16(wv) || !aligned16(out) ||
+      (kv_max > 0 && (!aligned16(kv_k) || !aligned16(kv_v))) || ((uintptr_t)items & 3u) != 0)
+    return fail(BD_ERR_INVALID_ARG, "%s: base pointers must be 16-byte aligned", fn);
+  if (kv_strides[1] * es * 64 > INT32_MAX || w_strides[1] * es * 64 > INT32_MAX)
+    return fail(BD_ERR_INVALID_ARG, "%s: key row strides above 32 MB are not supported", fn);
+  if ((int64_t)n_table * 4 > INT32_MAX) return fail(BD_ERR_INVALID_ARG, "%s: page table too long", fn);
+  const AttnPlan plan = attn_plan(dtype, B, Hq, Hkv, d, q, n_items, kv_max, true);
+  const int64_t grid_units = (8 + (int64_t)n_items * Hkv) * plan.nqt * plan.n_split;
+  if (grid_units > ((int64_t)1 << 31) - 1)
+    return fail(BD_ERR_INVALID_ARG, "%s: problem too large for one launch", fn);
+  AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.dtype = dtype; a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.d = d; a.q = q; a.bl = bl;
+  a.mask_mode = BD_MASK_BLOCK_CAUSAL;
+  a.n_rows = n_items; a.n_rows1 = n_items;
+  a.Q = q_ptr; a.wk = wk; a.wv = wv; a.out = out; a.lse = lse;
+  memcpy(a.qs, q_strides, sizeof(a.qs));
+  memcpy(a.ws, w_strides, sizeof(a.ws));
+  memcpy(a.os, out_strides, sizeof(a.os));
+  a.pk = kv_k; a.pv = kv_v; memcpy(a.ps, kv_strides, sizeof(a.ps));
+  a.p_cap = n_pages; a.p_max = kv_max;
+  a.items = items; a.table = table; a.n_table = n_table; a.page = page;
+  a.scale2 = sm_scale * kLog2e;
+  a.nw = plan.nw; a.nqt = plan.nqt; a.chunk = plan.chunk; a.n_split = plan.n_split;
+  if (plan.ws_bytes > 0) {
+    if (!workspace || ws_bytes < plan.ws_bytes)
+      return fail(BD_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, plan.ws_bytes);
+    if (((uintptr_t)workspace & 255u) != 0)
+      return fail(BD_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+    attn_bind_workspace(a, plan, (char *)workspace);
+  }
+  return hip_status(launch_attn(a, (hipStream_t)stream), fn);
 }
 
 int bd_qkv_rope_write(int dtype, int B, int q, int Dm, int Hq, int Hkv, int d, const void *x,

@@ -124,9 +124,25 @@ struct Item {
   int b, h, rl, u, c, nc;
   int kbeg, kend;     // prefix keys of this chunk
   bool with_window;   // last chunk also covers the window
+  int q0, q1;         // window queries of the item (block-table mode)
+  int toff;           // first page-table entry of the item (block-table mode)
 };
 
-__device__ inline bool decode_item(const AttnArgs &a, int bid, Item &it) {
+// Work item of one block-table list position: row, query range, page-table
+// offset and key count, validated (an invalid item is skipped).
+__device__ inline bool bt_item(const AttnArgs &a, int n, int &b, int &q0, int &q1, int &toff, int &P) {
+  const bd_attn_item e = a.items[n];
+  b = e.row;
+  q0 = e.q_begin;
+  q1 = min(e.q_end, a.q);
+  toff = e.table_off;
+  P = clampi(e.kv_len, 0, a.p_max);
+  return b >= 0 && b < a.B && q0 >= 0 && q0 < q1 && toff >= 0 &&
+         (int64_t)toff + cdiv(P, a.page) <= a.n_table;
+}
+
+template <bool BT>
+__device__ inline bool decode_item(const AttnArgs &a, int bid, Item &it, int nq_tile) {
   const int per_group = a.nqt * a.n_split;
   const int xcd = bid & 7;
   const int sigma = bid >> 3;
@@ -137,11 +153,23 @@ __device__ inline bool decode_item(const AttnArgs &a, int bid, Item &it) {
   it.c = mem - it.u * a.n_split;
   const int rank = gamma / a.Hkv;
   it.h = gamma - rank * a.Hkv;
-  it.rl = a.row_order ? a.row_order[rank] : rank;
-  it.r = row_ref(a, it.rl);
-  it.b = it.r.b;
-  if (it.b < 0 || it.b >= a.B) return false;
-  const int P = prefix_len(a, it.r);
+  int P;
+  if constexpr (BT) {
+    // list order is the caller's order: no ranking
+    it.rl = rank;
+    it.r = RowRef{0, false};
+    if (!bt_item(a, rank, it.b, it.q0, it.q1, it.toff, P)) return false;
+    if (it.q0 + it.u * nq_tile >= it.q1) return false;
+  } else {
+    it.rl = a.row_order ? a.row_order[rank] : rank;
+    it.r = row_ref(a, it.rl);
+    it.b = it.r.b;
+    if (it.b < 0 || it.b >= a.B) return false;
+    P = prefix_len(a, it.r);
+    it.q0 = 0;
+    it.q1 = a.q;
+    it.toff = 0;
+  }
   it.nc = P > 0 ? (int)cdiv(P, a.chunk) : 1;
   if (it.c >= it.nc) return false;
   it.kbeg = it.c * a.chunk;
@@ -152,7 +180,8 @@ __device__ inline bool decode_item(const AttnArgs &a, int bid, Item &it) {
 
 // WM: a window mask other than block-causal (a.mask_mode); a separate
 // instance, so the block-causal kernel carries none of its code.
-template <int NW, int G, bool WM>
+// BT: block-table mode (work items over a paged store; bd_attn_block_table).
+template <int NW, int G, bool WM, bool BT>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) {
   using S = Shape<NW, G>;
   __shared__ __attribute__((aligned(16))) bf16 Ks[2][kKTile];
@@ -165,10 +194,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
   const int ln = lane & 31;  // column / M row inside a 32x32 tile
 
   Item it;
-  if (!decode_item(a, blockIdx.x, it)) return;
+  if (!decode_item<BT>(a, blockIdx.x, it, S::NQ)) return;
   const int b = it.b, h = it.h;
-  const int i0 = it.u * S::NQ;
-  const int ilast = min(i0 + S::NQ, a.q) - 1;
+  // queries [q0, q1) of the item (all q window queries outside block-table mode)
+  const int q0 = BT ? it.q0 : 0;
+  const int q1 = BT ? it.q1 : a.q;
+  const int i0 = q0 + it.u * S::NQ;
+  const int ilast = min(i0 + S::NQ, q1) - 1;
   const int win_len = window_limit(ilast, a.bl, a.q);
   const int n_pref = it.kend > it.kbeg ? (int)cdiv(it.kend - it.kbeg, kTK) : 0;
   const int n_tiles = n_pref + (it.with_window ? (int)cdiv(win_len, kTK) : 0);
@@ -178,7 +210,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
   const int qb = wave - g * S::QB;
   const int hq = h * G + g;
   const int qi = i0 + qb * 32 + ln;
-  const bool qok = qi < a.q;
+  const bool qok = qi < q1;
   const int lim = window_limit(qok ? qi : ilast, a.bl, a.q);
   // other window masks: window keys in [w_shared, w_floor) are not visible
   const int w_floor = WM ? window_floor(qok ? qi : ilast, a.bl, a.mask_mode) : 0;
@@ -193,7 +225,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
     for (int ks = 0; ks < kD / 16; ++ks) qop[ks] = qok ? ld_bf16x8(qp + ks * 16) : bf16x8{};
   }
 
-  const PrefixSrc src = prefix_src(a, it.r, h, (int)sizeof(bf16));
+  // prefix base of (row b, KV head h); in block-table mode the page store's
+  // head h (pages are added per tile)
+  const PrefixSrc src = BT ? PrefixSrc{reinterpret_cast<const char *>(a.pk) + (int64_t)h * a.ps[2] * 2,
+                                       reinterpret_cast<const char *>(a.pv) + (int64_t)h * a.ps[2] * 2,
+                                       a.ps[1]}
+                           : prefix_src(a, it.r, h, (int)sizeof(bf16));
   const bf16 *pkb = reinterpret_cast<const bf16 *>(src.k);
   const bf16 *pvb = reinterpret_cast<const bf16 *>(src.v);
   const int64_t p_row = src.row, w_row = a.ws[1];   // key row strides
@@ -231,13 +268,43 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
   // (keep_offsets) so that no later instruction reuses their registers while
   // the loads are outstanding, which would make the compiler wait for them.
   int koff[S::KP], voff[4];
+  // block-table mode: page id of the next prefix tile to load, requested
+  // one tile ahead with a buffer load (it waits on the vector memory counter
+  // with the K/V loads, not on the LDS counter the tile's fragment reads
+  // use); valid rows of the tiles in the two LDS buffers
+  int pg_next = 0;
+  int rows_buf0 = kTK, rows_buf1 = kTK;
+  const auto trsrc = __builtin_amdgcn_make_buffer_rsrc((void *)a.table, (short)0,
+                                                       BT ? a.n_table * 4 : 0, 0x00020000);
+  auto request_page = [&](int tt) {
+    if (BT && tt < n_pref) {
+      const int k0 = it.kbeg + tt * kTK;
+      pg_next = (int)__builtin_amdgcn_raw_buffer_load_b32(trsrc, (it.toff + k0 / a.page) * 4, 0, 0);
+    }
+  };
   auto load = [&](int tt) {
     const bool win = tt >= n_pref;
     const int64_t sp = win ? w_row : p_row;
     const int rowb = (int)(sp * 2);
-    const int base = tile_base(tt), limit = tile_limit(tt);
+    int base = tile_base(tt), limit = tile_limit(tt);
+    const bf16 *kbase = win ? wkb : pkb, *vbase = win ? wvb : pvb;
+    if (BT && !win) {
+      // tile of keys [k0, k0 + 64) of the item's list: position k0 % page
+      // of its page (pages hold multiples of 64 keys); a page id outside the
+      // store contributes no rows
+      const int k0 = base;
+      const int pg = __builtin_amdgcn_readfirstlane(pg_next);
+      const bool pok = pg >= 0 && pg < a.p_cap;
+      const int64_t off = (int64_t)(pok ? pg : 0) * a.ps[0] + (int64_t)(k0 % a.page) * p_row;
+      kbase = pkb + off - (int64_t)k0 * p_row;   // rsrc adds base * row again
+      vbase = pvb + off - (int64_t)k0 * p_row;
+      if (!pok) limit = base;
+      const int rows = min(limit - base, kTK);
+      if (tt & 1) rows_buf1 = rows;
+      else rows_buf0 = rows;
+    }
     if (stage_k) {
-      const auto r = rsrc(win ? wkb : pkb, sp, base, limit);
+      const auto r = rsrc(kbase, sp, base, limit);
 #pragma unroll
       for (int p = 0; p < S::KP; ++p) {
         const int piece = ktid + p * kstep;
@@ -246,7 +313,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
       }
     }
     if (stage_v) {
-      const auto r = rsrc(win ? wvb : pvb, sp, base, limit);
+      const auto r = rsrc(vbase, sp, base, limit);
       const int k4 = tid & 15, db = (tid >> 4) & 15;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
@@ -254,6 +321,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
         vreg[jj] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff[jj], 0, 0));
       }
     }
+    request_page(tt + 1);
   };
   auto keep_offsets = [&]() {
 #pragma unroll
@@ -328,7 +396,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    const int base = tile_base(tt), limit = tile_limit(tt);
+    const int base = tile_base(tt);
+    // keys of the tile past `limit` are not visible (block-table prefix
+    // tiles: the rows their page holds)
+    const int limit = (BT && tt < n_pref) ? base + (buf ? rows_buf1 : rows_buf0) : tile_limit(tt);
     const bool win = tt >= n_pref;
     if (win || base + kTK > limit) {
       // register r of half kt holds key base + kt*32 + (r/4)*8 + hh*4 + r%4;
@@ -410,6 +481,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
   };
 
   // ---- tile loop: tile tt+1 is loaded during tile tt (double-buffered LDS)
+  request_page(0);
   if (n_tiles > 0) {
     load(0);
     store(0);
@@ -478,7 +550,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
 // the partials' [dims / 4][column][4] order of a column group they read one
 // 128-byte line.
 // U: partials requested per round of loads (8, or 32 for long chunk lists).
-template <int NW, int G, int U>
+template <int NW, int G, int U, bool BT>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   using S = Shape<NW, G>;
   constexpr int CPB = 256 / (kD / 4);  // columns per block: 8
@@ -493,8 +565,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int cg = col / 32;
   const int g = cg / S::QB;
   const int qb = cg - g * S::QB;
-  const int qi = u * S::NQ + qb * 32 + (col & 31);
-  if (qi >= a.q) return;
+  const int qoff = u * S::NQ + qb * 32 + (col & 31);
+  if (!BT && qoff >= a.q) return;
   const int64_t prow0 = unit * a.n_split * S::NCOL + col;
   // the partials of the first U chunks are requested before the row lookup
   // (row id, then prefix length), so the two latencies overlap; chunks past
@@ -512,10 +584,19 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     }
   };
   load(0, a.n_split);
-  const RowRef rr = row_ref(a, rl);
-  const int b = rr.b;
-  if (b < 0 || b >= a.B) return;
-  const int P = prefix_len(a, rr);
+  int b, P, qi;
+  if constexpr (BT) {
+    int q0, q1, toff;
+    if (!bt_item(a, rl, b, q0, q1, toff, P)) return;
+    qi = q0 + qoff;
+    if (qi >= q1) return;
+  } else {
+    const RowRef rr = row_ref(a, rl);
+    b = rr.b;
+    if (b < 0 || b >= a.B) return;
+    P = prefix_len(a, rr);
+    qi = qoff;
+  }
   const int nc = P > 0 ? (int)cdiv(P, a.chunk) : 1;
   if (nc == 1) return;  // written directly by the attention kernel
   // online merge in chunk order (every chunk holds visible prefix keys, so
@@ -795,7 +876,8 @@ bool attn_generic_supported(int dtype, int d) {
 constexpr int kCUs = 256;
 constexpr int kMinChunk = 256;
 
-AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int d, int q, int n_rows, int p_max) {
+AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int d, int q, int n_rows, int p_max,
+                   bool keep_order) {
   (void)B;
   AttnPlan p{};
   const int G = Hkv > 0 ? Hq / Hkv : 1;
@@ -822,7 +904,7 @@ AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int d, int q, int n_rows, 
       p.n_split = (int)cdiv(p_max, ch);
     }
   }
-  p.order = n_rows > 1 && n_rows <= kOrderMax && units * p.n_split > slots;
+  p.order = !keep_order && n_rows > 1 && n_rows <= kOrderMax && units * p.n_split > slots;
   size_t off = 0;
   p.off_order = off;
   if (p.order) off += align256((size_t)n_rows * sizeof(int));
@@ -841,6 +923,7 @@ AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int d, int q, int n_rows, 
 template <int NW, int G>
 static hipError_t launch_mfma(const AttnArgs &a, hipStream_t s) {
   const bool wm = a.mask_mode != BD_MASK_BLOCK_CAUSAL;
+  const bool bt = a.items != nullptr;
   using S = Shape<NW, G>;
   const int64_t n_groups = (int64_t)a.n_rows * a.Hkv;
   const int64_t per_group = (int64_t)a.nqt * a.n_split;
@@ -850,19 +933,27 @@ static hipError_t launch_mfma(const AttnArgs &a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (wm)
-    hipLaunchKernelGGL((attn_mfma_kernel<NW, G, true>), dim3((unsigned)grid), dim3(S::NT), 0, s, a);
+  if (bt)
+    hipLaunchKernelGGL((attn_mfma_kernel<NW, G, false, true>), dim3((unsigned)grid), dim3(S::NT), 0, s, a);
+  else if (wm)
+    hipLaunchKernelGGL((attn_mfma_kernel<NW, G, true, false>), dim3((unsigned)grid), dim3(S::NT), 0, s, a);
   else
-    hipLaunchKernelGGL((attn_mfma_kernel<NW, G, false>), dim3((unsigned)grid), dim3(S::NT), 0, s, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<NW, G, false, false>), dim3((unsigned)grid), dim3(S::NT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split <= 1) return e;
   const int64_t cgrid = n_groups * a.nqt * (S::NCOL / 8);
   // one round of loads covers up to 8 chunks; longer lists (pools of
   // thousands of keys) take 32 per round, fewer dependent round trips
-  if (a.n_split > 8)
-    hipLaunchKernelGGL((attn_combine_kernel<NW, G, 32>), dim3((unsigned)cgrid), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((attn_combine_kernel<NW, G, 8>), dim3((unsigned)cgrid), dim3(256), 0, s, a);
+  if (bt) {
+    if (a.n_split > 8)
+      hipLaunchKernelGGL((attn_combine_kernel<NW, G, 32, true>), dim3((unsigned)cgrid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((attn_combine_kernel<NW, G, 8, true>), dim3((unsigned)cgrid), dim3(256), 0, s, a);
+  } else if (a.n_split > 8) {
+    hipLaunchKernelGGL((attn_combine_kernel<NW, G, 32, false>), dim3((unsigned)cgrid), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((attn_combine_kernel<NW, G, 8, false>), dim3((unsigned)cgrid), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

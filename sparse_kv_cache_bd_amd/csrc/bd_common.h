@@ -118,6 +118,13 @@ struct AttnArgs {
   int64_t ps2[3];
   int p_cap2, p_max2;
   float scale2;  // sm_scale * log2(e)
+  // block-table mode (bd_attn_block_table): the list positions are work
+  // items {row, q_begin, q_end, table_off, kv_len} in the caller's order;
+  // an item's keys are kv_len keys on the pages table[table_off ..] of the
+  // paged store pk/pv (strides ps = {page, pos, head}; p_cap = pages).
+  const bd_attn_item *items;
+  const int32_t *table;
+  int n_table, page;
   // launch plan (attn_plan)
   int nw;                 // waves per block of the MFMA path (4 or 8)
   int nqt, chunk, n_split;
@@ -132,7 +139,8 @@ struct AttnPlan {
   bool order;
   size_t off_order, off_part_o, off_part_ml, ws_bytes;
 };
-AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int d, int q, int n_rows, int p_max);
+AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int d, int q, int n_rows, int p_max,
+                   bool keep_order = false);
 hipError_t launch_attn(const AttnArgs &a, hipStream_t s);
 
 // One prefix source of an attention call: its row list and the prefix

@@ -24,7 +24,7 @@ def L():
 
 def test_exports_every_header_function(L):
     names = bd.header_functions()
-    assert len(names) == 16
+    assert len(names) == 18
     for n in names:
         assert hasattr(L, n), n
 
@@ -254,6 +254,57 @@ def test_attn_noalloc_rejects_oversized_scratch(L):
     assert need > cap
     assert _attn_noalloc(L, **kw) == bd.BD_ERR_WORKSPACE
     assert "scratch" in bd.last_error() and str(need) in bd.last_error()
+
+
+def _attn_bt(L, ws_bytes=None, **kw):
+    a = dict(dtype=bd.BD_BF16, B=2, Hq=32, Hkv=8, d=128, q=64, bl=32, items=FAKE, n_items=2,
+             table=FAKE2, n_table=100, kv=FAKE, kvv=FAKE2, kvs=I3(128 * 1024, 1024, 128),
+             n_pages=50, page=128, kv_max=4000, Q=FAKE, qs=I3(64 * 4096, 4096, 128), wk=FAKE,
+             wv=FAKE2, wsd=I3(1 << 22, 1024, 128), scale=0.088, out=FAKE2,
+             os=I3(64 * 4096, 4096, 128), lse=None, ws=FAKE)
+    a.update(kw)
+    need = bd.attn_block_table_workspace_size(a["dtype"], a["Hq"], a["Hkv"], a["d"], a["q"],
+                                              a["n_items"], a["kv_max"])
+    wsb = need if ws_bytes is None else ws_bytes
+    return L.bd_attn_block_table(a["dtype"], a["B"], a["Hq"], a["Hkv"], a["d"], a["q"], a["bl"],
+                                 a["items"], a["n_items"], a["table"], a["n_table"], a["kv"],
+                                 a["kvv"], a["kvs"], a["n_pages"], a["page"], a["kv_max"], a["Q"],
+                                 a["qs"], a["wk"], a["wv"], a["wsd"], a["scale"], a["out"], a["os"],
+                                 a["lse"], a["ws"], wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=bd.BD_F32), bd.BD_ERR_UNSUPPORTED),       # MFMA path only
+    (dict(d=64), bd.BD_ERR_UNSUPPORTED),
+    (dict(Hq=24), bd.BD_ERR_UNSUPPORTED),                 # G = 3
+    (dict(Hq=33), bd.BD_ERR_INVALID_ARG),
+    (dict(page=96), bd.BD_ERR_INVALID_ARG),               # not a multiple of 64
+    (dict(page=0), bd.BD_ERR_INVALID_ARG),
+    (dict(n_items=-1), bd.BD_ERR_INVALID_ARG),
+    (dict(items=None), bd.BD_ERR_INVALID_ARG),
+    (dict(table=None), bd.BD_ERR_INVALID_ARG),
+    (dict(kv=MISALIGNED), bd.BD_ERR_INVALID_ARG),
+    (dict(kvs=I3(128 * 1024, 1024, 100)), bd.BD_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), bd.BD_ERR_INVALID_ARG),
+    (dict(ws=None), bd.BD_ERR_WORKSPACE),
+    (dict(n_items=0, items=None), bd.BD_OK),
+    (dict(B=0), bd.BD_OK),
+])
+def test_attn_block_table_validation(L, kw, code):
+    assert _attn_bt(L, **kw) == code
+    if code != bd.BD_OK:
+        assert bd.last_error().startswith("bd_attn_block_table")
+
+
+def test_attn_block_table_workspace(L):
+    # few items over long key lists: split partials, no row order (the
+    # caller's order is kept)
+    few = bd.attn_block_table_workspace_size(bd.BD_BF16, 32, 8, 128, 32, 4, 1638)
+    assert few == bd.attn_workspace_size(bd.BD_BF16, 4, 32, 8, 128, 32, 4, 1638) > 0
+    assert bd.attn_block_table_workspace_size(bd.BD_BF16, 32, 8, 128, 128, 64, 16384) == 0
+    need = bd.attn_block_table_workspace_size(bd.BD_BF16, 32, 8, 128, 64, 2, 4000)
+    assert need > 0
+    assert _attn_bt(L, ws_bytes=need - 1) == bd.BD_ERR_WORKSPACE
 
 
 def _attn_masked(L, mode, **kw):
