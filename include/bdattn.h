@@ -242,7 +242,11 @@ int bd_select_multi(int dtype, int B, int Hq, int Hkv, int d, const void *q,
  *   q, out    [B, q, Hq, d], strides {row, query, head}.  out has q's dtype.
  *   pk/pv     [B, p_cap, Hkv, d]; p_len device int32 [B], clamped to
  *             [0, min(p_max, p_cap)].  Prefix rows at or past P_b are never
- *             read, so they may hold anything (NaN included).
+ *             read, so they may hold anything (NaN included).  Every visible
+ *             key and value, and every query, must be finite: the kernels
+ *             are built without NaN semantics (maxima take no NaN-quieting
+ *             step), so a NaN or infinity there gives an unspecified
+ *             output, not necessarily NaN.
  *   wk/wv     [B, q, Hkv, d] (any strides, e.g. a view of the cache tail).
  *   lse       optional device float [B, Hq, q], contiguous.
  *   workspace at least bd_attn_workspace_size(...) bytes, 256-byte aligned
@@ -438,6 +442,67 @@ int bd_qkv_rope_write(int dtype, int B, int q, int Dm, int Hq, int Hkv, int d,
                       const int64_t q_strides[3], void *k_cache, void *v_cache,
                       const int64_t c_strides[3], int c_cap,
                       const int32_t *dst_pos, void *stream);
+
+/*
+ * Device check mode.  The per-row values the operations read from device
+ * memory (row ids, lengths, offsets, gather indices, page tables) are
+ * range-checked in the kernels, which clamp or skip what is out of range
+ * without any out-of-bounds access, silently.  A caller that wants to know
+ * calls the matching bd_check_* function on the same stream before the
+ * operation, with the same values: it ORs one BD_CHECK_* bit per kind of
+ * violation into *status (a device uint32 the caller clears; the checks
+ * never clear it, so several can share one word) and writes nothing else.
+ * The checks are asynchronous, allocate nothing and can be captured in a HIP
+ * graph.  (No page states a status word: this is the caller's view of the
+ * contract of each operation, as its comment above states it.)
+ *
+ * Host-side argument errors are returned as for the operations
+ * (BD_ERR_INVALID_ARG with bd_last_error(); nothing is launched).
+ */
+#define BD_CHECK_ROW     0x01u /* a row id outside [0, B)                     */
+#define BD_CHECK_LENGTH  0x02u /* a per-row length outside its range (p_len,
+                                  s_len, k_sel, k_cnt, kv_len): clamped       */
+#define BD_CHECK_OFFSET  0x04u /* a scatter offset with o_b < 0 or
+                                  o_b + q > data_cap: row skipped              */
+#define BD_CHECK_ALIAS   0x08u /* an aliased scatter whose target overlaps its
+                                  source window (o_b + q > t and o_b != t)     */
+#define BD_CHECK_INDEX   0x10u /* a gather index outside [0, src_cap) in a
+                                  row's first k_cnt slots: slot left unchanged */
+#define BD_CHECK_PAGE    0x20u /* a page id outside [0, n_pages) (no keys), or
+                                  an item's pages past the table (skipped)     */
+#define BD_CHECK_QUERIES 0x40u /* an item's query range empty or starting
+                                  outside [0, q): item skipped                 */
+
+/* bd_attn_packed (and _masked, _noalloc; each list of _dual): row ids in
+ * [0, B) (row_ids NULL = rows 0 .. n_rows-1) and p_len[b] in
+ * [0, min(p_max, p_cap, p_hi)].  p_hi is the caller's own bound: t = C - q
+ * for the FlowBlock call, where a prefix past t would overlap the window
+ * tail; p_cap (or anything larger) otherwise. */
+int bd_check_attn(int B, const int32_t *row_ids, int n_rows, const int32_t *p_len,
+                  int p_max, int p_cap, int p_hi, uint32_t *status, void *stream);
+/* bd_kv_scatter: row ids in [0, B); o_b >= 0 and o_b + q <= data_cap; with
+ * aliased != 0 (present and data are one tensor) also o_b + q <= t or
+ * o_b == t. */
+int bd_check_scatter(int B, int q, int t, int data_cap, const int32_t *o,
+                     const int32_t *row_ids, int n_rows, int aliased,
+                     uint32_t *status, void *stream);
+/* bd_gather: k_cnt[b] in [0, k_max] and idx[b, h, j] in [0, src_cap) for
+ * j < k_cnt[b] (idx [B, Hkv, k_max], contiguous). */
+int bd_check_gather(int B, int Hkv, const int32_t *idx, int k_max,
+                    const int32_t *k_cnt, int src_cap, uint32_t *status,
+                    void *stream);
+/* bd_select / bd_select_multi: s_len[b] in [0, min(s_max, k_cap)] and
+ * k_sel[b] in [0, k_max]. */
+int bd_check_select(int B, const int32_t *s_len, int s_max, int k_cap,
+                    const int32_t *k_sel, int k_max, uint32_t *status,
+                    void *stream);
+/* bd_attn_block_table: every item's row in [0, B), q_begin in [0, q) with
+ * q_end > q_begin, kv_len in [0, kv_max], table_off >= 0 with its
+ * ceil(kv_len / page) pages inside the table, and every one of those page
+ * ids in [0, n_pages). */
+int bd_check_block_table(int B, int q, const bd_attn_item *items, int n_items,
+                         const int32_t *table, int n_table, int n_pages,
+                         int page, int kv_max, uint32_t *status, void *stream);
 
 /*
  * bd_mask_materialize: test hook for the attention mask.  Writes

@@ -21,6 +21,9 @@ BD_OK, BD_ERR_INVALID_ARG, BD_ERR_UNSUPPORTED, BD_ERR_HIP, BD_ERR_WORKSPACE = 0,
 BD_BF16, BD_F32 = 0, 1
 BD_REP_MEAN, BD_REP_ROW = 0, 1
 BD_MASK_BLOCK_CAUSAL, BD_MASK_ISOLATED, BD_MASK_SHARED_FIRST = 0, 1, 2
+# device check mode: status bits (bd_check_*)
+CHECK_BITS = {"row": 0x01, "length": 0x02, "offset": 0x04, "alias": 0x08, "index": 0x10,
+              "page": 0x20, "queries": 0x40}
 MASK_MODES = {"block_causal": BD_MASK_BLOCK_CAUSAL, "isolated": BD_MASK_ISOLATED,
               "shared_first": BD_MASK_SHARED_FIRST}
 
@@ -65,6 +68,11 @@ _SIGS = {
                                    _vp, _i, _vp, _i, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp,
                                    _vp, _sz, _vp]),
     "bd_mask_materialize": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp]),
+    "bd_check_attn": (_i, [_i, _vp, _i, _vp, _i, _i, _i, _vp, _vp]),
+    "bd_check_scatter": (_i, [_i, _i, _i, _i, _vp, _vp, _i, _i, _vp, _vp]),
+    "bd_check_gather": (_i, [_i, _i, _vp, _i, _vp, _i, _vp, _vp]),
+    "bd_check_select": (_i, [_i, _vp, _i, _i, _vp, _i, _vp, _vp]),
+    "bd_check_block_table": (_i, [_i, _i, _vp, _i, _vp, _i, _i, _i, _i, _vp, _vp]),
     "bd_qkv_rope_write": (_i, [_i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, ctypes.c_float,
                                _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp]),
 }
@@ -518,3 +526,71 @@ def mask_materialize(B: int, C: int, q: int, bl: int, o, mask_mode: str = "block
     _check(lib().bd_mask_materialize(B, C, q, bl, MASK_MODES[mask_mode], _ptr(o), _ptr(out),
                                      _stream()))
     return out
+
+
+# ---------------------------------------------------------------------------
+# Device check mode: each function ORs BD_CHECK_* bits into ``status`` (a
+# one-element int32 GPU tensor the caller clears) on the current stream.
+
+def new_status(device=None) -> torch.Tensor:
+    return torch.zeros(1, dtype=torch.int32, device=device or "cuda")
+
+
+def check_names(status: torch.Tensor) -> list[str]:
+    """Names of the bits set in a status word (reads it on the host)."""
+    v = int(status.item()) & 0xFFFFFFFF
+    return [n for n, bit in CHECK_BITS.items() if v & bit]
+
+
+def _status(st):
+    if not isinstance(st, torch.Tensor) or not st.is_cuda or st.dtype != torch.int32 or st.numel() < 1:
+        raise ValueError("status must be an int32 GPU tensor with at least one element")
+    return st
+
+
+def check_attn(status, B: int, p_len, p_max: int, p_cap: int, p_hi: int | None = None, row_ids=None):
+    """Row ids in [0, B) and p_len in [0, min(p_max, p_cap, p_hi)]."""
+    p_len = _rows(p_len, "p_len", B)
+    rid = _i32(row_ids, "row_ids") if row_ids is not None else None
+    n = B if rid is None else rid.numel()
+    hi = p_cap if p_hi is None else p_hi
+    _check(lib().bd_check_attn(B, _ptr(rid), n, _ptr(p_len), p_max, p_cap, hi, _ptr(_status(status)),
+                               _stream()))
+
+
+def check_scatter(status, B: int, q: int, t: int, data_cap: int, o, aliased: bool, row_ids=None):
+    """o_b in [0, data_cap - q]; aliased: also o_b + q <= t or o_b == t."""
+    o = _rows(o, "o", B)
+    rid = _i32(row_ids, "row_ids") if row_ids is not None else None
+    n = B if rid is None else rid.numel()
+    _check(lib().bd_check_scatter(B, q, t, data_cap, _ptr(o), _ptr(rid), n, int(bool(aliased)),
+                                  _ptr(_status(status)), _stream()))
+
+
+def check_gather(status, idx, k_cnt, src_cap: int):
+    """k_cnt in [0, k_max]; idx of the copied slots in [0, src_cap)."""
+    idx = _i32(idx, "idx")
+    if idx.dim() != 3:
+        raise ValueError("idx must be [B, Hkv, k_max]")
+    B, Hkv, k_max = idx.shape
+    k_cnt = _rows(k_cnt, "k_cnt", B)
+    _check(lib().bd_check_gather(B, Hkv, _ptr(idx), k_max, _ptr(k_cnt), src_cap,
+                                 _ptr(_status(status)), _stream()))
+
+
+def check_select(status, s_len, s_max: int, k_cap: int, k_sel, k_max: int):
+    """s_len in [0, min(s_max, k_cap)] and k_sel in [0, k_max]."""
+    B = s_len.numel()
+    s_len, k_sel = _rows(s_len, "s_len", B), _rows(k_sel, "k_sel", B)
+    _check(lib().bd_check_select(B, _ptr(s_len), s_max, k_cap, _ptr(k_sel), k_max,
+                                 _ptr(_status(status)), _stream()))
+
+
+def check_block_table(status, B: int, q: int, items, table, n_pages: int, page: int, kv_max: int):
+    """Items' rows, query ranges, key counts, table ranges and page ids."""
+    items = _i32(items, "items")
+    if items.dim() != 2 or items.shape[1] != 5:
+        raise ValueError("items must be int32 [n_items, 5]")
+    table = _i32(table, "table")
+    _check(lib().bd_check_block_table(B, q, _ptr(items), items.shape[0], _ptr(table), table.numel(),
+                                      n_pages, page, kv_max, _ptr(_status(status)), _stream()))

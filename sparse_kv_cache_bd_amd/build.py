@@ -20,7 +20,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbdattn.so")
 
 SOURCES = ["bd_api.hip", "bd_move.hip", "bd_attn.hip", "bd_select.hip", "bd_produce.hip",
-           "bd_noalloc.hip"]
+           "bd_noalloc.hip", "bd_check.hip"]
 
 ARCH = "gfx950"
 

@@ -492,6 +492,71 @@ int bd_qkv_rope_write(int dtype, int B, int q, int Dm, int Hq, int Hkv, int d, c
   return hip_status(launch_produce(a, (hipStream_t)stream), "bd_qkv_rope_write launch");
 }
 
+int bd_check_attn(int B, const int32_t *row_ids, int n_rows, const int32_t *p_len, int p_max, int p_cap,
+                  int p_hi, uint32_t *status, void *stream) {
+  g_err[0] = 0;
+  if (B < 0 || n_rows < 0 || p_max < 0 || p_cap < 0 || p_hi < 0)
+    return fail(BD_ERR_INVALID_ARG, "bd_check_attn: negative size");
+  if (!row_ids && n_rows > B) return fail(BD_ERR_INVALID_ARG, "bd_check_attn: n_rows > B without row_ids");
+  if (n_rows == 0) return BD_OK;
+  if (!status || !p_len) return fail(BD_ERR_INVALID_ARG, "bd_check_attn: null pointer");
+  const int hi = p_max < p_cap ? (p_max < p_hi ? p_max : p_hi) : (p_cap < p_hi ? p_cap : p_hi);
+  return hip_status(launch_check_attn(B, row_ids, n_rows, p_len, hi, status, (hipStream_t)stream),
+                    "bd_check_attn launch");
+}
+
+int bd_check_scatter(int B, int q, int t, int data_cap, const int32_t *o, const int32_t *row_ids,
+                     int n_rows, int aliased, uint32_t *status, void *stream) {
+  g_err[0] = 0;
+  if (B < 0 || q < 0 || t < 0 || data_cap < 0 || n_rows < 0)
+    return fail(BD_ERR_INVALID_ARG, "bd_check_scatter: negative size");
+  if (!row_ids && n_rows > B) return fail(BD_ERR_INVALID_ARG, "bd_check_scatter: n_rows > B without row_ids");
+  if (n_rows == 0) return BD_OK;
+  if (!status || !o) return fail(BD_ERR_INVALID_ARG, "bd_check_scatter: null pointer");
+  return hip_status(launch_check_scatter(B, q, t, data_cap, o, row_ids, n_rows, aliased, status,
+                                         (hipStream_t)stream),
+                    "bd_check_scatter launch");
+}
+
+int bd_check_gather(int B, int Hkv, const int32_t *idx, int k_max, const int32_t *k_cnt, int src_cap,
+                    uint32_t *status, void *stream) {
+  g_err[0] = 0;
+  if (B < 0 || Hkv <= 0 || k_max < 0 || src_cap < 0)
+    return fail(BD_ERR_INVALID_ARG, "bd_check_gather: negative or zero size");
+  if ((int64_t)B * Hkv > 65535) return fail(BD_ERR_INVALID_ARG, "bd_check_gather: B * Hkv too large");
+  if (B == 0 || k_max == 0) return BD_OK;
+  if (!status || !idx || !k_cnt) return fail(BD_ERR_INVALID_ARG, "bd_check_gather: null pointer");
+  return hip_status(launch_check_gather(B, Hkv, idx, k_max, k_cnt, src_cap, status, (hipStream_t)stream),
+                    "bd_check_gather launch");
+}
+
+int bd_check_select(int B, const int32_t *s_len, int s_max, int k_cap, const int32_t *k_sel, int k_max,
+                    uint32_t *status, void *stream) {
+  g_err[0] = 0;
+  if (B < 0 || s_max < 0 || k_cap < 0 || k_max < 0)
+    return fail(BD_ERR_INVALID_ARG, "bd_check_select: negative size");
+  if (B == 0) return BD_OK;
+  if (!status || !s_len || !k_sel) return fail(BD_ERR_INVALID_ARG, "bd_check_select: null pointer");
+  return hip_status(launch_check_select(B, s_len, s_max < k_cap ? s_max : k_cap, k_sel, k_max, status,
+                                        (hipStream_t)stream),
+                    "bd_check_select launch");
+}
+
+int bd_check_block_table(int B, int q, const bd_attn_item *items, int n_items, const int32_t *table,
+                         int n_table, int n_pages, int page, int kv_max, uint32_t *status, void *stream) {
+  g_err[0] = 0;
+  if (B < 0 || q < 0 || n_items < 0 || n_table < 0 || n_pages < 0 || kv_max < 0)
+    return fail(BD_ERR_INVALID_ARG, "bd_check_block_table: negative size");
+  if (page <= 0 || page % 64 != 0)
+    return fail(BD_ERR_INVALID_ARG, "bd_check_block_table: page %d must be a positive multiple of 64", page);
+  if (n_items == 0) return BD_OK;
+  if (!status || !items || (n_table > 0 && !table))
+    return fail(BD_ERR_INVALID_ARG, "bd_check_block_table: null pointer");
+  return hip_status(launch_check_table(B, q, items, n_items, table, n_table, n_pages, page, kv_max, status,
+                                       (hipStream_t)stream),
+                    "bd_check_block_table launch");
+}
+
 int bd_mask_materialize(int B, int C, int q, int bl, int mask_mode, const int32_t *o, uint8_t *out,
                         void *stream) {
   g_err[0] = 0;

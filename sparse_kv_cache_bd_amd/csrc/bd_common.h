@@ -185,6 +185,19 @@ hipError_t launch_select(const SelectArgs &a, hipStream_t s);
 size_t select_multi_workspace(int B, int Hkv, int s_max);
 hipError_t launch_select_multi(const SelectArgs &a, hipStream_t s);
 
+// Device check mode (bd_check.hip): OR BD_CHECK_* bits into *status.
+hipError_t launch_check_attn(int B, const int32_t *row_ids, int n_rows, const int32_t *p_len, int p_hi,
+                             uint32_t *status, hipStream_t s);
+hipError_t launch_check_scatter(int B, int q, int t, int data_cap, const int32_t *o, const int32_t *row_ids,
+                                int n_rows, int aliased, uint32_t *status, hipStream_t s);
+hipError_t launch_check_gather(int B, int Hkv, const int32_t *idx, int k_max, const int32_t *k_cnt,
+                               int src_cap, uint32_t *status, hipStream_t s);
+hipError_t launch_check_select(int B, const int32_t *s_len, int s_hi, const int32_t *k_sel, int k_max,
+                               uint32_t *status, hipStream_t s);
+hipError_t launch_check_table(int B, int q, const bd_attn_item *items, int n_items, const int32_t *table,
+                              int n_table, int n_pages, int page, int kv_max, uint32_t *status,
+                              hipStream_t s);
+
 // Fused cache producer: QKV projection + RoPE + cache write (d = 128, bf16).
 struct ProduceArgs {
   int B, q, Dm, Hq, Hkv, c_cap;

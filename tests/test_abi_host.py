@@ -24,7 +24,7 @@ def L():
 
 def test_exports_every_header_function(L):
     names = bd.header_functions()
-    assert len(names) == 18
+    assert len(names) == 23
     for n in names:
         assert hasattr(L, n), n
 
@@ -464,3 +464,26 @@ int main(void) {
     assert r.returncode == 0, r.stderr
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0 and r.stdout.strip() == "ok", (r.returncode, r.stdout, r.stderr)
+
+
+def test_check_validation(L):
+    """The check functions validate their host arguments before any launch;
+    empty calls do nothing."""
+    S = FAKE2
+    assert L.bd_check_attn(2, None, 2, FAKE, 10, 10, 10, None, None) == bd.BD_ERR_INVALID_ARG
+    assert L.bd_check_attn(2, None, 3, FAKE, 10, 10, 10, S, None) == bd.BD_ERR_INVALID_ARG
+    assert L.bd_check_attn(-1, None, 0, FAKE, 10, 10, 10, S, None) == bd.BD_ERR_INVALID_ARG
+    assert L.bd_check_attn(2, None, 0, None, 10, 10, 10, None, None) == bd.BD_OK
+    assert L.bd_check_scatter(2, 32, 96, 128, None, None, 2, 1, S, None) == bd.BD_ERR_INVALID_ARG
+    assert L.bd_check_scatter(2, -1, 96, 128, FAKE, None, 2, 1, S, None) == bd.BD_ERR_INVALID_ARG
+    assert L.bd_check_scatter(2, 32, 96, 128, FAKE, None, 0, 1, None, None) == bd.BD_OK
+    assert L.bd_check_gather(2, 0, FAKE, 4, FAKE, 10, S, None) == bd.BD_ERR_INVALID_ARG
+    assert L.bd_check_gather(70000, 1, FAKE, 4, FAKE, 10, S, None) == bd.BD_ERR_INVALID_ARG
+    assert L.bd_check_gather(2, 8, FAKE, 4, None, 10, S, None) == bd.BD_ERR_INVALID_ARG
+    assert L.bd_check_gather(2, 8, None, 0, None, 10, None, None) == bd.BD_OK
+    assert L.bd_check_select(2, FAKE, 10, 10, FAKE, 5, None, None) == bd.BD_ERR_INVALID_ARG
+    assert L.bd_check_select(0, None, 10, 10, None, 5, None, None) == bd.BD_OK
+    assert L.bd_check_block_table(2, 64, FAKE, 2, FAKE, 10, 5, 96, 100, S, None) == bd.BD_ERR_INVALID_ARG
+    assert L.bd_check_block_table(2, 64, None, 2, FAKE, 10, 5, 64, 100, S, None) == bd.BD_ERR_INVALID_ARG
+    assert L.bd_check_block_table(2, 64, FAKE, 0, None, 0, 5, 64, 100, None, None) == bd.BD_OK
+    assert bd.last_error() == ""
