@@ -66,6 +66,8 @@ int bd_kv_scatter(int dtype, int B, int Hkv, int d, int q, int n_layers, const v
   if (B == 0 || q == 0 || n_layers == 0 || n_rows == 0) return BD_OK;
   if ((d * es) % 16 != 0)
     return fail(BD_ERR_UNSUPPORTED, "bd_kv_scatter: d * element size must be a multiple of 16 bytes");
+  if ((int64_t)Hkv * d * es > 16384)
+    return fail(BD_ERR_UNSUPPORTED, "bd_kv_scatter: one position of all KV heads exceeds 16 KB");
   if (!present_strides || !data_strides || !o)
     return fail(BD_ERR_INVALID_ARG, "bd_kv_scatter: null strides or offsets");
   if (!present_k || !data_k) return fail(BD_ERR_INVALID_ARG, "bd_kv_scatter: null K pointers");
@@ -104,6 +106,7 @@ int bd_gather(int dtype, int B, int Hkv, int d, const void *k_src, const void *v
   if (B == 0 || k_max == 0) return BD_OK;
   if ((d * es) % 16 != 0)
     return fail(BD_ERR_UNSUPPORTED, "bd_gather: d * element size must be a multiple of 16 bytes");
+  if (d * es > 16384) return fail(BD_ERR_UNSUPPORTED, "bd_gather: one head row exceeds 16 KB");
   if (!k_src || !k_pool || !idx || !k_cnt || !src_strides || !pool_strides)
     return fail(BD_ERR_INVALID_ARG, "bd_gather: null pointer");
   if ((v_src == nullptr) != (v_pool == nullptr))

@@ -13,7 +13,13 @@ namespace {
 constexpr int kThreads = 256;
 
 __device__ inline uint4 ld16(const char *p) { return *reinterpret_cast<const uint4 *>(p); }
-__device__ inline void st16(char *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
+// Stores are nontemporal (streaming): the copies' destinations are not read
+// again by the same launch, and the hint keeps them from displacing cached
+// lines (the scatter's and gather's sources) on their way to HBM.
+__device__ inline void st16(char *p, uint4 v) {
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(p));
+}
 
 // One block moves kTok window positions of one (layer, row, tensor) for all
 // KV heads.  vpr = 16-byte vectors per (pos, head) row = d * es / 16.

@@ -135,3 +135,78 @@ def test_mask_hook_bitexact(bd, C, bl, W):
     m = bd.mask_materialize(len(o), C, q, bl, torch.from_numpy(o).cuda())
     torch.cuda.synchronize()
     assert np.array_equal(m.cpu().numpy().astype(bool), orc.eq6_mask(C, q, bl, o))
+
+
+def test_scatter_many_items_per_block(bd):
+    """More work items than resident blocks (4 layers x 64 rows x 2 tensors
+    x 16 chunks of 8 positions = 8192 > 2048): every block walks several
+    items with the next item's loads in flight during the current stores."""
+    note("scatter: 8192 items over 2048 blocks")
+    rs = np.random.default_rng(77)
+    L, B, C, Hkv, d, q = 4, 64, 300, 8, 128, 128
+    t = C - q
+    data = torch.from_numpy(rs.standard_normal((L, B, C, Hkv, d)).astype(np.float32)).bfloat16()
+    o = rs.integers(0, t - q + 1, size=B).astype(np.int32)
+    o[5] = -1                                        # skipped rows among the items
+    o[6] = t                                         # identity write
+    dk, dv = data.cuda(), (-data).cuda()
+    bd.kv_scatter(dk, dv, dk, dv, torch.from_numpy(o).cuda(), t, q)
+    torch.cuda.synchronize()
+    rows = [b for b in range(B) if o[b] >= 0]
+    assert np.array_equal(bits(dk), orc.kv_scatter(bits(data), bits(data), o, t, q, rows=rows))
+    assert np.array_equal(bits(dv), orc.kv_scatter(bits(-data), bits(-data), o, t, q, rows=rows))
+
+
+def _gather_case(B, S, Hkv, d, kmax, seed, empty_frac=0.0):
+    rs = np.random.default_rng(seed)
+    src_k = torch.from_numpy(rs.standard_normal((B, S, Hkv, d)).astype(np.float32)).bfloat16()
+    k_cnt = rs.integers(1, kmax + 1, size=B).astype(np.int32)
+    k_cnt[rs.random(B) < empty_frac] = 0
+    idx = np.full((B, Hkv, kmax), -1, np.int32)
+    for b in range(B):
+        for h in range(Hkv):
+            idx[b, h, :k_cnt[b]] = np.sort(rs.choice(S, k_cnt[b], replace=False))
+    return src_k, k_cnt, idx
+
+
+@pytest.mark.parametrize("B,S,Hkv,kmax,empty", [
+    (8, 20000, 8, 3000, 0.0),       # 6016 items over 2048 blocks
+    (300, 400, 2, 90, 0.9),         # mostly empty rows
+    (4100, 40, 1, 8, 0.5),          # more rows than the LDS numbering: one block per row chunk
+])
+def test_gather_items_and_rows(bd, B, S, Hkv, kmax, empty):
+    note(f"gather B={B} S={S} Hkv={Hkv} kmax={kmax} empty={empty}")
+    src_k, k_cnt, idx = _gather_case(B, S, Hkv, 128, kmax, B + S, empty)
+    pool = torch.full((B, kmax, Hkv, 128), 3.0, dtype=torch.bfloat16)
+    gk, gv = pool.cuda(), (-pool).cuda()
+    bd.gather(src_k.cuda(), (2 * src_k).cuda(), torch.from_numpy(idx).cuda(),
+              torch.from_numpy(k_cnt).cuda(), gk, gv)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(gk), orc.gather(bits(src_k), idx, k_cnt, bits(pool)))
+    assert np.array_equal(bits(gv), orc.gather(bits(2 * src_k), idx, k_cnt, bits(-pool)))
+
+
+def test_gather_out_of_contract_values(bd):
+    """Counts above k_max are clamped to k_max, negative counts gather
+    nothing, and a slot whose index lies outside [0, S) keeps its value."""
+    note("gather: clamped counts and out-of-range indices")
+    B, S, Hkv, kmax = 4, 500, 2, 40
+    src_k, _, _ = _gather_case(B, S, Hkv, 128, kmax, 9)
+    rs = np.random.default_rng(10)
+    idx = np.stack([np.stack([np.sort(rs.choice(S, kmax, replace=False)) for _ in range(Hkv)])
+                    for _ in range(B)]).astype(np.int32)
+    idx[0, 1, 3] = -1
+    idx[1, 0, 7] = S
+    idx[3, 1, 0] = 1 << 30
+    k_cnt = np.array([kmax, kmax + 50, -4, 25], np.int32)
+    pool = torch.full((B, kmax, Hkv, 128), 5.0, dtype=torch.bfloat16)
+    gk = pool.cuda()
+    bd.gather(src_k.cuda(), None, torch.from_numpy(idx).cuda(), torch.from_numpy(k_cnt).cuda(), gk, None)
+    torch.cuda.synchronize()
+    eff = np.clip(k_cnt, 0, kmax)
+    safe = np.where((idx >= 0) & (idx < S), idx, 0)
+    ref = orc.gather(bits(src_k), safe, eff, bits(pool))
+    p0 = bits(pool)
+    for b, h, j in ((0, 1, 3), (1, 0, 7), (3, 1, 0)):
+        ref[b, j, h] = p0[b, j, h]                 # left unchanged
+    assert np.array_equal(bits(gk), ref)
