@@ -306,7 +306,8 @@ int attn_setup(const char *fn, int dtype, int B, int Hq, int Hkv, int d, int q, 
   if (grid_units > ((int64_t)1 << 31) - 1 || (int64_t)n_rows * Hq * a.nqt > ((int64_t)1 << 31) - 1)
     return fail(BD_ERR_INVALID_ARG, "%s: problem too large for one launch", fn);
   a.row_order = nullptr;
-  a.part_o = a.part_ml = nullptr;
+  a.part_o = nullptr;
+  a.part_ml = nullptr;
   a.items = nullptr;
   a.table = nullptr;
   a.n_table = 0;
@@ -318,7 +319,7 @@ int attn_setup(const char *fn, int dtype, int B, int Hq, int Hkv, int d, int q, 
 // Points the plan's scratch parts (row order, split partials) into ws.
 void attn_bind_workspace(AttnArgs &a, const AttnPlan &plan, char *ws) {
   a.row_order = plan.order ? (int *)(ws + plan.off_order) : nullptr;
-  a.part_o = plan.n_split > 1 ? (float *)(ws + plan.off_part_o) : nullptr;
+  a.part_o = plan.n_split > 1 ? (bf16 *)(ws + plan.off_part_o) : nullptr;
   a.part_ml = plan.n_split > 1 ? (float *)(ws + plan.off_part_ml) : nullptr;
 }
 

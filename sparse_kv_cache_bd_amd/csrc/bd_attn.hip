@@ -32,8 +32,8 @@
 // kernel ranks the rows by prefix length and blocks take rows longest first
 // (LPT order).  The items of one (row, KV head) go to the same XCD, so its
 // K/V come from HBM into that XCD's L2 once.  With few items the prefix is
-// cut into chunks; each chunk writes unnormalised partial O with its
-// (max, sum), and a combine kernel merges the chunks in a fixed order.
+// cut into chunks; each chunk writes its normalised partial O (bf16) with
+// its (max, sum), and a combine kernel merges the chunks in a fixed order.
 #include "bd_common.h"
 
 namespace bd {
@@ -523,19 +523,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
       a.lse[((int64_t)b * a.Hq + hq) * a.q + qi] = (m_run + __log2f(l_run)) * kLn2;
   } else {
     // partials [unit][chunk][column], unit = (natural row, KV head, query
-    // tile).  O of a 32-column group is stored as [dims / 4][column][4]:
-    // lane l's store s (dims 8s + 4hh ..) lands at float (64s + l) * 4, so
-    // each store instruction writes 1 KB contiguous.
+    // tile).  The chunk's O / l (a convex combination of V rows, so within
+    // V's range) is stored in bf16; (max, sum) stay fp32.  O of a 32-column
+    // group is stored as [dims / 4][column][4]: lane l's store s (dims
+    // 8s + 4hh ..) lands at element (64s + l) * 4, so each store instruction
+    // writes 512 bytes contiguous.
     const int64_t unit = ((int64_t)it.rl * a.Hkv + h) * a.nqt + it.u;
     const int col = wave * 32 + ln;
     const int64_t prow = (unit * a.n_split + it.c) * S::NCOL + col;
-    float *po = a.part_o + (prow - ln) * kD + lane * 4;
+    bf16 *po = a.part_o + (prow - ln) * kD + lane * 4;
+    const float inv = 1.f / l_run;
 #pragma unroll
     for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        f32x4 w = {acc[dt][rq * 4 + 0], acc[dt][rq * 4 + 1], acc[dt][rq * 4 + 2], acc[dt][rq * 4 + 3]};
-        *reinterpret_cast<f32x4 *>(po + (dt * 4 + rq) * 256) = w;
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[dt][rq * 4 + e] * inv);
+        *reinterpret_cast<bf16x4 *>(po + (dt * 4 + rq) * 256) = w;
       }
     if (hh == 0) {
       a.part_ml[prow * 2 + 0] = m_run;
@@ -572,14 +577,14 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   // (row id, then prefix length), so the two latencies overlap; chunks past
   // the row's count hold stale data and are never used
   float2 ml[U];
-  f32x4 po[U];
+  bf16x4 po[U];
   auto load = [&](int c0, int lim) {
 #pragma unroll
     for (int v = 0; v < U; ++v) {
       if (c0 + v < lim) {
         const int64_t prow = prow0 + (int64_t)(c0 + v) * S::NCOL;
         ml[v] = *reinterpret_cast<const float2 *>(a.part_ml + prow * 2);
-        po[v] = *reinterpret_cast<const f32x4 *>(a.part_o + (prow - (col & 31)) * kD + (d4 * 32 + (col & 31)) * 4);
+        po[v] = *reinterpret_cast<const bf16x4 *>(a.part_o + (prow - (col & 31)) * kD + (d4 * 32 + (col & 31)) * 4);
       }
     }
   };
@@ -608,11 +613,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 #pragma unroll
     for (int v = 0; v < U; ++v) {
       if (c0 + v < nc) {
+        // the partial holds O / l: its weight is l * 2^(m - M)
         const float mn = fmaxf(M, ml[v].x);
         const float sa = __builtin_amdgcn_exp2f(M - mn);
-        const float sb = __builtin_amdgcn_exp2f(ml[v].x - mn);
-        L = L * sa + ml[v].y * sb;
-        acc = acc * sa + po[v] * sb;
+        const float sb = ml[v].y * __builtin_amdgcn_exp2f(ml[v].x - mn);
+        L = L * sa + sb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = acc[e] * sa + (float)po[v][e] * sb;
         M = mn;
       }
     }
@@ -871,7 +878,7 @@ bool attn_generic_supported(int dtype, int d) {
 // fewer blocks than block slots on the GPU (one 8-wave or two 4-wave blocks
 // per CU), and
 // never below kMinChunk keys: each extra chunk costs a partial O row of
-// 512 bytes per column.  Rows are ordered longest first when the blocks do
+// 256 bytes per column.  Rows are ordered longest first when the blocks do
 // not all fit at once.
 constexpr int kCUs = 256;
 constexpr int kMinChunk = 256;
@@ -912,7 +919,7 @@ AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int d, int q, int n_rows, 
   p.off_part_ml = off;
   if (p.n_split > 1) {
     const size_t prows = (size_t)units * p.n_split * ncol;
-    off += align256(prows * kD * sizeof(float));
+    off += align256(prows * kD * sizeof(bf16));
     p.off_part_ml = off;
     off += align256(prows * 2 * sizeof(float));
   }

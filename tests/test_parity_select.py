@@ -144,3 +144,36 @@ def test_select_long_rows(bd, S_list, k_list, dup):
     if dup:
         kth = np.sort(sc[0, 0, :S_list[0]])[::-1][k_list[0] - 1]
         assert (sc[0, 0, :S_list[0]] == kth).sum() >= 2
+
+
+@pytest.mark.parametrize("S_list,k_list,dup", [
+    ([300000, 5000], [15000, 250], False),    # 74 blocks of 4096 scores on the long row
+    ([270000], [13501], True),                # ... with exact ties at the threshold
+])
+def test_select_very_long_rows(bd, S_list, k_list, dup):
+    """Rows of several hundred thousand scores (multi-block ranking with
+    digit histograms in global memory, per-block counts, ordered write)."""
+    note(f"select very long rows S={S_list} k={k_list} dup={dup}")
+    B = len(S_list)
+    Q, K = _case(21 + int(dup), B, S_list, 8, 2, dup=dup)
+    scale = 1.0 / math.sqrt(128)
+    idx, sc, k_max = _run(bd, Q, K, S_list, k_list, scale)
+    _check(Q, K, S_list, k_list, scale, idx, sc, k_max, label="very long")
+    for b, (S, k) in enumerate(zip(S_list, k_list)):
+        n = min(S, k)
+        assert (idx[b, :, n:] == -1).all()
+        assert (np.diff(idx[b, :, :n], axis=1) > 0).all()
+
+
+def test_select_all_scores_equal(bd):
+    """Every key identical: every score ties at the threshold and the
+    lowest positions are kept."""
+    note("select: all scores equal")
+    S_list, k_list = [20000, 3000], [1000, 2999]
+    Q, K = _case(31, 2, S_list, 16, 4)
+    K[:] = K[:, :1]
+    idx, sc, k_max = _run(bd, Q, K, S_list, k_list, 0.088)
+    for b, (S, k) in enumerate(zip(S_list, k_list)):
+        assert (sc[b, :, :S] == sc[b, :, :1]).all()
+        assert (idx[b, :, :k] == np.arange(k)).all() and (idx[b, :, k:] == -1).all()
+    _check(Q, K, S_list, k_list, 0.088, idx, sc, k_max, label="all equal")
