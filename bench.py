@@ -264,11 +264,40 @@ def bench_producer(bd, dev, reps):
     ms = time_calls(lambda: bd.qkv_rope_write(X, W, rope_pos, Hq, Hkv, Qo, Kc, Vc, dst), reps)
     flop = 2 * B * q * Dm * (Hq + 2 * Hkv) * d
     nbytes = (B * q * Dm + (Hq + 2 * Hkv) * d * Dm + B * q * (Hq + 2 * Hkv) * d) * 2
+    # the same work unfused, as the separate launches a framework issues:
+    # the projection as one library GEMM (hipBLASLt through torch), RoPE of
+    # the query and key heads as elementwise ops, then the copy of keys and
+    # values into the cache tail
+    t = C - q
+    j = torch.arange(d // 2, device=dev, dtype=torch.float64)
+    inv_freq = torch.pow(torch.tensor(10000.0, dtype=torch.float64, device=dev), -2.0 * j / d)
+    pos = rope_pos.to(torch.float64)[:, None] + torch.arange(q, device=dev, dtype=torch.float64)[None, :]
+    ang = pos[:, :, None] * inv_freq                          # [B, q, d/2]
+    cos = torch.cos(ang).float()[:, :, None, :]
+    sin = torch.sin(ang).float()[:, :, None, :]
+
+    Wt = W.t().contiguous()      # the library GEMM takes a plain [Dm, N] operand
+
+    def unfused():
+        Y = torch.matmul(X.view(B * q, Dm), Wt).view(B, q, Hq + 2 * Hkv, d)
+        qk = Y[:, :, :Hq + Hkv].float()
+        x1, x2 = qk[..., :d // 2], qk[..., d // 2:]
+        rot = torch.cat([x1 * cos - x2 * sin, x2 * cos + x1 * sin], dim=-1).bfloat16()
+        Qo.copy_(rot[:, :, :Hq])
+        Kc[:, t:].copy_(rot[:, :, Hq:])
+        Vc[:, t:].copy_(Y[:, :, Hq + Hkv:])
+
+    ms_unf = time_calls(unfused, reps)
+    ms_gemm = time_calls(lambda: torch.matmul(X.view(B * q, Dm), Wt), reps)
     res = {"tokens": B * q, "hidden": Dm, "heads": [Hq, Hkv], "us": round(ms * 1e3, 2),
            "TFLOP/s": _rate(flop, ms, 1e12),
            "frac_mfma_peak": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-           "gflop": round(flop / 1e9, 1), "min_mb": round(nbytes / 1e6, 1)}
-    del X, W, Kc, Vc, Qo
+           "gflop": round(flop / 1e9, 1), "min_mb": round(nbytes / 1e6, 1),
+           "unfused_us": round(ms_unf * 1e3, 2),
+           "unfused_gemm_only_us": round(ms_gemm * 1e3, 2),
+           "unfused_gemm_TFLOP/s": _rate(flop, ms_gemm, 1e12),
+           "fused_speedup_vs_unfused": round(ms_unf / ms, 3)}
+    del X, W, Wt, Kc, Vc, Qo
     torch.cuda.empty_cache()
     return res
 
@@ -312,6 +341,31 @@ def bench_block_table(bd, wl, Kc, Vc, Q, dense_pmax, ms_packed, reps, page=128):
     res["packed_contiguous_us"] = round(ms_packed * 1e3, 2)
     del KP, VP
     torch.cuda.empty_cache()
+    return res
+
+
+def bench_scatter_layers(bd, dev, reps):
+    """FlowBlock's write-back, Eq. (7), applied to every layer: the scatter
+    of one window per row for L layers in one call, on the packed-wavefront
+    shape (8 rows, C = 4096, q = 64) and the serving-mix shape (64 rows,
+    C = 16640, q = 128); 32/8 heads, d = 128, bf16.  Synthetic caches (the
+    values are copied bit for bit, so uninitialised memory is timed)."""
+    import torch
+    res = {}
+    for name, B, C, q, layers in (("packed_wavefront", 8, 4096, 64, (1, 8, 32)),
+                                  ("serving_mix", 64, 16640, 128, (1, 8))):
+        g = torch.Generator().manual_seed(1)
+        o = (torch.randint(16, (C - 2 * q) // 32, (B,), generator=g) * 32).to(torch.int32).to(dev)
+        for L in layers:
+            Kc = torch.empty((L, B, C, 8, 128), dtype=torch.bfloat16, device=dev)
+            Vc = torch.empty_like(Kc)
+            ms = time_calls(lambda: bd.kv_scatter(Kc, Vc, Kc, Vc, o, C - q, q), reps)
+            nbytes = L * B * q * 8 * 128 * 2 * 2 * 2
+            res[f"{name}_L{L}"] = {"us": round(ms * 1e3, 2), "GB/s": _rate(nbytes, ms, 1e9),
+                                   "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                   "mb": round(nbytes / 1e6, 1)}
+            del Kc, Vc
+            torch.cuda.empty_cache()
     return res
 
 
@@ -456,6 +510,7 @@ def bench_configs(dev, reps: int = 10):
         del Kc, Vc, pool_k, pool_v, ws, ws_a
         torch.cuda.empty_cache()
     out["producer_serving_mix"] = bench_producer(bd, dev, reps)
+    out["scatter_layers"] = bench_scatter_layers(bd, dev, reps)
     del flush
     torch.cuda.empty_cache()
     return out
@@ -597,7 +652,7 @@ def main():
                       "mb": round(work["scatter_bytes"] / 1e6, 2)}
 
     traffic = traffic_for_attention()
-    roof = {"bound": "mfma", "kernel": "attn_mfma_kernel<8, 4, false> (dense and sparse rows, one launch)",
+    roof = {"bound": "mfma", "kernel": "attn_mfma_kernel<8, 4, false, false> (dense and sparse rows, one launch)",
             "achieved": round(tf_a, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tf_a / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
             "algorithmic_bytes": attn_bytes,
