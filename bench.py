@@ -164,13 +164,20 @@ def cpu_baseline(wl, budget_s: float = 12.0):
             "seconds": round(el, 2)}
 
 
-def time_calls(fn, reps: int, warmup: int = 2) -> float:
+def time_calls(fn, reps: int, warmup: int = 2, settle_ms: float = 100.0) -> float:
     """Average milliseconds per call of ``fn`` (HIP events on the current
-    stream, which is the stream the library launches on).  A spin kernel
-    ahead of the first event gives the host time to queue every call, so
-    short calls are timed back to back on the GPU, not at the host's launch
-    rate."""
+    stream, which is the stream the library launches on).  Before the timed
+    calls, ``fn`` runs untimed for at least ``settle_ms`` of wall time (the
+    GPU's clocks settle at the load; a first call after an idle gap runs up
+    to 20 % slower), then ``warmup`` more times.  A spin kernel ahead of the
+    first event gives the host time to queue every call, so short calls are
+    timed back to back on the GPU, not at the host's launch rate."""
     import torch
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < settle_ms:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -530,6 +537,8 @@ def main():
                     help="skip the per-configuration measurements of the other workloads")
     ap.add_argument("--only", choices=["select", "gather", "attn", "attn_dense", "attn_sparse", "scatter"],
                     help="time only this operation of the step (for counter runs); prints one line")
+    ap.add_argument("--producer-only", action="store_true",
+                    help="time only the fused producer and its unfused sequence; prints one JSON line")
     ap.add_argument("--copy-probe", type=int, metavar="MB",
                     help="run a plain device copy of MB megabytes 5 times (counter calibration)")
     args = ap.parse_args()
@@ -556,6 +565,9 @@ def main():
         torch.cuda.synchronize()
         print(f"copy probe: 5 copies of {n * 4} bytes", flush=True)
         return
+    if args.producer_only:
+        print(json.dumps({"producer_serving_mix": bench_producer(bd, dev, args.steps)}), flush=True)
+        return
     log("generating the serving-mix workload")
     wl = synth.serving_mix(seed=args.seed)
     Kc, Vc, Q, o = (x.to(dev) for x in (wl.Kc, wl.Vc, wl.Q, wl.o))
@@ -579,7 +591,7 @@ def main():
         step.run()
     torch.cuda.synchronize()
     if args.only:
-        ms = time_calls(getattr(step, args.only), args.steps, 0)
+        ms = time_calls(getattr(step, args.only), args.steps, 0, settle_ms=0)
         print(f"{args.only}: {ms * 1e3:.1f} us per call over {args.steps} calls", flush=True)
         return
 

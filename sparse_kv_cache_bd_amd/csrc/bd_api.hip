@@ -476,7 +476,8 @@ int bd_qkv_rope_write(int dtype, int B, int q, int Dm, int Hq, int Hkv, int d, c
   if (Dm % 64 != 0) return fail(BD_ERR_UNSUPPORTED, "bd_qkv_rope_write: Dm must be a multiple of 64");
   if (!(rope_base > 1.f) || rope_base > 1e30f)
     return fail(BD_ERR_INVALID_ARG, "bd_qkv_rope_write: rope_base must be > 1");
-  if ((int64_t)B * q > ((int64_t)1 << 24) || Hq + 2 * Hkv > 65535)
+  if ((int64_t)B * q > ((int64_t)1 << 24) || Hq + 2 * Hkv > 65535 ||
+      cdiv(Hq + 2 * Hkv, 2) * cdiv((int64_t)B * q, 256) > INT32_MAX)
     return fail(BD_ERR_INVALID_ARG, "bd_qkv_rope_write: too large for one launch");
   if (B == 0 || q == 0) return BD_OK;
   if (!x || !w || !rope_pos || !q_out || !k_cache || !v_cache || !dst_pos || !x_strides ||

@@ -248,9 +248,11 @@ def test_attn_noalloc_rejects_oversized_scratch(L):
     BD_ERR_WORKSPACE before any HIP call (the size comes from the plan)."""
     cap = bd.noalloc_scratch_bytes()
     assert cap == 32 << 20
-    # one unit with a 4M-key prefix: the plan cuts 512 chunks of partials
-    kw = dict(B=1, n_rows=1, Hq=4, Hkv=1, q=32, pmax=1 << 22, pcap=1 << 22)
-    need = bd.attn_workspace_size(bd.BD_BF16, 1, 4, 1, 128, 32, 1, 1 << 22)
+    # 255 units (one short of a block per CU) over 1024-key prefixes: each is
+    # cut in two chunks, whose partials (255 x 2 x 256 columns) pass 32 MB;
+    # split plans are largest just below one unit per CU
+    kw = dict(B=255, n_rows=255, Hq=8, Hkv=1, q=32, pmax=1024, pcap=1024)
+    need = bd.attn_workspace_size(bd.BD_BF16, 255, 8, 1, 128, 32, 255, 1024)
     assert need > cap
     assert _attn_noalloc(L, **kw) == bd.BD_ERR_WORKSPACE
     assert "scratch" in bd.last_error() and str(need) in bd.last_error()

@@ -58,6 +58,8 @@ def _run(bd, X, W, rope_pos, dst_pos, Hq, Hkv, C, base=10000.0):
 
 @pytest.mark.parametrize("B,q,Dm,Hq,Hkv,rope_pos", [
     (3, 40, 256, 8, 2, [0, 1000, 131000]),      # one ragged token tile, large positions
+    (2, 256, 320, 5, 1, [3, 70000]),            # odd hidden-tile count, odd head count, XCD block order
+    (3, 300, 256, 8, 2, [11, 0, 90000]),        # ragged group of head pairs, 24 blocks in XCD order
     (2, 200, 512, 4, 4, [17, 4096]),            # tiles spanning rows
     (5, 64, 128, 16, 2, [5, 9, 33, 70000, 1]),  # G = 8
     (3, 40, 128, 1, 1, [2, 50, 7]),             # three heads: an odd head count
