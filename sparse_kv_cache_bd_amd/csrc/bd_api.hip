@@ -303,10 +303,11 @@ int attn_setup(const char *fn, int dtype, int B, int Hq, int Hkv, int d, int q, 
   plan = attn_plan(dtype, B, Hq, Hkv, d, q, n_rows, p_max);
   a.nw = plan.nw; a.nqt = plan.nqt; a.chunk = plan.chunk; a.n_split = plan.n_split;
   const int64_t grid_units = (8 + (int64_t)n_rows * Hkv) * a.nqt * a.n_split;
-  if (grid_units > ((int64_t)1 << 31) - 1 || (int64_t)n_rows * Hq * a.nqt > ((int64_t)1 << 31) - 1)
+  if (grid_units > ((int64_t)1 << 31) - 1 || (int64_t)n_rows * Hq * a.nqt * a.n_split > ((int64_t)1 << 31) - 1)
     return fail(BD_ERR_INVALID_ARG, "%s: problem too large for one launch", fn);
   a.row_order = nullptr;
   a.part_o = nullptr;
+  a.gpart_o = nullptr;
   a.part_ml = nullptr;
   a.items = nullptr;
   a.table = nullptr;
@@ -319,7 +320,8 @@ int attn_setup(const char *fn, int dtype, int B, int Hq, int Hkv, int d, int q, 
 // Points the plan's scratch parts (row order, split partials) into ws.
 void attn_bind_workspace(AttnArgs &a, const AttnPlan &plan, char *ws) {
   a.row_order = plan.order ? (int *)(ws + plan.off_order) : nullptr;
-  a.part_o = plan.n_split > 1 ? (bf16 *)(ws + plan.off_part_o) : nullptr;
+  a.part_o = plan.n_split > 1 && plan.nw > 0 ? (bf16 *)(ws + plan.off_part_o) : nullptr;
+  a.gpart_o = plan.n_split > 1 && plan.nw == 0 ? (float *)(ws + plan.off_part_o) : nullptr;
   a.part_ml = plan.n_split > 1 ? (float *)(ws + plan.off_part_ml) : nullptr;
 }
 

@@ -682,7 +682,11 @@ __global__ __launch_bounds__(256 * KG) void attn_generic_kernel(AttnArgs a) {
   const int ql = tid >> 3;   // query inside tile
   const int sub = tid & 7;   // dimension slice
   const int nqt = a.nqt;
-  int unit = blockIdx.x;
+  // block = (chunk, query tile, query head, row); chunk c covers prefix keys
+  // [c * chunk, (c + 1) * chunk), the last chunk also the window
+  const int64_t unit_id = blockIdx.x / a.n_split;
+  const int c = (int)(blockIdx.x - unit_id * a.n_split);
+  int unit = (int)unit_id;
   const int u = unit % nqt;
   unit /= nqt;
   const int hq = unit % a.Hq;
@@ -691,7 +695,12 @@ __global__ __launch_bounds__(256 * KG) void attn_generic_kernel(AttnArgs a) {
   const int b = rr.b;
   if (b < 0 || b >= a.B) return;
   const int h = hq / a.G;
-  const int P = prefix_len(a, rr);
+  const int P_row = prefix_len(a, rr);
+  const int nc = P_row > 0 ? (int)cdiv(P_row, a.chunk) : 1;
+  if (c >= nc) return;
+  const int kbeg = c * a.chunk;
+  const int P = min(P_row, kbeg + a.chunk);   // end of this chunk's prefix keys
+  const bool with_window = c == nc - 1;
   const int qi = u * kQT + ql;
   const bool q_ok = qi < a.q;
   const int ilast = min(u * kQT + kQT, a.q) - 1;
@@ -715,8 +724,8 @@ __global__ __launch_bounds__(256 * KG) void attn_generic_kernel(AttnArgs a) {
   const int64_t p_row = src.row;
   const T *wkb = reinterpret_cast<const T *>(a.wk) + (int64_t)b * a.ws[0] + (int64_t)h * a.ws[2];
   const T *wvb = reinterpret_cast<const T *>(a.wv) + (int64_t)b * a.ws[0] + (int64_t)h * a.ws[2];
-  const int npt = (int)cdiv(P, kGenKeys);
-  const int nwt = (int)cdiv(win_len, kGenKeys);
+  const int npt = (int)cdiv(P - kbeg, kGenKeys);
+  const int nwt = with_window ? (int)cdiv(win_len, kGenKeys) : 0;
   const int ntile = npt + nwt;
   // staging: element tid + 256 i of the tile (consecutive threads on
   // consecutive dims), every load of a tile in flight together; tile t+1 is
@@ -724,7 +733,7 @@ __global__ __launch_bounds__(256 * KG) void attn_generic_kernel(AttnArgs a) {
   float kreg[EPT], vreg[EPT];
   auto gload = [&](int tile) {
     const bool win = tile >= npt;
-    const int base = win ? (tile - npt) * kGenKeys : tile * kGenKeys;
+    const int base = win ? (tile - npt) * kGenKeys : kbeg + tile * kGenKeys;
     const int limit = win ? win_len : P;
     const T *kb = win ? wkb : pkb;
     const T *vb = win ? wvb : pvb;
@@ -761,7 +770,7 @@ __global__ __launch_bounds__(256 * KG) void attn_generic_kernel(AttnArgs a) {
     if (more) gload(tile + KG);
     if (tile < ntile) {
     const bool win = tile >= npt;
-    const int base = win ? (tile - npt) * kGenKeys : tile * kGenKeys;
+    const int base = win ? (tile - npt) * kGenKeys : kbeg + tile * kGenKeys;
     const int limit = win ? win_len : P;
     const int vlim = win ? lim_i : limit;   // keys at or past vlim are not visible
     // the tile in groups of 8 keys (a runtime loop bounds the registers the
@@ -854,12 +863,69 @@ __global__ __launch_bounds__(256 * KG) void attn_generic_kernel(AttnArgs a) {
     }
   }
   if (!q_ok) return;
+  const float inv = 1.f / l_run;
+  if (nc > 1) {
+    // partial of chunk c: O / l in fp32 and (max, sum); rows [unit][chunk][query]
+    const int64_t prow = (unit_id * a.n_split + c) * kQT + ql;
+    float *po = a.gpart_o + prow * D + sub * DL;
+#pragma unroll
+    for (int e = 0; e < DL; e += 4)
+      *reinterpret_cast<f32x4 *>(po + e) = f32x4{o[e] * inv, o[e + 1] * inv, o[e + 2] * inv, o[e + 3] * inv};
+    if (sub == 0) *reinterpret_cast<float2 *>(a.part_ml + prow * 2) = float2{m_run, l_run};
+    return;
+  }
   T *op = reinterpret_cast<T *>(a.out) + (int64_t)b * a.os[0] + (int64_t)qi * a.os[1] +
           (int64_t)hq * a.os[2] + sub * DL;
-  const float inv = 1.f / l_run;
 #pragma unroll
   for (int e = 0; e < DL; ++e) op[e] = (T)(o[e] * inv);
   if (a.lse && sub == 0) a.lse[((int64_t)b * a.Hq + hq) * a.q + qi] = (m_run + log2f(l_run)) * kLn2;
+}
+
+// Merge the general path's split partials: one thread per (query, 4 dims)
+// of a (row, query head, query tile) unit, chunks in a fixed order.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_generic_combine_kernel(AttnArgs a) {
+  constexpr int D4 = D / 4;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int d4 = (int)(idx % D4);
+  const int64_t r = idx / D4;
+  const int ql = (int)(r % kQT);
+  const int64_t unit_id = r / kQT;
+  int unit = (int)unit_id;
+  const int u = unit % a.nqt;
+  unit /= a.nqt;
+  const int hq = unit % a.Hq;
+  const int rl = unit / a.Hq;
+  if (rl >= a.n_rows) return;
+  const RowRef rr = row_ref(a, rl);
+  const int b = rr.b;
+  if (b < 0 || b >= a.B) return;
+  const int qi = u * kQT + ql;
+  if (qi >= a.q) return;
+  const int P = prefix_len(a, rr);
+  const int nc = P > 0 ? (int)cdiv(P, a.chunk) : 1;
+  if (nc == 1) return;   // written directly by the attention kernel
+  float M = -INFINITY, L = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int cc = 0; cc < nc; ++cc) {
+    const int64_t prow = (unit_id * a.n_split + cc) * kQT + ql;
+    const float2 ml = *reinterpret_cast<const float2 *>(a.part_ml + prow * 2);
+    const f32x4 po = *reinterpret_cast<const f32x4 *>(a.gpart_o + prow * D + d4 * 4);
+    // every chunk holds visible prefix keys: each partial max is finite
+    const float mn = fmaxf(M, ml.x);
+    const float sa = __builtin_amdgcn_exp2f(M - mn);
+    const float sb = ml.y * __builtin_amdgcn_exp2f(ml.x - mn);
+    L = L * sa + sb;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = acc[e] * sa + po[e] * sb;
+    M = mn;
+  }
+  const float inv = 1.f / L;
+  T *op = reinterpret_cast<T *>(a.out) + (int64_t)b * a.os[0] + (int64_t)qi * a.os[1] +
+          (int64_t)hq * a.os[2] + d4 * 4;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) op[e] = (T)(acc[e] * inv);
+  if (a.lse && d4 == 0) a.lse[((int64_t)b * a.Hq + hq) * a.q + qi] = (M + log2f(L)) * kLn2;
 }
 
 }  // namespace
@@ -891,8 +957,25 @@ AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int d, int q, int n_rows, 
   p.chunk = 1 << 30;
   p.n_split = 1;
   if (!attn_mfma_supported(dtype, d, G)) {
+    // general path: blocks of one (row, query head, 32-query tile); with
+    // fewer blocks than CUs the prefix is cut into chunks of whole 32-key
+    // tiles (one tile at least), each writing an fp32 O / l with its
+    // (max, sum), merged by a combine kernel in chunk order
     p.nw = 0;
     p.nqt = (int)cdiv(q, kQT);
+    const int64_t units = (int64_t)n_rows * Hq * p.nqt;
+    if (p_max > kGenKeys && units < kCUs) {
+      const int64_t want = cdiv(kCUs, units);
+      const int64_t ch = cdiv(cdiv(p_max, want), kGenKeys) * kGenKeys;
+      if (ch < p_max) {
+        p.chunk = (int)ch;
+        p.n_split = (int)cdiv(p_max, ch);
+        const size_t prows = (size_t)units * p.n_split * kQT;
+        p.off_part_o = 0;
+        p.off_part_ml = align256(prows * d * sizeof(float));
+        p.ws_bytes = p.off_part_ml + align256(prows * 2 * sizeof(float));
+      }
+    }
     return p;
   }
   p.nw = ((int64_t)q * G <= 128 && G <= 4) ? 4 : 8;
@@ -982,10 +1065,11 @@ hipError_t launch_attn(const AttnArgs &a, hipStream_t s) {
     }
     return hipErrorInvalidValue;
   }
-  const int64_t grid = (int64_t)a.n_rows * a.Hq * a.nqt;
-  // fewer blocks than CUs: key groups per block (4 at d = 64, 2 at d = 128,
-  // as the LDS allows)
-  const bool few = grid < kCUs;
+  const int64_t units = (int64_t)a.n_rows * a.Hq * a.nqt;
+  const int64_t grid = units * a.n_split;
+  // fewer blocks than CUs (a prefix too short to split): key groups per
+  // block (4 at d = 64, 2 at d = 128, as the LDS allows)
+  const bool few = grid < kCUs && a.n_split == 1;
   const dim3 g((unsigned)grid);
   if (a.dtype == BD_F32) {
     if (a.d == 64) {
@@ -1003,6 +1087,16 @@ hipError_t launch_attn(const AttnArgs &a, hipStream_t s) {
       if (few) hipLaunchKernelGGL((attn_generic_kernel<bf16, 128, 2>), g, dim3(512), 0, s, a);
       else hipLaunchKernelGGL((attn_generic_kernel<bf16, 128, 1>), g, dim3(256), 0, s, a);
     }
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_split <= 1) return e;
+  const dim3 cg((unsigned)cdiv(units * kQT * (a.d / 4), 256));
+  if (a.dtype == BD_F32) {
+    if (a.d == 64) hipLaunchKernelGGL((attn_generic_combine_kernel<float, 64>), cg, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((attn_generic_combine_kernel<float, 128>), cg, dim3(256), 0, s, a);
+  } else {
+    if (a.d == 64) hipLaunchKernelGGL((attn_generic_combine_kernel<bf16, 64>), cg, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((attn_generic_combine_kernel<bf16, 128>), cg, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }

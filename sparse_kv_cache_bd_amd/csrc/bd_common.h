@@ -129,7 +129,8 @@ struct AttnArgs {
   int nw;                 // waves per block of the MFMA path (4 or 8)
   int nqt, chunk, n_split;
   int *row_order;         // rows by descending prefix length, or NULL (natural order)
-  bf16 *part_o;    // split partials: O / l of each chunk, bf16
+  bf16 *part_o;    // split partials: O / l of each chunk, bf16 (MFMA path)
+  float *gpart_o;  // split partials: O / l of each chunk, fp32 (general path)
   float *part_ml;  // (max, sum) of each chunk
 };
 // Launch plan of one bd_attn_packed call: block shape, query tiles, key

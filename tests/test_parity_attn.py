@@ -218,6 +218,22 @@ def test_fp32_general_path_many_blocks(bd):
     np.testing.assert_allclose(L.cpu().numpy(), ref_lse, atol=1e-5, rtol=1e-5)
 
 
+def test_fp32_general_path_split_prefix(bd):
+    """Few general-path blocks over long ragged prefixes: the prefix is cut
+    into 32-key chunks (dozens per row), each writing an fp32 partial, and
+    the combine merges them; an empty prefix and a one-chunk row are written
+    directly."""
+    note("attn fp32 general path, split prefix")
+    o = [2000, 0, 777, 19]
+    Q, K, V, q, t = _cache_case(77, 4, 2100, 2, 2, 128, 32, 2, o, dtype=torch.float32)
+    out, L = _run_cache(bd, Q, K, V, o, 32, 1.0 / math.sqrt(128), lse=True)
+    ref, ref_lse = orc.cache_attention_eq6(Q, K, V, o, 32, 1.0 / math.sqrt(128))
+    check_attention(out, ref, torch.float32, label="fp32 split prefix")
+    np.testing.assert_allclose(L.cpu().numpy(), ref_lse, atol=1e-5, rtol=1e-5)
+    plan_bytes = bd.attn_workspace_size(torch.float32, 4, 2, 2, 128, q, 4, max(o))
+    assert plan_bytes > 0          # the plan splits this launch
+
+
 def test_tiny_dense_config(bd):
     """The tiny fp32 configuration: 1 row, 4/4 heads, d = 64, prefix 256,
     W = 1, plus the scatter of the 32 new KV rows."""
