@@ -209,6 +209,7 @@ struct ProduceArgs {
   const int32_t *rope_pos;  // absolute position of window token 0, per row
   const int32_t *dst_pos;   // cache position of window token 0, per row
   double inv_freq[64];      // rope_base^(-2j/128), j < 64
+  float step_rot[64][2];    // cos, sin of 32 x inv_freq[j] (set by launch_produce)
   bf16 *qo;
   int64_t qos[3];
   bf16 *kc, *vc;

@@ -14,7 +14,9 @@
 // X are double-buffered in LDS (128 KB); while a tile's 64 MFMAs run, the
 // next tile goes from registers to the other buffer and the tile after it is
 // loaded into the registers, the three interleaved one-for-one with the
-// MFMAs by scheduling barriers.  One block barrier per tile.  Blocks are
+// MFMAs by scheduling barriers.  One block barrier per tile, placed before
+// the tile's last 16 MFMAs, which then hide the next tile's first fragment
+// reads.  Blocks are
 // ordered so that the 32 running on one XCD (dispatch is round-robin over
 // the 8 XCDs) share 4 head pairs and 8 token tiles, which their L2 serves.
 //
@@ -22,11 +24,19 @@
 // (position x inverse frequency / 2 pi; positions reach 1e5 and more, the
 // inverse frequencies come from the host in double), reduced to [-1/2, 1/2]
 // in double, and its sine and cosine taken by the hardware's
-// revolution-scaled sin / cos in fp32; the rotation is applied to the fp32
-// accumulators and results are rounded to bf16 once.  Each wave then writes
-// its 128 x 128 tile into its own 32 KB of the (now idle) LDS and reads it
-// back token-major, so every store instruction writes whole 256-byte head
-// rows of 4 tokens.
+// revolution-scaled sin / cos in fp32.  A lane's four tokens are 32 apart;
+// when all of a wave's lanes hold four consecutive positions of one row
+// (always when the window length is a multiple of 128), only the first angle
+// is formed that way and the next three advance it by the fixed rotation of
+// 32 positions (cos, sin of 32 x inverse frequency, computed on the host in
+// double): three complex products in fp32 in place of three
+// double-precision reductions and six sin / cos.  The rotation is applied to
+// the fp32 accumulators, results are rounded to bf16 once and written, per
+// 32 x 32 block pair, into the wave's own 32 KB of the (now idle) LDS; read
+// back token-major, every store instruction writes whole 256-byte head rows
+// of 4 tokens.  Each of the three variants (no rotation, per-angle, stepped)
+// is one straight-line pass over the accumulators, so none of them keeps
+// more than one block pair outside the accumulator registers.
 #include "bd_common.h"
 
 namespace bd {
@@ -44,6 +54,68 @@ constexpr int kPGroup = 4;   // head pairs per group of the block order
 // chunks, and 16 lanes reading one chunk of 16 consecutive rows, each touch
 // 16 distinct 4-bank groups of the 64 LDS banks.
 __device__ inline int lds_off(int row, int c) { return row * kPStr + ((c ^ ((row >> 1) & 7)) << 3); }
+
+// Rotation (ROT) of the lane's accumulators and their bf16 rows into the
+// wave's transpose buffer tw: [128 tokens][128 features], 16-byte chunk c of
+// token row t at chunk c ^ (t & 15), the 8-byte halves swapped for rows with
+// bit 4 set, so the 32 lanes of one write (rows 0..31) spread over all 64
+// banks.  Lane (hh, ln) holds features mb*32 + g*8 + hh*4 + e (r = 4g + e)
+// of token nb*32 + ln; dimension j and its partner j + 64 are blocks mb and
+// mb + 2 of the same register.  STEP: the angles of tokens nb = 1..3 advance
+// the angle of nb = 0 by the rotation of 32 positions.
+template <bool ROT, bool STEP>
+__device__ __forceinline__ void rope_to_lds(f32x16 (&acc)[4][4], bf16 *tw, const double (&pos)[4],
+                                            const ProduceArgs &a, int hh, int ln) {
+  constexpr double kRev = 0.15915494309189533577;   // 1 / (2 pi)
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    double fr[16];   // revolutions per position of the lane's dimensions
+    float stc[16], sts[16];
+    float cs[16], sn[16];
+    if (ROT) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = mb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+        fr[r] = a.inv_freq[j] * kRev;
+        if (STEP) { stc[r] = a.step_rot[j][0]; sts[r] = a.step_rot[j][1]; }
+      }
+    }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      float lo[16], hi[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { lo[r] = acc[nb][mb][r]; hi[r] = acc[nb][mb + 2][r]; }
+      if (ROT) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if (STEP && nb > 0) {
+            const float c0 = cs[r], s0 = sn[r];
+            cs[r] = c0 * stc[r] - s0 * sts[r];
+            sn[r] = s0 * stc[r] + c0 * sts[r];
+          } else {
+            const double x = pos[nb] * fr[r];
+            const float t = (float)(x - __builtin_rint(x));   // [-1/2, 1/2] revolutions
+            sn[r] = __builtin_amdgcn_sinf(t);
+            cs[r] = __builtin_amdgcn_cosf(t);
+          }
+          const float l = lo[r], h = hi[r];
+          lo[r] = l * cs[r] - h * sn[r];
+          hi[r] = h * cs[r] + l * sn[r];
+        }
+      }
+      const int row = nb * 32 + ln;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 v, u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { v[e] = (bf16)lo[g * 4 + e]; u[e] = (bf16)hi[g * 4 + e]; }
+        const int sw = (hh ^ (ln >> 4)) << 2;
+        *reinterpret_cast<bf16x4 *>(&tw[row * kPD + (((mb * 4 + g) ^ (row & 15)) << 3) + sw]) = v;
+        *reinterpret_cast<bf16x4 *>(&tw[row * kPD + ((((mb + 2) * 4 + g) ^ (row & 15)) << 3) + sw]) = u;
+      }
+    }
+  }
+}
 
 __global__ __launch_bounds__(256, 1) void produce_kernel(ProduceArgs a, int n_pairs, int n_tb, int xcd_order) {
   // block -> (head pair, token tile): with xcd_order, XCD x (= blockIdx % 8)
@@ -113,49 +185,56 @@ __global__ __launch_bounds__(256, 1) void produce_kernel(ProduceArgs a, int n_pa
       wf[mb] = *reinterpret_cast<const bf16x8 *>(&Wb[lds_off(hsel * kPD + mb * 32 + ln, ks * 2 + hh)]);
   };
   // One tile from (Wb, Xb); the registers' tile goes to (Wn, Xn) and the tile
-  // at hidden offset k0 is loaded.  Per 16-element step: 16 MFMAs, the next
-  // step's 8 fragment reads, 4 staging writes and 4 global loads.
+  // at hidden offset k0 is loaded.  Steps 0-2 (16 elements each): 16 MFMAs,
+  // the next step's 8 fragment reads, and the 16 staging writes and global
+  // loads spread 6 / 5 / 5.  The block barrier then comes before step 3: the
+  // tile's last fragments are already in registers and (Wn, Xn) is complete,
+  // so the next tile's first fragments are read while step 3's MFMAs run.
+  // After the last tile that read is not used; the epilogue's LDS writes
+  // (each wave into its own 32 KB) may overlap it, which changes nothing a
+  // wave keeps.
+  bf16x8 xf[2][4], wf[2][4];
+  auto mfma16 = [&](int b) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[b][mb], xf[b][nb], acc[nb][mb], 0, 0, 0);
+  };
   auto step = [&](const bf16 *Wb, const bf16 *Xb, bf16 *Wn, bf16 *Xn, int k0) {
-    bf16x8 xf[2][4], wf[2][4];
-    frag(Wb, Xb, 0, xf[0], wf[0]);
 #pragma unroll
-    for (int ks = 0; ks < kPBK / 16; ++ks) {
-      if (ks < kPBK / 16 - 1) frag(Wb, Xb, ks + 1, xf[(ks + 1) & 1], wf[(ks + 1) & 1]);
+    for (int ks = 0; ks < 3; ++ks) {
+      frag(Wb, Xb, ks + 1, xf[(ks + 1) & 1], wf[(ks + 1) & 1]);
+      const int u0 = ks == 0 ? 0 : 1 + 5 * ks, nl = ks == 0 ? 6 : 5;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        lstore(Wn, Xn, 4 * ks + j);
-        gload(4 * ks + j, k0);
+      for (int j = 0; j < nl; ++j) {
+        lstore(Wn, Xn, u0 + j);
+        gload(u0 + j, k0);
       }
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks & 1][mb], xf[ks & 1][nb], acc[nb][mb], 0, 0, 0);
+      mfma16(ks & 1);
       // masks: 0x008 MFMA, 0x020 global load, 0x100 LDS read, 0x200 LDS write
-      if (ks < kPBK / 16 - 1) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (i < nl) {
           __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         }
       }
     }
+    // nothing moves across the barrier (the compiler would otherwise hoist
+    // step 3's MFMAs above it)
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    frag(Wn, Xn, 0, xf[0], wf[0]);
+    mfma16(1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
   };
   // loads past the last tile are clamped to it (their data is never used),
   // so every wait count is static
@@ -166,6 +245,7 @@ __global__ __launch_bounds__(256, 1) void produce_kernel(ProduceArgs a, int n_pa
 #pragma unroll
   for (int u = 0; u < 16; ++u) gload(u, min(1, nit - 1) * kPBK);
   __syncthreads();
+  frag(W0, X0, 0, xf[0], wf[0]);
   int it = 0;
   for (; it + 1 < nit; it += 2) {
     step(W0, X0, W1, X1, min(it + 2, nit - 1) * kPBK);
@@ -177,52 +257,20 @@ __global__ __launch_bounds__(256, 1) void produce_kernel(ProduceArgs a, int n_pa
   // token nb*32 + ln of its half
   if (!head_ok) return;
   const int kind = head < a.Hq ? 0 : (head < a.Hq + a.Hkv ? 1 : 2);   // q, k, v
-  if (kind < 2) {
-    constexpr double kRev = 0.15915494309189533577;   // 1 / (2 pi)
-    double pos[4];
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int T = min(t0 + tq * 128 + nb * 32 + ln, n_tok - 1);
-      const int b = T / a.q, i = T - b * a.q;
-      pos[nb] = (double)a.rope_pos[b] + (double)i;
-    }
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      double fr[4][4];   // revolutions per position of the lane's dimensions mb*32 + g*8 + hh*4 + e
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) fr[g][e] = a.inv_freq[mb * 32 + g * 8 + hh * 4 + e] * kRev;
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const double x = pos[nb] * fr[r >> 2][r & 3];
-          const float t = (float)(x - __builtin_rint(x));   // [-1/2, 1/2] revolutions
-          const float s = __builtin_amdgcn_sinf(t), c = __builtin_amdgcn_cosf(t);
-          const float lo = acc[nb][mb][r], hi = acc[nb][mb + 2][r];
-          acc[nb][mb][r] = lo * c - hi * s;
-          acc[nb][mb + 2][r] = hi * c + lo * s;
-        }
-    }
-  }
-  // transpose through this wave's 32 KB: [128 tokens][128 features] bf16,
-  // 16-byte chunk c of token row t stored at chunk c ^ (t & 15); the 8-byte
-  // halves are swapped for rows with bit 4 set, so the 32 lanes of one write
-  // (rows 0..31) spread over all 64 banks
   bf16 *const tw = wave == 0 ? W0 : (wave == 1 ? W1 : (wave == 2 ? X0 : X1));
+  double pos[4];
+  bool step_ok = true;
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int row = nb * 32 + ln;
-        bf16x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (bf16)acc[nb][mb][g * 4 + e];
-        *reinterpret_cast<bf16x4 *>(&tw[row * kPD + (((mb * 4 + g) ^ (row & 15)) << 3) + ((hh ^ (ln >> 4)) << 2)]) = v;
-      }
+  for (int nb = 0; nb < 4; ++nb) {
+    const int T = min(t0 + tq * 128 + nb * 32 + ln, n_tok - 1);
+    const int b = T / a.q, i = T - b * a.q;
+    pos[nb] = (double)a.rope_pos[b] + (double)i;
+    step_ok = step_ok && pos[nb] == pos[0] + 32.0 * nb;
+  }
+  // the three variants are chosen per wave (uniform branches)
+  if (kind == 2) rope_to_lds<false, false>(acc, tw, pos, a, hh, ln);
+  else if (__all(step_ok)) rope_to_lds<true, true>(acc, tw, pos, a, hh, ln);
+  else rope_to_lds<true, false>(acc, tw, pos, a, hh, ln);
   // the wave reads what its other lanes wrote: LDS completes a wave's
   // accesses in order; the fences keep the compiler from reordering them
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -259,7 +307,12 @@ __global__ __launch_bounds__(256, 1) void produce_kernel(ProduceArgs a, int n_pa
 
 }  // namespace
 
-hipError_t launch_produce(const ProduceArgs &a, hipStream_t s) {
+hipError_t launch_produce(const ProduceArgs &args, hipStream_t s) {
+  ProduceArgs a = args;
+  for (int j = 0; j < 64; ++j) {
+    a.step_rot[j][0] = (float)cos(32.0 * a.inv_freq[j]);
+    a.step_rot[j][1] = (float)sin(32.0 * a.inv_freq[j]);
+  }
   const int n_pairs = (int)cdiv(a.Hq + 2 * a.Hkv, 2), n_tb = (int)cdiv((int64_t)a.B * a.q, kPTok);
   const int total = n_pairs * n_tb;
   hipLaunchKernelGGL(produce_kernel, dim3((unsigned)total), dim3(256), 0, s, a, n_pairs, n_tb,

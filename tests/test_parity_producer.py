@@ -63,6 +63,7 @@ def _run(bd, X, W, rope_pos, dst_pos, Hq, Hkv, C, base=10000.0):
     (2, 200, 512, 4, 4, [17, 4096]),            # tiles spanning rows
     (5, 64, 128, 16, 2, [5, 9, 33, 70000, 1]),  # G = 8
     (3, 40, 128, 1, 1, [2, 50, 7]),             # three heads: an odd head count
+    (2, 128, 256, 4, 2, [1000003, 2500000]),   # stepped rotation at positions past 1e6
 ])
 def test_producer_small(bd, B, q, Dm, Hq, Hkv, rope_pos):
     note(f"producer B={B} q={q} Dm={Dm} Hq={Hq} Hkv={Hkv}")
