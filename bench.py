@@ -537,6 +537,8 @@ def main():
                     help="skip the per-configuration measurements of the other workloads")
     ap.add_argument("--only", choices=["select", "gather", "attn", "attn_dense", "attn_sparse", "scatter"],
                     help="time only this operation of the step (for counter runs); prints one line")
+    ap.add_argument("--select-only", choices=["sparse_32k", "sparse_128k"],
+                    help="time bd_select alone on one sparse workload (for profiling)")
     ap.add_argument("--producer-only", action="store_true",
                     help="time only the fused producer and its unfused sequence; prints one JSON line")
     ap.add_argument("--copy-probe", type=int, metavar="MB",
@@ -567,6 +569,18 @@ def main():
         return
     if args.producer_only:
         print(json.dumps({"producer_serving_mix": bench_producer(bd, dev, args.steps)}), flush=True)
+        return
+    if args.select_only:
+        wl = getattr(synth, args.select_only)()
+        Kc, Qsel = wl.Kc.to(dev), wl.Qsel.to(dev)
+        s_len, k_sel = wl.s_len.to(dev), wl.k_sel.to(dev)
+        idx = torch.empty((wl.B, wl.Hkv, wl.k_max), dtype=torch.int32, device=dev)
+        ws = bd.workspace(bd.select_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.d, wl.s_max, wl.k_max), dev)
+        f = lambda: bd.select(Qsel, Kc, s_len, wl.s_max, k_sel, wl.k_max, wl.sm_scale, idx_out=idx, ws=ws)
+        for _ in range(args.warmup):
+            f()
+        ms = time_calls(f, args.steps, 0, settle_ms=args.settle_ms)
+        print(f"select {args.select_only}: {ms * 1e3:.1f} us per call over {args.steps} calls", flush=True)
         return
     log("generating the serving-mix workload")
     wl = synth.serving_mix(seed=args.seed)
