@@ -252,6 +252,24 @@ def select_multi_sweep(bd, wl, Kc, s_len, k_sel, sel_bytes, ms_rep, dev, reps):
     return res
 
 
+def hbm_reference(dev, reps: int = 20) -> dict:
+    """Streaming rates of torch's own device kernels on 1 GiB fp32 buffers:
+    copy (read + write), sum (read) and fill (write), as the practical HBM
+    reference next to the 8 TB/s peak."""
+    import torch
+    n = (1 << 30) // 4
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    nb = n * 4
+    out = {"bytes": nb,
+           "copy_TB/s": round(2 * nb / (time_calls(lambda: b.copy_(a), reps) * 1e-3) / 1e12, 2),
+           "read_TB/s": round(nb / (time_calls(lambda: a.sum(), reps) * 1e-3) / 1e12, 2),
+           "write_TB/s": round(nb / (time_calls(lambda: b.fill_(1.0), reps) * 1e-3) / 1e12, 2)}
+    del a, b
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_producer(bd, dev, reps):
     """Flash-dLLM's fused cache producer (QKV projection + RoPE + cache write)
     at the serving-mix shape: 64 rows x 128 window tokens, hidden 4096 (32
@@ -695,6 +713,8 @@ def main():
         torch.cuda.empty_cache()
         configs = bench_configs(dev)
         configs["block_table_serving_mix_dense"] = block_table
+        log("HBM reference: torch copy / sum / fill of 1 GiB")
+        configs["hbm_reference"] = hbm_reference(dev)
 
     cpu = None
     if not args.no_cpu_baseline:
