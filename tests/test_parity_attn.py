@@ -97,6 +97,31 @@ def test_split_and_single_chunk_plans(bd, B, o_max, W):
     np.testing.assert_allclose(L.cpu().numpy(), ref_lse, atol=2e-3, rtol=1e-3)
 
 
+@pytest.mark.parametrize("n_rows", [200, 300])
+def test_many_rows_longest_first(bd, n_rows):
+    """More work items than the GPU holds: the planner kernel ranks the rows
+    and blocks take them longest first (with split prefixes at 200 rows, one
+    chunk per unit at 300).  The order is a schedule only, so every row must
+    match."""
+    G, Hkv, W, bl, d = 4, 2, 1, 32, 128
+    rs = np.random.default_rng(n_rows)
+    o = [int(v) for v in rs.integers(0, 400, size=n_rows)]
+    o[int(rs.integers(0, n_rows))] = 0
+    note(f"attn many rows n={n_rows} o in [{min(o)}, {max(o)}]")
+    C = max(o) + W * bl + 8
+    Q, K, V, q, t = _cache_case(700 + n_rows, n_rows, C, G * Hkv, Hkv, d, bl, W, o)
+    ws = bd.attn_workspace_size(bd.BD_BF16, n_rows, G * Hkv, Hkv, d, q, n_rows, max(o))
+    # the planner's order buffer (n_rows int32), plus split partials at 200 rows
+    order = ((n_rows * 4 + 255) // 256) * 256
+    assert (ws > order) if n_rows == 200 else (ws == order)
+    scale = 1.0 / math.sqrt(d)
+    out, _ = _run_cache(bd, Q, K, V, o, bl, scale)
+    pick = sorted(set(rs.choice(n_rows, 20, replace=False).tolist() +
+                      [int(np.argmax(o)), int(np.argmin(o))]))
+    ref, _ = orc.cache_attention_eq6(Q[pick], K[pick], V[pick], [o[i] for i in pick], bl, scale)
+    check_attention(out[pick], ref, torch.bfloat16, label=f"many rows {n_rows}")
+
+
 def test_sharp_logits(bd):
     """Unscaled N(0,1) Q, K, V with sm_scale = 1: peaked softmax."""
     note("attn sharp logits")
