@@ -20,8 +20,8 @@
 // <= 256), so the O rescale runs on few tiles.
 //
 // Pipelining: K and V tiles are double-buffered in LDS with one barrier per
-// tile; the global loads of tile t+1 are issued before the MFMAs of tile t
-// and written to LDS after them.  Inside a tile the exponentials of the
+// tile; the loads of tile t+1 are issued before the MFMAs of tile t (K
+// straight into LDS, V into registers and written transposed after them).  Inside a tile the exponentials of the
 // second 32-key half are independent of the P V MFMAs of the first half.
 //
 // Rows at or past the prefix length are never read (the buffer range check
@@ -43,9 +43,9 @@ namespace {
 // ----------------------------------------------------------------- MFMA path
 constexpr int kD = 128;            // head dim of the MFMA path
 constexpr int kTK = 64;            // keys per staged tile
-constexpr int kKStr = kD + 8;      // LDS row stride of K (elements): 272 B
+constexpr int kKRow = kD;          // LDS row of K (elements): 256 B, 16-byte chunks swizzled
 constexpr int kVStr = kTK + 8;     // LDS row stride of V^T (elements): 144 B
-constexpr int kKTile = kTK * kKStr;
+constexpr int kKTile = kTK * kKRow;
 constexpr int kVTile = kD * kVStr;
 constexpr float kRescaleSlack = 8.f;  // log2 units
 
@@ -100,10 +100,10 @@ __device__ inline PrefixSrc prefix_src(const AttnArgs &a, const RowRef &r, int h
 }
 
 // Block of NW waves, one 32-column group per wave; two waves share a SIMD.
-// Tile staging: 256 V items (4 keys x 8 dims) and 1024 K pieces (16 bytes)
-// per 64-key tile.  With 8 waves, waves 0-3 stage V and waves 4-7 stage K
-// (4 loads per thread each); with 4 waves every thread stages 1 V item and
-// 4 K pieces.
+// Tile staging: 256 V items (4 keys x 8 dims, through registers) and 16 K
+// transfers of 1 KB (memory to LDS) per 64-key tile.  With 8 waves, waves
+// 0-3 stage V (4 loads per thread) and waves 4-7 K (4 transfers per wave);
+// with 4 waves every wave does both.
 template <int NW, int G>
 struct Shape {
   static constexpr int NT = 64 * NW;           // threads
@@ -112,7 +112,6 @@ struct Shape {
   static constexpr int NQ = 32 * QB;           // queries per block
   static constexpr int NCOL = 32 * NCG;        // columns per block
   static constexpr bool SPLIT_STAGE = NW == 8;
-  static constexpr int KP = SPLIT_STAGE ? 4 : kTK * 16 / NT;  // K pieces per staging thread
   static constexpr int VI = 1;                 // V items per staging thread
   static_assert(QB >= 1 && NCG % G == 0, "GQA group larger than the block");
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
@@ -184,8 +183,13 @@ __device__ inline bool decode_item(const AttnArgs &a, int bid, Item &it, int nq_
 template <int NW, int G, bool WM, bool BT>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) {
   using S = Shape<NW, G>;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][kKTile];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[2][kVTile];
+  // one array per buffer: the compiler then sees that the K transfers into
+  // one buffer never alias the fragment reads of the other, and waits for
+  // them only at the tile barrier
+  __shared__ __attribute__((aligned(16))) bf16 Ks0[kKTile];
+  __shared__ __attribute__((aligned(16))) bf16 Ks1[kKTile];
+  __shared__ __attribute__((aligned(16))) bf16 Vt0[kVTile];
+  __shared__ __attribute__((aligned(16))) bf16 Vt1[kVTile];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -241,22 +245,23 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
   auto tile_base = [&](int tt) { return tt < n_pref ? it.kbeg + tt * kTK : (tt - n_pref) * kTK; };
   auto tile_limit = [&](int tt) { return tt < n_pref ? it.kend : win_len; };
 
-  // ---- staging: global -> registers -> LDS with buffer loads.  Each tile
-  // gets a buffer resource based at its first key whose size ends at the
-  // tile's last valid key, so rows at or past the limit read as zeros (the
-  // hardware range check) and unused rows are never touched.  Offsets are
-  // 32-bit: one tile spans at most kTK rows (the host checks the row
-  // strides).
-  // K piece: key piece / 16, dims 8 * (piece % 16): 16 lanes read one
-  // 256-byte key row.  V item: keys 4*k4 .. 4*k4+3 with k4 = tid % 16 and
-  // dims 8 * (tid / 16 % 16): the 16 lanes of a write pass hold the 16
-  // key-quads of one dim chunk, so each transposed write pass fills one
-  // 128-byte V^T row.
+  // ---- staging with buffer loads.  Each tile gets a buffer resource based
+  // at its first key whose size ends at the tile's last valid key, so rows at
+  // or past the limit read as zeros (the hardware range check) and unused
+  // rows are never touched.  Offsets are 32-bit: one tile spans at most kTK
+  // rows (the host checks the row strides).
+  // K goes straight from memory into LDS (buffer-to-LDS transfers): four
+  // K-staging waves each move 4 blocks of 4 key rows, one 1 KB transfer per
+  // block; lane l writes the 16 bytes at l * 16 of its block, i.e. chunk
+  // l % 16 of row l / 16 in the block, and loads into it global chunk
+  // (l % 16) ^ (row % 16), so chunk c of key row r sits at chunk
+  // c ^ (r % 16) of the row (the fragment reads of 32 rows then spread over
+  // the banks).  V goes through registers: item keys 4*k4 .. 4*k4+3 with
+  // k4 = tid % 16 and dims 8 * (tid / 16 % 16); the 16 lanes of a write pass
+  // hold the 16 key-quads of one dim chunk, so each transposed write pass
+  // fills one 128-byte V^T row.
   const bool stage_v = !S::SPLIT_STAGE || wave < 4;
   const bool stage_k = !S::SPLIT_STAGE || wave >= 4;
-  const int ktid = S::SPLIT_STAGE ? tid - 256 : tid;   // K staging thread index
-  const int kstep = S::SPLIT_STAGE ? 256 : S::NT;
-  bf16x8 kreg[S::KP];
   bf16x8 vreg[4];
   auto rsrc = [](const bf16 *p, int64_t row_el, int base, int limit) {
     const int64_t rowb = row_el * 2;
@@ -264,10 +269,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
     return __builtin_amdgcn_make_buffer_rsrc((void *)(p + (int64_t)base * row_el), (short)0,
                                              (int)(rows * rowb), 0x00020000);
   };
-  // Byte offsets of the loads in flight; kept live until the LDS stores
+  // Byte offsets of the V loads in flight; kept live until the LDS stores
   // (keep_offsets) so that no later instruction reuses their registers while
   // the loads are outstanding, which would make the compiler wait for them.
-  int koff[S::KP], voff[4];
+  int voff[4];
   // block-table mode: page id of the next prefix tile to load, requested
   // one tile ahead with a buffer load (it waits on the vector memory counter
   // with the K/V loads, not on the LDS counter the tile's fragment reads
@@ -282,7 +287,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
       pg_next = (int)__builtin_amdgcn_raw_buffer_load_b32(trsrc, (it.toff + k0 / a.page) * 4, 0, 0);
     }
   };
-  auto load = [&](int tt) {
+  auto load = [&](int tt, bf16 *Kn) __attribute__((always_inline)) {
     const bool win = tt >= n_pref;
     const int64_t sp = win ? w_row : p_row;
     const int rowb = (int)(sp * 2);
@@ -304,12 +309,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
       else rows_buf0 = rows;
     }
     if (stage_k) {
+      const int wk = __builtin_amdgcn_readfirstlane(wave) - (S::SPLIT_STAGE ? 4 : 0);
       const auto r = rsrc(kbase, sp, base, limit);
 #pragma unroll
-      for (int p = 0; p < S::KP; ++p) {
-        const int piece = ktid + p * kstep;
-        koff[p] = (piece >> 4) * rowb + (piece & 15) * 16;
-        kreg[p] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, koff[p], 0, 0));
+      for (int p = 0; p < 4; ++p) {
+        const int blk = wk * 4 + p;
+        const int row = blk * 4 + (lane >> 4), pc = lane & 15;
+#if defined(__HIP_DEVICE_COMPILE__)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)&Kn[blk * 512], 16,
+                                                 row * rowb + ((pc ^ (row & 15)) << 4), 0, 0, 0);
+#else
+        (void)r, (void)row, (void)pc;   // the builtin exists in the device pass only
+#endif
       }
     }
     if (stage_v) {
@@ -325,25 +336,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
   };
   auto keep_offsets = [&]() {
 #pragma unroll
-    for (int p = 0; p < S::KP; ++p) asm volatile("" ::"v"(koff[p]));
-#pragma unroll
     for (int jj = 0; jj < 4; ++jj) asm volatile("" ::"v"(voff[jj]));
   };
-  auto store = [&](int buf) {
-    if (stage_k) {
-#pragma unroll
-      for (int p = 0; p < S::KP; ++p) {
-        const int piece = ktid + p * kstep;
-        *reinterpret_cast<bf16x8 *>(&Ks[buf][(piece >> 4) * kKStr + (piece & 15) * 8]) = kreg[p];
-      }
-    }
+  auto store = [&](bf16 *Vn) __attribute__((always_inline)) {
     if (stage_v) {
       const int k4 = tid & 15, db = (tid >> 4) & 15;
       const int slot = (k4 >> 2) * 16 + vt_slot((k4 & 3) * 4);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         bf16x4 w = {vreg[0][e], vreg[1][e], vreg[2][e], vreg[3][e]};
-        *reinterpret_cast<bf16x4 *>(&Vt[buf][(db * 8 + e) * kVStr + slot]) = w;
+        *reinterpret_cast<bf16x4 *>(&Vn[(db * 8 + e) * kVStr + slot]) = w;
       }
     }
   };
@@ -365,29 +367,30 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
   // latency is covered inside the wave.  3 to 5 measure the same; 6 is
   // slower.
   constexpr int kFragAhead = 4;
-  auto kfrag = [&](int buf, int i) {  // K fragment i = ks * 2 + kt
-    return ld_bf16x8(&Ks[buf][((i & 1) * 32 + ln) * kKStr + (i >> 1) * 16 + hh * 8]);
+  auto kfrag = [&](const bf16 *Kb, int i) __attribute__((always_inline)) {  // K fragment i = ks * 2 + kt
+    const int row = (i & 1) * 32 + ln, c = (i >> 1) * 2 + hh;
+    return ld_bf16x8(&Kb[row * kKRow + ((c ^ (row & 15)) << 3)]);
   };
-  auto vfrag = [&](int buf, int j) {  // V^T fragment j = kt * 8 + k2 * 4 + dt
-    return ld_bf16x8(&Vt[buf][((j & 3) * 32 + ln) * kVStr + (j >> 3) * 32 + ((j >> 2) & 1) * 16 + hh * 8]);
+  auto vfrag = [&](const bf16 *Vb, int j) __attribute__((always_inline)) {  // V^T fragment j = kt * 8 + k2 * 4 + dt
+    return ld_bf16x8(&Vb[((j & 3) * 32 + ln) * kVStr + (j >> 3) * 32 + ((j >> 2) & 1) * 16 + hh * 8]);
   };
-  auto tile = [&](int tt, int buf) {
+  auto tile = [&](int tt, int buf, const bf16 *Kb, const bf16 *Vb) __attribute__((always_inline)) {
     f32x16 s[2];
     // the two 32-key halves interleaved: two independent accumulator chains
     s[0] = f32x16{};
     s[1] = f32x16{};
     bf16x8 kf[16];
 #pragma unroll
-    for (int i = 0; i < kFragAhead; ++i) kf[i] = kfrag(buf, i);
+    for (int i = 0; i < kFragAhead; ++i) kf[i] = kfrag(Kb, i);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      if (i + kFragAhead < 16) kf[i + kFragAhead] = kfrag(buf, i + kFragAhead);
+      if (i + kFragAhead < 16) kf[i + kFragAhead] = kfrag(Kb, i + kFragAhead);
       s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qop[i >> 1], s[i & 1], 0, 0, 0);
     }
     // the first V^T fragments are read while the softmax runs
     bf16x8 vf[16];
 #pragma unroll
-    for (int j = 0; j < kFragAhead; ++j) vf[j] = vfrag(buf, j);
+    for (int j = 0; j < kFragAhead; ++j) vf[j] = vfrag(Vb, j);
     // schedule: kFragAhead reads, then (1 MFMA, 1 read) x 16 (the last
     // kFragAhead reads are the V^T prefetches)
     __builtin_amdgcn_sched_group_barrier(0x100, kFragAhead, 0);
@@ -471,7 +474,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
         for (int dt = 0; dt < kD / 32; ++dt) {
           const int j = kt * 8 + k2 * 4 + dt;
           acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], pop[k2], acc[dt], 0, 0, 0);
-          if (j + kFragAhead < 16) vf[j + kFragAhead] = vfrag(buf, j + kFragAhead);
+          if (j + kFragAhead < 16) vf[j + kFragAhead] = vfrag(Vb, j + kFragAhead);
           // MFMAs and LDS reads keep this order (read j+4 after MFMA j);
           // VALU, SALU and transcendental work may move across
           __builtin_amdgcn_sched_barrier(0x406);
@@ -483,22 +486,30 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
   // ---- tile loop: tile tt+1 is loaded during tile tt (double-buffered LDS)
   request_page(0);
   if (n_tiles > 0) {
-    load(0);
-    store(0);
+    load(0, Ks0);
+    store(Vt0);
   }
   // every load issued so far (Q, tile 0) has landed: the loop below then
-  // only waits for its own prefetches, at the LDS stores
+  // only waits for its own prefetches, at the LDS stores and the barrier
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int tt = 0; tt < n_tiles; ++tt) {
+  // the K transfers into a buffer complete before the barrier that ends the
+  // tile (the barrier's fence waits for this wave's transfers), so the next
+  // tile reads them after every wave's have landed
+  auto step = [&](int tt, int buf, const bf16 *Kb, const bf16 *Vb, bf16 *Kn, bf16 *Vn)
+      __attribute__((always_inline)) {
     const bool more = tt + 1 < n_tiles;
-    if (more) load(tt + 1);
-    tile(tt, tt & 1);
+    if (more) load(tt + 1, Kn);
+    tile(tt, buf, Kb, Vb);
     if (more) {
-      store((tt + 1) & 1);
+      store(Vn);
       keep_offsets();
     }
     __syncthreads();
+  };
+  for (int tt = 0; tt < n_tiles; tt += 2) {
+    step(tt, 0, Ks0, Vt0, Ks1, Vt1);
+    if (tt + 1 < n_tiles) step(tt + 1, 1, Ks1, Vt1, Ks0, Vt0);
   }
 
   // ---- epilogue
