@@ -13,16 +13,18 @@
 // (keys on M, columns on N): a lane then holds 16 scores of one column, so
 // the online softmax (FlashAttention running max / sum) is lane-local, with
 // one exchange with lane l^32 for the column max.  O^T += V^T P^T takes the
-// S^T accumulator registers directly as the B operand; V is staged
-// transposed in LDS with the key order inside each 16-key group permuted to
-// match.  The running max is only raised when a tile's max exceeds it by
-// more than 2^8 (the result is the same for any reference value; p stays
-// <= 256), so the O rescale runs on few tiles.
+// S^T accumulator registers directly as the B operand; V stays key-major in
+// LDS and its V^T fragments come from transposing LDS reads
+// (ds_read_b64_tr_b16), two per fragment, which hand each lane the keys its
+// accumulator registers hold.  The running max is only raised when a tile's
+// max exceeds it by more than 2^8 (the result is the same for any reference
+// value; p stays <= 256), so the O rescale runs on few tiles.
 //
 // Pipelining: K and V tiles are double-buffered in LDS with one barrier per
-// tile; the loads of tile t+1 are issued before the MFMAs of tile t (K
-// straight into LDS, V into registers and written transposed after them).  Inside a tile the exponentials of the
-// second 32-key half are independent of the P V MFMAs of the first half.
+// tile; both go from memory straight into LDS (buffer-to-LDS transfers, no
+// registers, no LDS store instructions), the transfers of tile t+1 issued
+// before the MFMAs of tile t.  Inside a tile the exponentials of the second
+// 32-key half are independent of the P V MFMAs of the first half.
 //
 // Rows at or past the prefix length are never read (the buffer range check
 // returns zeros for them, and their scores are masked), which keeps NaN
@@ -44,22 +46,14 @@ namespace {
 constexpr int kD = 128;            // head dim of the MFMA path
 constexpr int kTK = 64;            // keys per staged tile
 constexpr int kKRow = kD;          // LDS row of K (elements): 256 B, 16-byte chunks swizzled
-constexpr int kVStr = kTK + 8;     // LDS row stride of V^T (elements): 144 B
 constexpr int kKTile = kTK * kKRow;
-constexpr int kVTile = kD * kVStr;
+constexpr int kVTile = kTK * kD;   // key-major V (elements): 256-byte rows, 16-byte chunks swizzled
 constexpr float kRescaleSlack = 8.f;  // log2 units
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 struct bf16x2x4 { bf16x2 v[4]; };
 
 __device__ inline bf16x8 ld_bf16x8(const bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
-
-// LDS slot of key k16 (0..15) inside a 16-key group of V^T: bits 2 and 3
-// swapped, so that lane half hh reads keys {hh*4 + 0..3, 8 + hh*4 + 0..3},
-// the keys its S^T accumulator registers hold.
-__device__ inline int vt_slot(int k16) {
-  return (k16 & 3) | ((k16 & 4) << 1) | ((k16 & 8) >> 1);
-}
 
 // Row list position rl -> row and prefix source (the second source holds
 // the positions at or past n_rows1).
@@ -100,10 +94,9 @@ __device__ inline PrefixSrc prefix_src(const AttnArgs &a, const RowRef &r, int h
 }
 
 // Block of NW waves, one 32-column group per wave; two waves share a SIMD.
-// Tile staging: 256 V items (4 keys x 8 dims, through registers) and 16 K
-// transfers of 1 KB (memory to LDS) per 64-key tile.  With 8 waves, waves
-// 0-3 stage V (4 loads per thread) and waves 4-7 K (4 transfers per wave);
-// with 4 waves every wave does both.
+// Tile staging: 16 K and 16 V transfers of 1 KB (memory to LDS) per 64-key
+// tile.  With 8 waves, waves 0-3 move V and waves 4-7 K (4 transfers per
+// wave); with 4 waves every wave moves 4 of each.
 template <int NW, int G>
 struct Shape {
   static constexpr int NT = 64 * NW;           // threads
@@ -250,29 +243,22 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
   // or past the limit read as zeros (the hardware range check) and unused
   // rows are never touched.  Offsets are 32-bit: one tile spans at most kTK
   // rows (the host checks the row strides).
-  // K goes straight from memory into LDS (buffer-to-LDS transfers): four
-  // K-staging waves each move 4 blocks of 4 key rows, one 1 KB transfer per
+  // K and V go straight from memory into LDS (buffer-to-LDS transfers):
+  // each staging wave moves 4 blocks of 4 key rows, one 1 KB transfer per
   // block; lane l writes the 16 bytes at l * 16 of its block, i.e. chunk
-  // l % 16 of row l / 16 in the block, and loads into it global chunk
-  // (l % 16) ^ (row % 16), so chunk c of key row r sits at chunk
-  // c ^ (r % 16) of the row (the fragment reads of 32 rows then spread over
-  // the banks).  V goes through registers: item keys 4*k4 .. 4*k4+3 with
-  // k4 = tid % 16 and dims 8 * (tid / 16 % 16); the 16 lanes of a write pass
-  // hold the 16 key-quads of one dim chunk, so each transposed write pass
-  // fills one 128-byte V^T row.
+  // l % 16 of row l / 16 in the block, and loads into it a chosen global
+  // chunk, which swizzles the rows: chunk c of key row r sits at chunk
+  // c ^ (r % 16) for K (the fragment reads of 32 rows spread over the
+  // banks) and at c ^ 4 (r % 4) for V (the transposing reads of 4 rows x
+  // 4 dims per lane group spread over the banks).
   const bool stage_v = !S::SPLIT_STAGE || wave < 4;
   const bool stage_k = !S::SPLIT_STAGE || wave >= 4;
-  bf16x8 vreg[4];
   auto rsrc = [](const bf16 *p, int64_t row_el, int base, int limit) {
     const int64_t rowb = row_el * 2;
     const int rows = min(limit - base, kTK);
     return __builtin_amdgcn_make_buffer_rsrc((void *)(p + (int64_t)base * row_el), (short)0,
                                              (int)(rows * rowb), 0x00020000);
   };
-  // Byte offsets of the V loads in flight; kept live until the LDS stores
-  // (keep_offsets) so that no later instruction reuses their registers while
-  // the loads are outstanding, which would make the compiler wait for them.
-  int voff[4];
   // block-table mode: page id of the next prefix tile to load, requested
   // one tile ahead with a buffer load (it waits on the vector memory counter
   // with the K/V loads, not on the LDS counter the tile's fragment reads
@@ -287,7 +273,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
       pg_next = (int)__builtin_amdgcn_raw_buffer_load_b32(trsrc, (it.toff + k0 / a.page) * 4, 0, 0);
     }
   };
-  auto load = [&](int tt, bf16 *Kn) __attribute__((always_inline)) {
+  auto load = [&](int tt, bf16 *Kn, bf16 *Vn) __attribute__((always_inline)) {
     const bool win = tt >= n_pref;
     const int64_t sp = win ? w_row : p_row;
     const int rowb = (int)(sp * 2);
@@ -319,37 +305,27 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)&Kn[blk * 512], 16,
                                                  row * rowb + ((pc ^ (row & 15)) << 4), 0, 0, 0);
 #else
-        (void)r, (void)row, (void)pc;   // the builtin exists in the device pass only
+        (void)r, (void)row, (void)pc, (void)rowb;   // the builtin exists in the device pass only
 #endif
       }
     }
     if (stage_v) {
+      const int wv = __builtin_amdgcn_readfirstlane(wave);
       const auto r = rsrc(vbase, sp, base, limit);
-      const int k4 = tid & 15, db = (tid >> 4) & 15;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        voff[jj] = (4 * k4 + jj) * rowb + db * 16;
-        vreg[jj] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff[jj], 0, 0));
+      for (int p = 0; p < 4; ++p) {
+        const int blk = wv * 4 + p;
+        const int row = blk * 4 + (lane >> 4), pc = lane & 15;
+#if defined(__HIP_DEVICE_COMPILE__)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)&Vn[blk * 512], 16,
+                                                 row * rowb + ((pc ^ ((row & 3) << 2)) << 4), 0, 0, 0);
+#else
+        (void)r, (void)row, (void)pc, (void)rowb;
+#endif
       }
     }
     request_page(tt + 1);
   };
-  auto keep_offsets = [&]() {
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) asm volatile("" ::"v"(voff[jj]));
-  };
-  auto store = [&](bf16 *Vn) __attribute__((always_inline)) {
-    if (stage_v) {
-      const int k4 = tid & 15, db = (tid >> 4) & 15;
-      const int slot = (k4 >> 2) * 16 + vt_slot((k4 & 3) * 4);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        bf16x4 w = {vreg[0][e], vreg[1][e], vreg[2][e], vreg[3][e]};
-        *reinterpret_cast<bf16x4 *>(&Vn[(db * 8 + e) * kVStr + slot]) = w;
-      }
-    }
-  };
-
   f32x16 acc[kD / 32];
 #pragma unroll
   for (int dt = 0; dt < kD / 32; ++dt) acc[dt] = f32x16{};
@@ -371,8 +347,23 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
     const int row = (i & 1) * 32 + ln, c = (i >> 1) * 2 + hh;
     return ld_bf16x8(&Kb[row * kKRow + ((c ^ (row & 15)) << 3)]);
   };
-  auto vfrag = [&](const bf16 *Vb, int j) __attribute__((always_inline)) {  // V^T fragment j = kt * 8 + k2 * 4 + dt
-    return ld_bf16x8(&Vb[((j & 3) * 32 + ln) * kVStr + (j >> 3) * 32 + ((j >> 2) & 1) * 16 + hh * 8]);
+  // V^T fragment j = kt * 8 + k2 * 4 + dt from key-major V by two
+  // transposing reads: lane (hh, ln) gets V[kb + hh*4 + e][db + ln] and
+  // V[kb + 8 + hh*4 + e][db + ln] (e < 4), the keys its S^T accumulator
+  // registers hold; chunk c of key row r sits at chunk c ^ 4 (r mod 4)
+  const int tr_g = lane >> 4, tr_j = lane & 15;
+  const int tr_row = (tr_g >> 1) * 4 + (tr_j >> 2);    // + kb (a multiple of 16)
+  const int tr_col = 16 * (tr_g & 1) + 4 * (tr_j & 3);  // + db (a multiple of 32)
+  auto vfrag = [&](const bf16 *Vb, int j) __attribute__((always_inline)) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef short v8s __attribute__((ext_vector_type(8)));
+    const int kb = (j >> 3) * 32 + ((j >> 2) & 1) * 16, db = (j & 3) * 32;
+    const int row = kb + tr_row, col = db + tr_col;
+    const bf16 *p = &Vb[row * kD + (((col >> 3) ^ ((row & 3) << 2)) << 3) + (col & 7)];
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)p);
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(p + 8 * kD));
+    const v8s w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, w);
   };
   auto tile = [&](int tt, int buf, const bf16 *Kb, const bf16 *Vb) __attribute__((always_inline)) {
     f32x16 s[2];
@@ -485,10 +476,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
 
   // ---- tile loop: tile tt+1 is loaded during tile tt (double-buffered LDS)
   request_page(0);
-  if (n_tiles > 0) {
-    load(0, Ks0);
-    store(Vt0);
-  }
+  if (n_tiles > 0) load(0, Ks0, Vt0);
   // every load issued so far (Q, tile 0) has landed: the loop below then
   // only waits for its own prefetches, at the LDS stores and the barrier
   __builtin_amdgcn_s_waitcnt(0);
@@ -498,13 +486,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
   // tile reads them after every wave's have landed
   auto step = [&](int tt, int buf, const bf16 *Kb, const bf16 *Vb, bf16 *Kn, bf16 *Vn)
       __attribute__((always_inline)) {
-    const bool more = tt + 1 < n_tiles;
-    if (more) load(tt + 1, Kn);
+    if (tt + 1 < n_tiles) load(tt + 1, Kn, Vn);
     tile(tt, buf, Kb, Vb);
-    if (more) {
-      store(Vn);
-      keep_offsets();
-    }
     __syncthreads();
   };
   for (int tt = 0; tt < n_tiles; tt += 2) {
