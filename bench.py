@@ -559,6 +559,9 @@ def main():
                     help="time only this operation of the step (for counter runs); prints one line")
     ap.add_argument("--select-only", choices=["sparse_32k", "sparse_128k"],
                     help="time bd_select alone on one sparse workload (for profiling)")
+    ap.add_argument("--pool-only", choices=["sparse_32k", "sparse_128k"],
+                    help="time the T denoising attentions over one sparse workload's pool alone "
+                         "(select and gather run once before, untimed; for profiling)")
     ap.add_argument("--producer-only", action="store_true",
                     help="time only the fused producer and its unfused sequence; prints one JSON line")
     ap.add_argument("--copy-probe", type=int, metavar="MB",
@@ -601,6 +604,33 @@ def main():
             f()
         ms = time_calls(f, args.steps, 0, settle_ms=args.settle_ms)
         print(f"select {args.select_only}: {ms * 1e3:.1f} us per call over {args.steps} calls", flush=True)
+        return
+    if args.pool_only:
+        wl = getattr(synth, args.pool_only)()
+        Kc, Vc, Qsel = wl.Kc.to(dev), wl.Vc.to(dev), wl.Qsel.to(dev)
+        s_len, k_sel = wl.s_len.to(dev), wl.k_sel.to(dev)
+        B, Hkv, d, k_max, s_max = wl.B, wl.Hkv, wl.d, wl.k_max, wl.s_max
+        idx = torch.empty((B, Hkv, k_max), dtype=torch.int32, device=dev)
+        ws = bd.workspace(bd.select_workspace_size(B, wl.Hq, Hkv, d, s_max, k_max), dev)
+        pool_k = torch.zeros((B, k_max, Hkv, d), dtype=Kc.dtype, device=dev)
+        pool_v = torch.zeros_like(pool_k)
+        bd.select(Qsel, Kc, s_len, s_max, k_sel, k_max, wl.sm_scale, idx_out=idx, ws=ws)
+        bd.gather(Kc, Vc, idx, k_sel, pool_k, pool_v)
+        steps_q = [x.to(dev) for x in wl.extra["step_q"]]
+        steps_kv = [(a.to(dev), b.to(dev)) for a, b in wl.extra["step_kv"]]
+        outb = torch.empty_like(steps_q[0])
+        ws_a = bd.workspace(bd.attn_workspace_size(Qsel.dtype, B, wl.Hq, Hkv, d, wl.q, B, k_max), dev)
+
+        def f():
+            for st in range(wl.T):
+                wk, wv = steps_kv[st]
+                bd.attn_packed(steps_q[st], pool_k, pool_v, k_sel, k_max, wk, wv, wl.bl,
+                               wl.sm_scale, out=outb, ws=ws_a)
+        for _ in range(args.warmup):
+            f()
+        ms = time_calls(f, args.steps, 0, settle_ms=args.settle_ms)
+        print(f"pool attention {args.pool_only}: {ms * 1e3 / wl.T:.2f} us per denoising step "
+              f"over {args.steps} x {wl.T} steps", flush=True)
         return
     log("generating the serving-mix workload")
     wl = synth.serving_mix(seed=args.seed)

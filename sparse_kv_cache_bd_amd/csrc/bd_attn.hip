@@ -273,6 +273,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
       pg_next = (int)__builtin_amdgcn_raw_buffer_load_b32(trsrc, (it.toff + k0 / a.page) * 4, 0, 0);
     }
   };
+  // per-lane parts of the transfer offsets, fixed over the tiles: lane l
+  // fills chunk l % 16 of row 4 blk + l / 16; row r's global chunk c lands at
+  // chunk c ^ (r % 16) for K and c ^ 4 (r % 4) for V, and r % 16 =
+  // 4 p + l / 16 for transfer p, r % 4 = l / 16
+  const int lrow_p = (lane >> 4) * (int)(p_row * 2), lrow_w = (lane >> 4) * (int)(w_row * 2);
+  int kchunk[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) kchunk[p] = ((lane & 15) ^ (4 * p + (lane >> 4))) << 4;
+  const int vchunk = ((lane & 15) ^ ((lane >> 4) << 2)) << 4;
   auto load = [&](int tt, bf16 *Kn, bf16 *Vn) __attribute__((always_inline)) {
     const bool win = tt >= n_pref;
     const int64_t sp = win ? w_row : p_row;
@@ -294,18 +303,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
       if (tt & 1) rows_buf1 = rows;
       else rows_buf0 = rows;
     }
+    // lane offset: row (lane / 16) of the block at the tile's row stride
+    const int lrow = win ? lrow_w : lrow_p;
     if (stage_k) {
       const int wk = __builtin_amdgcn_readfirstlane(wave) - (S::SPLIT_STAGE ? 4 : 0);
       const auto r = rsrc(kbase, sp, base, limit);
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const int blk = wk * 4 + p;
-        const int row = blk * 4 + (lane >> 4), pc = lane & 15;
 #if defined(__HIP_DEVICE_COMPILE__)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)&Kn[blk * 512], 16,
-                                                 row * rowb + ((pc ^ (row & 15)) << 4), 0, 0, 0);
+                                                 blk * 4 * rowb + lrow + kchunk[p], 0, 0, 0);
 #else
-        (void)r, (void)row, (void)pc, (void)rowb;   // the builtin exists in the device pass only
+        (void)r, (void)blk, (void)rowb, (void)lrow;   // the builtin exists in the device pass only
 #endif
       }
     }
@@ -315,12 +325,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const int blk = wv * 4 + p;
-        const int row = blk * 4 + (lane >> 4), pc = lane & 15;
 #if defined(__HIP_DEVICE_COMPILE__)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)&Vn[blk * 512], 16,
-                                                 row * rowb + ((pc ^ ((row & 3) << 2)) << 4), 0, 0, 0);
+                                                 blk * 4 * rowb + lrow + vchunk, 0, 0, 0);
 #else
-        (void)r, (void)row, (void)pc, (void)rowb;
+        (void)r, (void)blk, (void)rowb, (void)lrow;
 #endif
       }
     }
