@@ -8,15 +8,15 @@
 // tokens: Y^T = W_head X^T with v_mfma_f32_32x32x16_bf16, features on M and
 // tokens on N, so a lane ends with 16 features of one token; dimension j and
 // its rotary partner j + 64 sit in the same lane and register (M blocks mb
-// and mb + 2).  Four waves, one per SIMD: wave (head h, token half t) owns
-// the head's 128 features x 128 tokens, 16 accumulators in AGPRs, so each
-// MFMA costs half an LDS fragment read.  Tiles of 64 hidden elements of W and
-// X are double-buffered in LDS (128 KB); while a tile's 64 MFMAs run, the
-// next tile goes from registers to the other buffer and the tile after it is
-// loaded into the registers, the three interleaved one-for-one with the
-// MFMAs by scheduling barriers.  One block barrier per tile, placed before
-// the tile's last 16 MFMAs, which then hide the next tile's first fragment
-// reads.  Blocks are
+// and mb + 2).  Eight waves, two per SIMD (one wave alone cannot issue MFMAs
+// back to back): wave (head h, token quarter t) owns the head's 128 features
+// x 64 tokens, 8 accumulators, so each MFMA costs three quarters of an LDS
+// fragment read.  Tiles of 64 hidden elements of W and X are double-buffered
+// in LDS (128 KB); while a tile's 32 MFMAs per wave run, the next tile goes
+// from registers to the other buffer and the tile after it is loaded into
+// the registers, the three interleaved with the MFMAs by scheduling barriers.
+// One block barrier per tile, placed before the tile's last 8 MFMAs, which
+// then hide the next tile's first fragment reads.  Blocks are
 // ordered so that the 32 running on one XCD (dispatch is round-robin over
 // the 8 XCDs) share 4 head pairs and 8 token tiles, which their L2 serves.
 //
@@ -24,19 +24,20 @@
 // (position x inverse frequency / 2 pi; positions reach 1e5 and more, the
 // inverse frequencies come from the host in double), reduced to [-1/2, 1/2]
 // in double, and its sine and cosine taken by the hardware's
-// revolution-scaled sin / cos in fp32.  A lane's four tokens are 32 apart;
-// when all of a wave's lanes hold four consecutive positions of one row
-// (always when the window length is a multiple of 128), only the first angle
-// is formed that way and the next three advance it by the fixed rotation of
-// 32 positions (cos, sin of 32 x inverse frequency, computed on the host in
-// double): three complex products in fp32 in place of three
-// double-precision reductions and six sin / cos.  The rotation is applied to
-// the fp32 accumulators, results are rounded to bf16 once and written, per
-// 32 x 32 block pair, into the wave's own 32 KB of the (now idle) LDS; read
-// back token-major, every store instruction writes whole 256-byte head rows
-// of 4 tokens.  Each of the three variants (no rotation, per-angle, stepped)
-// is one straight-line pass over the accumulators, so none of them keeps
-// more than one block pair outside the accumulator registers.
+// revolution-scaled sin / cos in fp32.  A lane's two tokens are 32 apart;
+// when all of a wave's lanes hold two consecutive positions of one row
+// (always when the window length is a multiple of 64), only the first angle
+// is formed that way and the second advances it by the fixed rotation of 32
+// positions (cos, sin of 32 x inverse frequency, computed on the host in
+// double): one complex product in fp32 in place of a double-precision
+// reduction and two sin / cos.  The rotation is applied to the fp32
+// accumulators, results are rounded to bf16 once and written, per 32 x 32
+// block pair, into the wave's own 16 KB of the (now idle) LDS; read back
+// token-major, every store instruction writes whole 256-byte head rows of 4
+// tokens (streaming stores: nothing in this launch reads them).  Each of the
+// three variants (no rotation, per-angle, stepped) is one straight-line pass
+// over the accumulators, so none of them keeps more than one block pair
+// outside the accumulator registers.
 #include "bd_common.h"
 
 namespace bd {
@@ -56,15 +57,15 @@ constexpr int kPGroup = 4;   // head pairs per group of the block order
 __device__ inline int lds_off(int row, int c) { return row * kPStr + ((c ^ ((row >> 1) & 7)) << 3); }
 
 // Rotation (ROT) of the lane's accumulators and their bf16 rows into the
-// wave's transpose buffer tw: [128 tokens][128 features], 16-byte chunk c of
+// wave's transpose buffer tw: [32 NB tokens][128 features], 16-byte chunk c of
 // token row t at chunk c ^ (t & 15), the 8-byte halves swapped for rows with
 // bit 4 set, so the 32 lanes of one write (rows 0..31) spread over all 64
 // banks.  Lane (hh, ln) holds features mb*32 + g*8 + hh*4 + e (r = 4g + e)
 // of token nb*32 + ln; dimension j and its partner j + 64 are blocks mb and
-// mb + 2 of the same register.  STEP: the angles of tokens nb = 1..3 advance
-// the angle of nb = 0 by the rotation of 32 positions.
-template <bool ROT, bool STEP>
-__device__ __forceinline__ void rope_to_lds(f32x16 (&acc)[4][4], bf16 *tw, const double (&pos)[4],
+// mb + 2 of the same register.  STEP: the angle of each token nb > 0
+// advances that of token nb - 1 by the rotation of 32 positions.
+template <bool ROT, bool STEP, int NB>
+__device__ __forceinline__ void rope_to_lds(f32x16 (&acc)[NB][4], bf16 *tw, const double (&pos)[NB],
                                             const ProduceArgs &a, int hh, int ln) {
   constexpr double kRev = 0.15915494309189533577;   // 1 / (2 pi)
 #pragma unroll
@@ -81,7 +82,7 @@ __device__ __forceinline__ void rope_to_lds(f32x16 (&acc)[4][4], bf16 *tw, const
       }
     }
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
+    for (int nb = 0; nb < NB; ++nb) {
       float lo[16], hi[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) { lo[r] = acc[nb][mb][r]; hi[r] = acc[nb][mb + 2][r]; }
@@ -117,7 +118,7 @@ __device__ __forceinline__ void rope_to_lds(f32x16 (&acc)[4][4], bf16 *tw, const
   }
 }
 
-__global__ __launch_bounds__(256, 1) void produce_kernel(ProduceArgs a, int n_pairs, int n_tb, int xcd_order) {
+__global__ __launch_bounds__(512, 1) void produce_kernel(ProduceArgs a, int n_pairs, int n_tb, int xcd_order) {
   // block -> (head pair, token tile): with xcd_order, XCD x (= blockIdx % 8)
   // runs the contiguous eighth x of the tiles; tiles run in groups of
   // kPGroup head pairs, token tiles outer, so concurrent blocks share operands
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(256, 1) void produce_kernel(ProduceArgs a, int n_pa
   const int nheads = a.Hq + 2 * a.Hkv;
   const int t0 = tb * kPTok;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hsel = wave >> 1, tq = wave & 1;   // head of the pair, token half
+  const int hsel = wave >> 2, tq = wave & 3;   // head of the pair, token quarter
   const int head = min(2 * pair + hsel, nheads - 1);
   const bool head_ok = 2 * pair + hsel < nheads;
   const int hh = lane >> 5, ln = lane & 31;
@@ -143,7 +144,7 @@ __global__ __launch_bounds__(256, 1) void produce_kernel(ProduceArgs a, int n_pa
   __shared__ __attribute__((aligned(16))) bf16 X0[kPTok * kPStr];
   __shared__ __attribute__((aligned(16))) bf16 X1[kPTok * kPStr];
 
-  // staging: thread tid holds chunk kc of rows srow + 32u (u < 8) of both the
+  // staging: thread tid holds chunk kc of rows srow + 64u (u < 4) of both the
   // W tile (the pair's 256 feature rows; a missing second head re-reads the
   // last head, its results are not stored) and the X tile (tokens past the
   // end re-read the last token, their results are not stored)
@@ -152,71 +153,71 @@ __global__ __launch_bounds__(256, 1) void produce_kernel(ProduceArgs a, int n_pa
 #pragma unroll
   for (int h = 0; h < 2; ++h)
     wrow[h] = a.w + ((int64_t)min(2 * pair + h, nheads - 1) * kPD + srow) * a.Dm + kq;
-  const bf16 *xr[8];
+  const bf16 *xr[4];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int T = min(t0 + srow + 32 * u, n_tok - 1);
+  for (int u = 0; u < 4; ++u) {
+    const int T = min(t0 + srow + 64 * u, n_tok - 1);
     const int b = T / a.q, i = T - b * a.q;
     xr[u] = a.x + (int64_t)b * a.xs[0] + (int64_t)i * a.xs[1] + kq;
   }
-  bf16x8 rg[16];   // units 0..7: W rows srow + 32u; 8..15: X rows srow + 32(u - 8)
+  bf16x8 rg[8];   // units 0..3: W rows srow + 64u; 4..7: X rows srow + 64(u - 4)
   const int nit = a.Dm / kPBK;
   auto gload = [&](int u, int k0) {
-    if (u < 8) rg[u] = *reinterpret_cast<const bf16x8 *>(wrow[u >> 2] + (int64_t)(32 * (u & 3)) * a.Dm + k0);
-    else rg[u] = *reinterpret_cast<const bf16x8 *>(xr[u - 8] + k0);
+    if (u < 4) rg[u] = *reinterpret_cast<const bf16x8 *>(wrow[u >> 1] + (int64_t)(64 * (u & 1)) * a.Dm + k0);
+    else rg[u] = *reinterpret_cast<const bf16x8 *>(xr[u - 4] + k0);
   };
   auto lstore = [&](bf16 *Wn, bf16 *Xn, int u) {
-    if (u < 8) *reinterpret_cast<bf16x8 *>(&Wn[lds_off(srow + 32 * u, kc)]) = rg[u];
-    else *reinterpret_cast<bf16x8 *>(&Xn[lds_off(srow + 32 * (u - 8), kc)]) = rg[u];
+    if (u < 4) *reinterpret_cast<bf16x8 *>(&Wn[lds_off(srow + 64 * u, kc)]) = rg[u];
+    else *reinterpret_cast<bf16x8 *>(&Xn[lds_off(srow + 64 * (u - 4), kc)]) = rg[u];
   };
 
   // acc[nb][mb]: token block nb (32 tokens) x feature block mb (32 features)
-  f32x16 acc[4][4];
+  f32x16 acc[2][4];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
+  for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = f32x16{};
   auto frag = [&](const bf16 *Wb, const bf16 *Xb, int ks, bf16x8 *xf, bf16x8 *wf) {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-      xf[nb] = *reinterpret_cast<const bf16x8 *>(&Xb[lds_off(tq * 128 + nb * 32 + ln, ks * 2 + hh)]);
+    for (int nb = 0; nb < 2; ++nb)
+      xf[nb] = *reinterpret_cast<const bf16x8 *>(&Xb[lds_off(tq * 64 + nb * 32 + ln, ks * 2 + hh)]);
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
       wf[mb] = *reinterpret_cast<const bf16x8 *>(&Wb[lds_off(hsel * kPD + mb * 32 + ln, ks * 2 + hh)]);
   };
   // One tile from (Wb, Xb); the registers' tile goes to (Wn, Xn) and the tile
-  // at hidden offset k0 is loaded.  Steps 0-2 (16 elements each): 16 MFMAs,
-  // the next step's 8 fragment reads, and the 16 staging writes and global
-  // loads spread 6 / 5 / 5.  The block barrier then comes before step 3: the
+  // at hidden offset k0 is loaded.  Steps 0-2 (16 elements each): 8 MFMAs,
+  // the next step's 6 fragment reads, and the 8 staging writes and global
+  // loads spread 3 / 3 / 2.  The block barrier then comes before step 3: the
   // tile's last fragments are already in registers and (Wn, Xn) is complete,
   // so the next tile's first fragments are read while step 3's MFMAs run.
   // After the last tile that read is not used; the epilogue's LDS writes
-  // (each wave into its own 32 KB) may overlap it, which changes nothing a
+  // (each wave into its own 16 KB) may overlap it, which changes nothing a
   // wave keeps.
-  bf16x8 xf[2][4], wf[2][4];
-  auto mfma16 = [&](int b) {
+  bf16x8 xf[2][2], wf[2][4];
+  auto mfma8 = [&](int b) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+      for (int nb = 0; nb < 2; ++nb)
         acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[b][mb], xf[b][nb], acc[nb][mb], 0, 0, 0);
   };
   auto step = [&](const bf16 *Wb, const bf16 *Xb, bf16 *Wn, bf16 *Xn, int k0) {
 #pragma unroll
     for (int ks = 0; ks < 3; ++ks) {
       frag(Wb, Xb, ks + 1, xf[(ks + 1) & 1], wf[(ks + 1) & 1]);
-      const int u0 = ks == 0 ? 0 : 1 + 5 * ks, nl = ks == 0 ? 6 : 5;
+      const int u0 = ks * 3, nl = ks < 2 ? 3 : 2;
 #pragma unroll
       for (int j = 0; j < nl; ++j) {
         lstore(Wn, Xn, u0 + j);
         gload(u0 + j, k0);
       }
-      mfma16(ks & 1);
+      mfma8(ks & 1);
       // masks: 0x008 MFMA, 0x020 global load, 0x100 LDS read, 0x200 LDS write
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int i = 0; i < 8; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (i < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         if (i < nl) {
           __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
@@ -229,21 +230,21 @@ __global__ __launch_bounds__(256, 1) void produce_kernel(ProduceArgs a, int n_pa
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
     frag(Wn, Xn, 0, xf[0], wf[0]);
-    mfma16(1);
+    mfma8(1);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
   // loads past the last tile are clamped to it (their data is never used),
   // so every wait count is static
 #pragma unroll
-  for (int u = 0; u < 16; ++u) gload(u, 0);
+  for (int u = 0; u < 8; ++u) gload(u, 0);
 #pragma unroll
-  for (int u = 0; u < 16; ++u) lstore(W0, X0, u);
+  for (int u = 0; u < 8; ++u) lstore(W0, X0, u);
 #pragma unroll
-  for (int u = 0; u < 16; ++u) gload(u, min(1, nit - 1) * kPBK);
+  for (int u = 0; u < 8; ++u) gload(u, min(1, nit - 1) * kPBK);
   __syncthreads();
   frag(W0, X0, 0, xf[0], wf[0]);
   int it = 0;
@@ -254,23 +255,24 @@ __global__ __launch_bounds__(256, 1) void produce_kernel(ProduceArgs a, int n_pa
   if (it < nit) step(W0, X0, W1, X1, (nit - 1) * kPBK);   // odd tile count
 
   // ---- epilogue: lane holds features mb*32 + g*8 + hh*4 + e (r = 4g + e) of
-  // token nb*32 + ln of its half
+  // token nb*32 + ln of its quarter
   if (!head_ok) return;
   const int kind = head < a.Hq ? 0 : (head < a.Hq + a.Hkv ? 1 : 2);   // q, k, v
-  bf16 *const tw = wave == 0 ? W0 : (wave == 1 ? W1 : (wave == 2 ? X0 : X1));
-  double pos[4];
+  bf16 *const tb2 = (wave >> 1) == 0 ? W0 : ((wave >> 1) == 1 ? W1 : ((wave >> 1) == 2 ? X0 : X1));
+  bf16 *const tw = tb2 + (wave & 1) * (64 * kPD);
+  double pos[2];
   bool step_ok = true;
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int T = min(t0 + tq * 128 + nb * 32 + ln, n_tok - 1);
+  for (int nb = 0; nb < 2; ++nb) {
+    const int T = min(t0 + tq * 64 + nb * 32 + ln, n_tok - 1);
     const int b = T / a.q, i = T - b * a.q;
     pos[nb] = (double)a.rope_pos[b] + (double)i;
     step_ok = step_ok && pos[nb] == pos[0] + 32.0 * nb;
   }
   // the three variants are chosen per wave (uniform branches)
-  if (kind == 2) rope_to_lds<false, false>(acc, tw, pos, a, hh, ln);
-  else if (__all(step_ok)) rope_to_lds<true, true>(acc, tw, pos, a, hh, ln);
-  else rope_to_lds<true, false>(acc, tw, pos, a, hh, ln);
+  if (kind == 2) rope_to_lds<false, false, 2>(acc, tw, pos, a, hh, ln);
+  else if (__all(step_ok)) rope_to_lds<true, true, 2>(acc, tw, pos, a, hh, ln);
+  else rope_to_lds<true, false, 2>(acc, tw, pos, a, hh, ln);
   // the wave reads what its other lanes wrote: LDS completes a wave's
   // accesses in order; the fences keep the compiler from reordering them
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -281,11 +283,11 @@ __global__ __launch_bounds__(256, 1) void produce_kernel(ProduceArgs a, int n_pa
   const int hk = kind == 1 ? head - a.Hq : head - a.Hq - a.Hkv;
   bf16 *const cache = kind == 1 ? a.kc : a.vc;
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
+  for (int j = 0; j < 16; ++j) {
     const int row = j * 4 + (lane >> 4);   // bit 4 of row is bit 2 of j
     bf16x8 v = *reinterpret_cast<const bf16x8 *>(&tw[row * kPD + ((c16 ^ (row & 15)) << 3)]);
     if (j & 4) v = __builtin_shufflevector(v, v, 4, 5, 6, 7, 0, 1, 2, 3);
-    const int T = t0 + tq * 128 + row;
+    const int T = t0 + tq * 64 + row;
     if (T >= n_tok) continue;
     // b = T / q from a float estimate (T < 2^24, checked on the host) and
     // one correction each way
@@ -301,7 +303,8 @@ __global__ __launch_bounds__(256, 1) void produce_kernel(ProduceArgs a, int n_pa
       if (p < 0 || p >= a.c_cap) continue;   // outside the cache: not written
       dst = cache + (int64_t)b * a.cs[0] + (int64_t)p * a.cs[1] + (int64_t)hk * a.cs[2];
     }
-    *reinterpret_cast<bf16x8 *>(dst + c16 * 8) = v;
+    typedef int i32x4v __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(__builtin_bit_cast(i32x4v, v), reinterpret_cast<i32x4v *>(dst + c16 * 8));
   }
 }
 
@@ -315,7 +318,7 @@ hipError_t launch_produce(const ProduceArgs &args, hipStream_t s) {
   }
   const int n_pairs = (int)cdiv(a.Hq + 2 * a.Hkv, 2), n_tb = (int)cdiv((int64_t)a.B * a.q, kPTok);
   const int total = n_pairs * n_tb;
-  hipLaunchKernelGGL(produce_kernel, dim3((unsigned)total), dim3(256), 0, s, a, n_pairs, n_tb,
+  hipLaunchKernelGGL(produce_kernel, dim3((unsigned)total), dim3(512), 0, s, a, n_pairs, n_tb,
                      total % 8 == 0 ? 1 : 0);
   return hipGetLastError();
 }
