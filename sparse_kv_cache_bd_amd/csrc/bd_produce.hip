@@ -131,7 +131,7 @@ __global__ __launch_bounds__(512, 1) void produce_kernel(ProduceArgs a, int n_pa
 
   const int nheads = a.Hq + 2 * a.Hkv;
   const int t0 = tb * kPTok;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hsel = wave >> 2, tq = wave & 3;   // head of the pair, token quarter
   const int head = min(2 * pair + hsel, nheads - 1);
   const bool head_ok = 2 * pair + hsel < nheads;
@@ -247,16 +247,19 @@ __global__ __launch_bounds__(512, 1) void produce_kernel(ProduceArgs a, int n_pa
   for (int u = 0; u < 8; ++u) gload(u, min(1, nit - 1) * kPBK);
   __syncthreads();
   frag(W0, X0, 0, xf[0], wf[0]);
-  int it = 0;
-  for (; it + 1 < nit; it += 2) {
+  for (int it = 0; it < nit; it += 2) {
     step(W0, X0, W1, X1, min(it + 2, nit - 1) * kPBK);
-    step(W1, X1, W0, X0, min(it + 3, nit - 1) * kPBK);
+    if (it + 1 < nit) step(W1, X1, W0, X0, min(it + 3, nit - 1) * kPBK);   // odd tile count
   }
-  if (it < nit) step(W0, X0, W1, X1, (nit - 1) * kPBK);   // odd tile count
 
   // ---- epilogue: lane holds features mb*32 + g*8 + hh*4 + e (r = 4g + e) of
   // token nb*32 + ln of its quarter
   if (!head_ok) return;
+  // the lane's indices formed again from the execution mask (nothing
+  // derived from the thread index is kept across the loop)
+  {
+    const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int hh = lane >> 5, ln = lane & 31;
   const int kind = head < a.Hq ? 0 : (head < a.Hq + a.Hkv ? 1 : 2);   // q, k, v
   bf16 *const tb2 = (wave >> 1) == 0 ? W0 : ((wave >> 1) == 1 ? W1 : ((wave >> 1) == 2 ? X0 : X1));
   bf16 *const tw = tb2 + (wave & 1) * (64 * kPD);
@@ -305,6 +308,7 @@ __global__ __launch_bounds__(512, 1) void produce_kernel(ProduceArgs a, int n_pa
     }
     typedef int i32x4v __attribute__((ext_vector_type(4)));
     __builtin_nontemporal_store(__builtin_bit_cast(i32x4v, v), reinterpret_cast<i32x4v *>(dst + c16 * 8));
+  }
   }
 }
 
