@@ -257,9 +257,8 @@ __global__ __launch_bounds__(512, 1) void produce_kernel(ProduceArgs a, int n_pa
   if (!head_ok) return;
   // the lane's indices formed again from the execution mask (nothing
   // derived from the thread index is kept across the loop)
-  {
-    const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-    const int hh = lane >> 5, ln = lane & 31;
+  const int el = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int ehh = el >> 5, eln = el & 31;
   const int kind = head < a.Hq ? 0 : (head < a.Hq + a.Hkv ? 1 : 2);   // q, k, v
   bf16 *const tb2 = (wave >> 1) == 0 ? W0 : ((wave >> 1) == 1 ? W1 : ((wave >> 1) == 2 ? X0 : X1));
   bf16 *const tw = tb2 + (wave & 1) * (64 * kPD);
@@ -267,27 +266,27 @@ __global__ __launch_bounds__(512, 1) void produce_kernel(ProduceArgs a, int n_pa
   bool step_ok = true;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    const int T = min(t0 + tq * 64 + nb * 32 + ln, n_tok - 1);
+    const int T = min(t0 + tq * 64 + nb * 32 + eln, n_tok - 1);
     const int b = T / a.q, i = T - b * a.q;
     pos[nb] = (double)a.rope_pos[b] + (double)i;
     step_ok = step_ok && pos[nb] == pos[0] + 32.0 * nb;
   }
   // the three variants are chosen per wave (uniform branches)
-  if (kind == 2) rope_to_lds<false, false, 2>(acc, tw, pos, a, hh, ln);
-  else if (__all(step_ok)) rope_to_lds<true, true, 2>(acc, tw, pos, a, hh, ln);
-  else rope_to_lds<true, false, 2>(acc, tw, pos, a, hh, ln);
+  if (kind == 2) rope_to_lds<false, false, 2>(acc, tw, pos, a, ehh, eln);
+  else if (__all(step_ok)) rope_to_lds<true, true, 2>(acc, tw, pos, a, ehh, eln);
+  else rope_to_lds<true, false, 2>(acc, tw, pos, a, ehh, eln);
   // the wave reads what its other lanes wrote: LDS completes a wave's
   // accesses in order; the fences keep the compiler from reordering them
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const int c16 = lane & 15;
+  const int c16 = el & 15;
   const float inv_q = 1.f / (float)a.q;
   const int hk = kind == 1 ? head - a.Hq : head - a.Hq - a.Hkv;
   bf16 *const cache = kind == 1 ? a.kc : a.vc;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const int row = j * 4 + (lane >> 4);   // bit 4 of row is bit 2 of j
+    const int row = j * 4 + (el >> 4);   // bit 4 of row is bit 2 of j
     bf16x8 v = *reinterpret_cast<const bf16x8 *>(&tw[row * kPD + ((c16 ^ (row & 15)) << 3)]);
     if (j & 4) v = __builtin_shufflevector(v, v, 4, 5, 6, 7, 0, 1, 2, 3);
     const int T = t0 + tq * 64 + row;
@@ -308,7 +307,6 @@ __global__ __launch_bounds__(512, 1) void produce_kernel(ProduceArgs a, int n_pa
     }
     typedef int i32x4v __attribute__((ext_vector_type(4)));
     __builtin_nontemporal_store(__builtin_bit_cast(i32x4v, v), reinterpret_cast<i32x4v *>(dst + c16 * 8));
-  }
   }
 }
 
