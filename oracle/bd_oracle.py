@@ -46,6 +46,7 @@ __all__ = [
     "rep_query",
     "center_row",
     "selection_scores",
+    "rep_attention",
     "multi_query_scores",
     "topk_select",
     "gather",
@@ -342,6 +343,38 @@ def selection_scores(q_rep, K, s_len, sm_scale: float):
             m[b, h * G:(h + 1) * G] = mg[:, 0]
             l[b, h * G:(h + 1) * G] = lg[:, 0]
     return s_hat, m, l
+
+
+def rep_attention(q_rep, K, V, s_len, sm_scale: float):
+    """Attention output of the representative query over the full prefix,
+    HERALD Sec. IV-B4: beside the scores, the fused selection kernel keeps
+    the running output ``o_g`` of every query head with ``(m_g, l_g)``, and
+    the output goes back at once so the next layer's FFN can run.
+
+    For row ``b`` and query head ``hq = h*G + g`` (KV head ``h``):
+    ``o[b, hq] = sum_s exp(z[g, s] - m_g) / l_g * V[b, s, h]`` over
+    ``s < S_b``, with ``z``, ``m_g``, ``l_g`` as in ``selection_scores``:
+    single-query softmax attention over the prefix.  Rows with ``S_b = 0``
+    have no output (zeros).
+
+    q_rep: ``[B, Hq, d]``; K, V: ``[B, C, Hkv, d]``; s_len: ``[B]``.
+    Returns ``o [B, Hq, d]`` float64.
+    """
+    q_rep = _f64(q_rep)
+    s_len = _i64(s_len)
+    B, Hq, d = q_rep.shape
+    Hkv = K.shape[2]
+    G = Hq // Hkv
+    o = np.zeros((B, Hq, d))
+    for b in range(B):
+        S = int(s_len[b])
+        if S == 0:
+            continue
+        for h in range(Hkv):
+            qg = q_rep[b, h * G:(h + 1) * G]               # [G, d]
+            z = sm_scale * (qg @ _f64(K[b, :S, h]).T)      # [G, S]
+            o[b, h * G:(h + 1) * G], _ = _softmax_attend(z, _f64(V[b, :S, h]))
+    return o
 
 
 def multi_query_scores(Q, K, s_len, sm_scale: float):

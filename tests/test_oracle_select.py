@@ -218,3 +218,56 @@ def test_multi_query_bruteforce_and_closed_forms():
         dz = 0.8 * (qc @ (K[0, 0, h] - K[0, 1, h]))
         np.testing.assert_allclose(sh2[0, h, 0], sps.expit(dz).sum(), rtol=1e-13)
         np.testing.assert_allclose(sh2[0, h, 1], sps.expit(-dz).sum(), rtol=1e-13)
+
+
+def test_rep_attention_is_single_query_sdpa():
+    """rep_attention against torch SDPA in float64, one query per head over
+    the row's prefix; query head hq reads KV head hq // G; a row with no
+    prefix gives zeros."""
+    rs = np.random.default_rng(11)
+    B, C, Hq, Hkv, d = 3, 70, 8, 2, 16
+    G = Hq // Hkv
+    q_rep = rs.standard_normal((B, Hq, d))
+    K = rs.standard_normal((B, C, Hkv, d))
+    V = rs.standard_normal((B, C, Hkv, d))
+    s_len = np.array([70, 23, 0])
+    o = orc.rep_attention(q_rep, K, V, s_len, 0.45)
+    assert o.shape == (B, Hq, d)
+    for b in range(B):
+        S = int(s_len[b])
+        for hq in range(Hq):
+            if S == 0:
+                assert (o[b, hq] == 0).all()
+                continue
+            h = hq // G
+            qt = torch.from_numpy(q_rep[b, hq])[None, None]            # [1, 1, d]
+            kt = torch.from_numpy(K[b, :S, h])[None]
+            vt = torch.from_numpy(V[b, :S, h])[None]
+            ref = F.scaled_dot_product_attention(qt, kt, vt, scale=0.45)[0, 0].numpy()
+            np.testing.assert_allclose(o[b, hq], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_rep_attention_closed_forms():
+    """Equal keys give the mean of the value rows; one prefix row gives that
+    row; a key far more aligned with the query than the others gives its
+    value row; the group's outputs summed equal s_hat @ V (the scores are the
+    group's attention probabilities summed)."""
+    rs = np.random.default_rng(12)
+    Hq, Hkv, d, S = 4, 1, 8, 9
+    q_rep = rs.standard_normal((1, Hq, d))
+    V = rs.standard_normal((1, S, Hkv, d))
+    K = np.repeat(rs.standard_normal((1, 1, Hkv, d)), S, axis=1)
+    o = orc.rep_attention(q_rep, K, V, [S], 0.3)
+    for hq in range(Hq):
+        np.testing.assert_allclose(o[0, hq], V[0, :, 0].mean(0), rtol=1e-12, atol=1e-14)
+    o1 = orc.rep_attention(q_rep, K, V, [1], 0.3)
+    for hq in range(Hq):
+        np.testing.assert_allclose(o1[0, hq], V[0, 0, 0], rtol=1e-14)
+    K2 = rs.standard_normal((1, S, Hkv, d)) * 0.01
+    K2[0, 5, 0] = 50.0 * q_rep[0, 2]
+    o2 = orc.rep_attention(q_rep, K2, V, [S], 1.0)
+    np.testing.assert_allclose(o2[0, 2], V[0, 5, 0], rtol=1e-9, atol=1e-9)
+    K3 = rs.standard_normal((1, S, Hkv, d))
+    o3 = orc.rep_attention(q_rep, K3, V, [S], 0.8)
+    sh, _, _ = orc.selection_scores(q_rep, K3, [S], 0.8)
+    np.testing.assert_allclose(o3[0].sum(0), sh[0, 0] @ V[0, :, 0], rtol=1e-12, atol=1e-13)
