@@ -186,6 +186,41 @@ int bd_select(int dtype, int B, int Hq, int Hkv, int d, const void *q,
               void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * bd_select_attn: bd_select plus the representative query's attention
+ * output, HERALD Sec. IV-B4: beside the importance scores the fused
+ * selection kernel keeps, for every query head g, the FlashAttention running
+ * statistics (m_g, l_g) and output o_g, and the attention output goes back at
+ * once so that the layer's FFN can run.
+ *
+ * Everything bd_select computes, with the same arguments and results, plus,
+ * for every row b with S_b > 0 and k_b > 0 and query head hq = h*G + g:
+ *   o_rep[b, hq, :] = sum_{s < S_b} exp(z[g, s] - m_g) / l_g * v[b, s, h, :]
+ * (softmax attention of q_rep over the row's prefix; z, m_g, l_g as in
+ * bd_select, the same weights whose sums over g are the ranked scores).
+ * Rows with S_b == 0 or k_b == 0 get o_rep all zeros.
+ *
+ *   v         [B, k_cap, Hkv, d] bf16, strides v_strides {row, position,
+ *             head}, 16-byte aligned with 16-byte stride multiples.
+ *   o_rep     device bf16 [B, Hq, d], contiguous; required.
+ *   idx_out   may be NULL when k_max == 0 (o_rep is then all zeros).
+ *   workspace at least bd_select_attn_workspace_size(...) bytes, 256-byte
+ *             aligned (bd_select's plus fp32 output partials per 1024
+ *             prefix positions).
+ *
+ * Built for dtype BD_BF16 with d == 128 and Hq / Hkv <= 8.
+ */
+size_t bd_select_attn_workspace_size(int B, int Hq, int Hkv, int d, int s_max,
+                                     int k_max);
+int bd_select_attn(int dtype, int B, int Hq, int Hkv, int d, const void *q,
+                   const int64_t q_strides[3], int nq, int rep_mode,
+                   int rep_row, const void *k, const int64_t k_strides[3],
+                   const void *v, const int64_t v_strides[3], int k_cap,
+                   const int32_t *s_len, int s_max, const int32_t *k_sel,
+                   int k_max, float sm_scale, int32_t *idx_out,
+                   float *score_out, void *o_rep, void *workspace,
+                   size_t ws_bytes, void *stream);
+
+/*
  * bd_select_multi: exact multi-query selection, the selection phase of
  * HERALD Sec. III-C / Sec. IV-A2 before the query reduction (every block
  * query ranks the prefix, as in MAGE's full-KV selection at a block's first

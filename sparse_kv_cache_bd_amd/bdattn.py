@@ -45,6 +45,9 @@ _SIGS = {
     "bd_select_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
     "bd_select": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _i, _i, _i, _vp, _vp, _i, _vp, _i, _vp, _i,
                        ctypes.c_float, _vp, _vp, _vp, _sz, _vp]),
+    "bd_select_attn_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "bd_select_attn": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp,
+                            _i, _vp, _i, ctypes.c_float, _vp, _vp, _vp, _vp, _sz, _vp]),
     "bd_select_multi_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "bd_select_multi": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _i, _vp, _vp, _i, _vp, _i, _vp, _i,
                              ctypes.c_float, _vp, _vp, _vp, _sz, _vp]),
@@ -287,6 +290,42 @@ def select(q, k, s_len, s_max: int, k_sel, k_max: int, sm_scale: float, rep_mode
                            _ptr(k_sel), k_max, float(sm_scale), _ptr(idx_out), _ptr(score_out),
                            _ptr(ws), 0 if ws is None else ws.numel(), _stream()))
     return idx_out
+
+
+def select_attn_workspace_size(B, Hq, Hkv, d, s_max, k_max) -> int:
+    return int(lib().bd_select_attn_workspace_size(B, Hq, Hkv, d, s_max, k_max))
+
+
+def select_attn(q, k, v, s_len, s_max: int, k_sel, k_max: int, sm_scale: float,
+                rep_mode: int = BD_REP_MEAN, rep_row: int = 0, idx_out=None, score_out=None,
+                o_rep=None, ws=None):
+    """Representative-query top-k plus the representative query's attention
+    output.  q [B, nq, Hq, d]; k, v [B, C, Hkv, d].  Returns (idx [B, Hkv,
+    k_max], o_rep [B, Hq, d])."""
+    q, k, v = _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, nq, Hq, d] and k [B, C, Hkv, d]")
+    B, nq, Hq, d = q.shape
+    Hkv = k.shape[2]
+    k = _kv(k, "k", B, Hkv, d, q.dtype)
+    v = _kv(v, "v", B, Hkv, d, q.dtype, min_len=k.shape[1])
+    s_len, k_sel = _rows(s_len, "s_len", B), _rows(k_sel, "k_sel", B)
+    if idx_out is None:
+        idx_out = torch.empty((B, Hkv, k_max), dtype=torch.int32, device=q.device)
+    idx_out = _buf(idx_out, "idx_out", (B, Hkv, k_max), torch.int32)
+    score_out = _buf(score_out, "score_out", (B, Hkv, s_max), torch.float32)
+    if o_rep is None:
+        o_rep = torch.empty((B, Hq, d), dtype=q.dtype, device=q.device)
+    o_rep = _buf(o_rep, "o_rep", (B, Hq, d), q.dtype)
+    need = select_attn_workspace_size(B, Hq, Hkv, d, s_max, k_max)
+    if ws is None:
+        ws = workspace(need, q.device)
+    _check(lib().bd_select_attn(_DTYPE[q.dtype], B, Hq, Hkv, d, _ptr(q), _strides(q, 3), nq,
+                                rep_mode, rep_row, _ptr(k), _strides(k, 3), _ptr(v), _strides(v, 3),
+                                k.shape[1], _ptr(s_len), s_max, _ptr(k_sel), k_max,
+                                float(sm_scale), _ptr(idx_out), _ptr(score_out), _ptr(o_rep),
+                                _ptr(ws), 0 if ws is None else ws.numel(), _stream()))
+    return idx_out, o_rep
 
 
 def select_multi_workspace_size(B, Hq, Hkv, d, nq, s_max, k_max) -> int:

@@ -132,36 +132,44 @@ size_t bd_select_workspace_size(int B, int Hq, int Hkv, int d, int s_max, int k_
   return select_workspace(B, Hq, Hkv, d, s_max, k_max);
 }
 
-int bd_select(int dtype, int B, int Hq, int Hkv, int d, const void *q, const int64_t q_strides[3],
-              int nq, int rep_mode, int rep_row, const void *k, const int64_t k_strides[3], int k_cap,
-              const int32_t *s_len, int s_max, const int32_t *k_sel, int k_max, float sm_scale,
-              int32_t *idx_out, float *score_out, void *workspace, size_t ws_bytes, void *stream) {
+// bd_select and bd_select_attn: the same checks and launch; v / v_strides /
+// o_rep are null for bd_select.
+static int select_impl(const char *fn, int dtype, int B, int Hq, int Hkv, int d, const void *q,
+                       const int64_t q_strides[3], int nq, int rep_mode, int rep_row, const void *k,
+                       const int64_t k_strides[3], const void *v, const int64_t v_strides[3], int k_cap,
+                       const int32_t *s_len, int s_max, const int32_t *k_sel, int k_max, float sm_scale,
+                       int32_t *idx_out, float *score_out, void *o_rep, void *workspace, size_t ws_bytes,
+                       void *stream) {
   g_err[0] = 0;
-  if (dtype != BD_BF16) return fail(BD_ERR_UNSUPPORTED, "bd_select: only BD_BF16 is built");
-  if (d != 128) return fail(BD_ERR_UNSUPPORTED, "bd_select: only d == 128 is built");
+  const bool with_out = o_rep != nullptr;
+  if (dtype != BD_BF16) return fail(BD_ERR_UNSUPPORTED, "%s: only BD_BF16 is built", fn);
+  if (d != 128) return fail(BD_ERR_UNSUPPORTED, "%s: only d == 128 is built", fn);
   if (B < 0 || Hq <= 0 || Hkv <= 0 || s_max < 0 || k_max < 0 || k_cap < 0)
-    return fail(BD_ERR_INVALID_ARG, "bd_select: negative or zero size");
-  if (Hq % Hkv != 0) return fail(BD_ERR_INVALID_ARG, "bd_select: Hq %% Hkv != 0");
-  if (Hq / Hkv > 8 || Hq > 64) return fail(BD_ERR_UNSUPPORTED, "bd_select: needs Hq/Hkv <= 8 and Hq <= 64");
-  if (B == 0 || k_max == 0) return BD_OK;
-  if (!idx_out || !s_len || !k_sel) return fail(BD_ERR_INVALID_ARG, "bd_select: null pointer");
+    return fail(BD_ERR_INVALID_ARG, "%s: negative or zero size", fn);
+  if (Hq % Hkv != 0) return fail(BD_ERR_INVALID_ARG, "%s: Hq %% Hkv != 0", fn);
+  if (Hq / Hkv > 8 || Hq > 64) return fail(BD_ERR_UNSUPPORTED, "%s: needs Hq/Hkv <= 8 and Hq <= 64", fn);
+  if (B == 0 || (k_max == 0 && !with_out)) return BD_OK;
+  if ((k_max > 0 && !idx_out) || !s_len || !k_sel) return fail(BD_ERR_INVALID_ARG, "%s: null pointer", fn);
   if (s_max > 0 && (!q || !k || !q_strides || !k_strides))
-    return fail(BD_ERR_INVALID_ARG, "bd_select: null pointer");
+    return fail(BD_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (with_out && s_max > 0 && (!v || !v_strides)) return fail(BD_ERR_INVALID_ARG, "%s: null pointer", fn);
   if (rep_mode != BD_REP_MEAN && rep_mode != BD_REP_ROW)
-    return fail(BD_ERR_INVALID_ARG, "bd_select: unknown rep_mode %d", rep_mode);
-  if (nq <= 0) return fail(BD_ERR_INVALID_ARG, "bd_select: nq must be positive");
+    return fail(BD_ERR_INVALID_ARG, "%s: unknown rep_mode %d", fn, rep_mode);
+  if (nq <= 0) return fail(BD_ERR_INVALID_ARG, "%s: nq must be positive", fn);
   if (rep_mode == BD_REP_ROW && (rep_row < 0 || rep_row >= nq))
-    return fail(BD_ERR_INVALID_ARG, "bd_select: rep_row %d outside [0, %d)", rep_row, nq);
-  if (!(sm_scale > 0.f) || sm_scale > 1e30f) return fail(BD_ERR_INVALID_ARG, "bd_select: bad sm_scale");
+    return fail(BD_ERR_INVALID_ARG, "%s: rep_row %d outside [0, %d)", fn, rep_row, nq);
+  if (!(sm_scale > 0.f) || sm_scale > 1e30f) return fail(BD_ERR_INVALID_ARG, "%s: bad sm_scale", fn);
   if ((int64_t)B * Hkv > 65535 || (int64_t)B * Hq > 65535 || B > 65535)
-    return fail(BD_ERR_INVALID_ARG, "bd_select: too many rows for one launch");
+    return fail(BD_ERR_INVALID_ARG, "%s: too many rows for one launch", fn);
   if (s_max > 0 && (!strides_ok(q_strides, 3, 2) || !strides_ok(k_strides, 3, 2) || !aligned16(q) || !aligned16(k)))
-    return fail(BD_ERR_INVALID_ARG, "bd_select: q/k must be 16-byte aligned with 16-byte stride multiples");
-  const size_t need = select_workspace(B, Hq, Hkv, d, s_max, k_max);
+    return fail(BD_ERR_INVALID_ARG, "%s: q/k must be 16-byte aligned with 16-byte stride multiples", fn);
+  if (with_out && s_max > 0 && (!strides_ok(v_strides, 3, 2) || !aligned16(v)))
+    return fail(BD_ERR_INVALID_ARG, "%s: v must be 16-byte aligned with 16-byte stride multiples", fn);
+  const size_t need = select_workspace(B, Hq, Hkv, d, s_max, k_max, with_out);
   if (!workspace || ws_bytes < need)
-    return fail(BD_ERR_WORKSPACE, "bd_select: workspace %zu bytes, need %zu", ws_bytes, need);
+    return fail(BD_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
   if (((uintptr_t)workspace & 255u) != 0)
-    return fail(BD_ERR_WORKSPACE, "bd_select: workspace must be 256-byte aligned");
+    return fail(BD_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
   SelectArgs a;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.d = d; a.nq = nq; a.rep_mode = rep_mode;
   a.rep_row = rep_row; a.k_cap = k_cap; a.s_max = s_max; a.k_max = k_max;
@@ -169,7 +177,40 @@ int bd_select(int dtype, int B, int Hq, int Hkv, int d, const void *q, const int
   for (int i = 0; i < 3; ++i) { a.qs[i] = q_strides ? q_strides[i] : 0; a.ks[i] = k_strides ? k_strides[i] : 0; }
   a.s_len = s_len; a.k_sel = k_sel; a.scale2 = sm_scale * kLog2e;
   a.idx_out = idx_out; a.score_out = score_out; a.ws = (char *)workspace;
-  return hip_status(launch_select(a, (hipStream_t)stream), "bd_select launch");
+  a.v = (const bf16 *)v;
+  for (int i = 0; i < 3; ++i) a.vs[i] = v_strides ? v_strides[i] : 0;
+  a.o_rep = (bf16 *)o_rep;
+  char what[64];
+  snprintf(what, sizeof(what), "%s launch", fn);
+  return hip_status(launch_select(a, (hipStream_t)stream), what);
+}
+
+int bd_select(int dtype, int B, int Hq, int Hkv, int d, const void *q, const int64_t q_strides[3],
+              int nq, int rep_mode, int rep_row, const void *k, const int64_t k_strides[3], int k_cap,
+              const int32_t *s_len, int s_max, const int32_t *k_sel, int k_max, float sm_scale,
+              int32_t *idx_out, float *score_out, void *workspace, size_t ws_bytes, void *stream) {
+  return select_impl("bd_select", dtype, B, Hq, Hkv, d, q, q_strides, nq, rep_mode, rep_row, k, k_strides,
+                     nullptr, nullptr, k_cap, s_len, s_max, k_sel, k_max, sm_scale, idx_out, score_out,
+                     nullptr, workspace, ws_bytes, stream);
+}
+
+size_t bd_select_attn_workspace_size(int B, int Hq, int Hkv, int d, int s_max, int k_max) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || s_max < 0 || k_max < 0 || Hq % Hkv != 0) return 0;
+  return select_workspace(B, Hq, Hkv, d, s_max, k_max, true);
+}
+
+int bd_select_attn(int dtype, int B, int Hq, int Hkv, int d, const void *q, const int64_t q_strides[3],
+                   int nq, int rep_mode, int rep_row, const void *k, const int64_t k_strides[3],
+                   const void *v, const int64_t v_strides[3], int k_cap, const int32_t *s_len, int s_max,
+                   const int32_t *k_sel, int k_max, float sm_scale, int32_t *idx_out, float *score_out,
+                   void *o_rep, void *workspace, size_t ws_bytes, void *stream) {
+  if (B > 0 && !o_rep) {
+    g_err[0] = 0;
+    return fail(BD_ERR_INVALID_ARG, "bd_select_attn: null pointer (o_rep)");
+  }
+  return select_impl("bd_select_attn", dtype, B, Hq, Hkv, d, q, q_strides, nq, rep_mode, rep_row, k,
+                     k_strides, v, v_strides, k_cap, s_len, s_max, k_sel, k_max, sm_scale, idx_out,
+                     score_out, o_rep, workspace, ws_bytes, stream);
 }
 
 size_t bd_select_multi_workspace_size(int B, int Hq, int Hkv, int d, int nq, int s_max, int k_max) {

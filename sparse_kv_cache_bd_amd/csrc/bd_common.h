@@ -180,8 +180,12 @@ struct SelectArgs {
   int32_t *idx_out;
   float *score_out;
   char *ws;
+  // representative query's attention output (bd_select_attn); null in bd_select
+  const bf16 *v;
+  int64_t vs[3];
+  bf16 *o_rep;
 };
-size_t select_workspace(int B, int Hq, int Hkv, int d, int s_max, int k_max);
+size_t select_workspace(int B, int Hq, int Hkv, int d, int s_max, int k_max, bool with_out = false);
 hipError_t launch_select(const SelectArgs &a, hipStream_t s);
 // Exact multi-query selection: nq * G <= 128 columns per KV head.
 size_t select_multi_workspace(int B, int Hkv, int s_max);

@@ -19,6 +19,10 @@
 //          are exactly the values that get ranked.  (No cross-block merge
 //          inside the scan: that needs device-scope fences, which write back
 //          and invalidate the L2 of the XCD on every block.)
+//   out    (bd_select_attn only) the representative query's attention
+//          output, o[g] = sum_s exp2(z[g, s] - m_g) / l_g * V[s]: a pass
+//          over V after the score pass with the same weights, fp32 partials
+//          per 1024-token chunk, summed in chunk order by a merge kernel.
 //   topk   exact radix select of the k-th largest score on its fp32 bit
 //          pattern (non-negative floats order like their bit patterns;
 //          digits of 11, 11 and 10 bits; the first digit's histogram is
@@ -51,18 +55,20 @@ constexpr int kRankU = 8;          // keys per thread per histogram round
 constexpr int kLdsKeys = 32768;    // longest score row ranked by one block from LDS
 constexpr int kCK = 4096;          // scores per block of the multi-block ranking path
 constexpr int kZStr = kTS + 16;    // LDS row stride of the scan's z staging (floats)
+constexpr int kOTok = 1024;        // tokens per block of the output pass
 
 struct SelLayout {
-  size_t qhi, qlo, z, part, scores, hist, ccount, total;
-  int nch_scan, nch_topk;
+  size_t qhi, qlo, z, part, scores, hist, ccount, opart, total;
+  int nch_scan, nch_topk, nch_o;
   bool multi;  // rows longer than kLdsKeys: multi-block ranking
   int zs;  // row stride of z (s_max rounded up to 4: 16-byte aligned rows)
 };
 
-SelLayout sel_layout(int B, int Hq, int Hkv, int d, int s_max) {
+SelLayout sel_layout(int B, int Hq, int Hkv, int d, int s_max, bool with_out = false) {
   SelLayout L;
   L.nch_scan = (int)cdiv(s_max > 0 ? s_max : 1, kTS);
   L.nch_topk = (int)cdiv(s_max > 0 ? s_max : 1, kCK);
+  L.nch_o = (int)cdiv(s_max > 0 ? s_max : 1, kOTok);
   L.multi = s_max > kLdsKeys;
   L.zs = (int)cdiv(s_max, 4) * 4;
   const size_t P = (size_t)B * Hkv;
@@ -75,6 +81,7 @@ SelLayout sel_layout(int B, int Hq, int Hkv, int d, int s_max) {
   L.scores = take(P * (size_t)s_max * 4);
   L.hist = take(P * 3 * kBins * 4);
   L.ccount = L.multi ? take(P * L.nch_topk * 2 * 4) : 0;
+  L.opart = with_out ? take(P * L.nch_o * (size_t)(Hq / Hkv) * d * 4) : 0;
   L.total = off;
   return L;
 }
@@ -83,7 +90,8 @@ struct SelPtrs {
   bf16 *qhi, *qlo;
   float *z, *part, *scores;
   uint32_t *hist, *ccount;   // digit histograms (digit 0 for every row); per-chunk counts
-  int nch_scan, zs, nch_topk;
+  float *opart;              // output pass: fp32 partials [row][KV head][chunk][G][d]
+  int nch_scan, zs, nch_topk, nch_o;
   bool multi;
 };
 
@@ -350,6 +358,37 @@ __global__ __launch_bounds__(kThreads, 2) void sel_scan_kernel(SelectArgs a, Sel
 
 }
 
+// (max, 1 / sum) of each query head of KV head h's group: merge of the
+// scan's chunk partials, wave g for head g, chunks cc = lane, lane + 64, ...,
+// then a fixed butterfly (the same result in every block that asks).
+// Visible to the block after a barrier.
+__device__ inline void group_stats(const SelectArgs &a, const SelPtrs &w, int b, int h, int S,
+                                   float *st_m, float *st_il) {
+  const int wv = threadIdx.x >> 6, ln = threadIdx.x & 63;
+  const int nch = (int)cdiv(S, kTS);
+  for (int g = wv; g < a.G; g += kThreads / 64) {
+    const float *pp = w.part + ((int64_t)b * a.Hq + h * a.G + g) * w.nch_scan * 2;
+    float M = -INFINITY, L = 0.f;
+    for (int c0 = ln; c0 < nch; c0 += 64 * 8) {  // 8 loads in flight, merged in order
+      float2 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int cc = c0 + 64 * u;
+        v[u] = cc < nch ? *reinterpret_cast<const float2 *>(pp + cc * 2) : float2{-INFINITY, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (c0 + 64 * u < nch) merge_ml(M, L, v[u].x, v[u].y);
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) merge_ml(M, L, __shfl_xor(M, o), __shfl_xor(L, o));
+    if (ln == 0) {
+      st_m[g] = M;
+      st_il[g] = 1.f / L;
+    }
+  }
+}
+
 // ------------------------------------------------------------------ score
 // Block = (chunk of kScoreTok tokens, KV head, row); 4 consecutive tokens per
 // thread.
@@ -360,35 +399,8 @@ __global__ __launch_bounds__(kThreads) void sel_score_kernel(SelectArgs a, SelPt
   if (S == 0 || kb == 0) return;
   constexpr int per = kScoreTok / kThreads;
   if (c * kScoreTok >= S) return;
-  // (max, sum) of each query head of the group: merge of the scan's chunk
-  // partials, wave g for head g, chunks cc = lane, lane + 64, ..., then a
-  // fixed butterfly (the same result in every block)
   __shared__ float st_m[8], st_il[8];
-  {
-    const int wv = threadIdx.x >> 6, ln = threadIdx.x & 63;
-    const int nch = (int)cdiv(S, kTS);
-    for (int g = wv; g < a.G; g += kThreads / 64) {
-      const float *pp = w.part + ((int64_t)b * a.Hq + h * a.G + g) * w.nch_scan * 2;
-      float M = -INFINITY, L = 0.f;
-      for (int c0 = ln; c0 < nch; c0 += 64 * 8) {  // 8 loads in flight, merged in order
-        float2 v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int cc = c0 + 64 * u;
-          v[u] = cc < nch ? *reinterpret_cast<const float2 *>(pp + cc * 2) : float2{-INFINITY, 0.f};
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (c0 + 64 * u < nch) merge_ml(M, L, v[u].x, v[u].y);
-      }
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) merge_ml(M, L, __shfl_xor(M, o), __shfl_xor(L, o));
-      if (ln == 0) {
-        st_m[g] = M;
-        st_il[g] = 1.f / L;
-      }
-    }
-  }
+  group_stats(a, w, b, h, S, st_m, st_il);
   __shared__ uint32_t hist[kBins];
   for (int e = threadIdx.x; e < kBins; e += kThreads) hist[e] = 0;
   __syncthreads();
@@ -436,6 +448,117 @@ __global__ __launch_bounds__(kThreads) void sel_score_kernel(SelectArgs a, SelPt
     for (int e = threadIdx.x; e < kBins; e += kThreads)
       if (hist[e]) atomicAdd(&gh[e], hist[e]);
   }
+}
+
+// ----------------------------------------------------------------- output
+// HERALD Sec. IV-B4 keeps, beside the scores, the running output o_g of the
+// representative query for every query head and hands it back at once (the
+// next layer's FFN waits for it).  Here: o[g] = sum_s p[g, s] V[s, h] with
+// p[g, s] = exp2(z[g, s] - m_g) / l_g, the weights the scores sum.  Block =
+// (chunk of kOTok tokens, KV head, row) in rounds of 256 tokens: the round's
+// weights go to LDS (thread t forms token t's), then thread (token group tg,
+// dims 8 dc .. 8 dc + 7) reads 16 value rows (16 lanes read one 256-byte
+// row) and accumulates G x 8 sums; the 16 token groups are added by two
+// lane exchanges and a fixed-order sum over the 4 waves.
+__global__ __launch_bounds__(kThreads) void sel_out_kernel(SelectArgs a, SelPtrs w) {
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int S, kb;
+  row_sizes(a, b, S, kb);
+  if (S == 0 || kb == 0 || c * kOTok >= S) return;
+  __shared__ float st_m[8], st_il[8];
+  group_stats(a, w, b, h, S, st_m, st_il);
+  __syncthreads();
+  __shared__ float ps[8][kThreads];     // weights of the round's tokens
+  __shared__ float red[4][8][kSD];      // per-wave sums
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int dc = lane & 15;
+  const int tg = wv * 4 + (lane >> 4);  // tokens tg + 16 i of a round
+  float acc[8][8];
+#pragma unroll
+  for (int g = 0; g < 8; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+  const bf16 *vb = a.v + (int64_t)b * a.vs[0] + (int64_t)h * a.vs[2] + dc * 8;
+  const int s_end = min(S, (c + 1) * kOTok);
+  for (int s0 = c * kOTok; s0 < s_end; s0 += kThreads) {
+    {
+      const int s = s0 + t;
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        if (g < a.G) {
+          float p = 0.f;
+          if (s < s_end)
+            p = __builtin_amdgcn_exp2f(w.z[((int64_t)b * a.Hq + h * a.G + g) * w.zs + s] - st_m[g]) * st_il[g];
+          ps[g][t] = p;
+        }
+      }
+    }
+    __syncthreads();
+    bf16x8 vv[16];   // rows past the prefix read its last row (weight 0)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int s = min(s0 + tg + 16 * i, S - 1);
+      vv[i] = *reinterpret_cast<const bf16x8 *>(vb + (int64_t)s * a.vs[1]);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int j = tg + 16 * i;
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        if (g < a.G) {
+          const float p = ps[g][j];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[g][e] = __builtin_fmaf(p, (float)vv[i][e], acc[g][e]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    if (g < a.G) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float x = acc[g][e];
+        x += __shfl_xor(x, 16);
+        x += __shfl_xor(x, 32);
+        if (lane < 16) red[wv][g][dc * 8 + e] = x;
+      }
+    }
+  }
+  __syncthreads();
+  float *op = w.opart + (((int64_t)b * a.Hkv + h) * w.nch_o + c) * (a.G * kSD);
+  for (int o = t; o < a.G * kSD; o += kThreads) {
+    const int g = o / kSD, dd = o - g * kSD;
+    op[o] = ((red[0][g][dd] + red[1][g][dd]) + red[2][g][dd]) + red[3][g][dd];
+  }
+}
+
+// Block = (query head, row), one thread per dimension: the chunk partials in
+// chunk order; rows without a prefix or a budget get zeros.
+__global__ __launch_bounds__(kSD) void sel_out_merge_kernel(SelectArgs a, SelPtrs w) {
+  const int hq = blockIdx.x, b = blockIdx.y, dd = threadIdx.x;
+  int S, kb;
+  row_sizes(a, b, S, kb);
+  bf16 *o = a.o_rep + ((int64_t)b * a.Hq + hq) * kSD + dd;
+  if (S == 0 || kb == 0) {
+    *o = (bf16)0.f;
+    return;
+  }
+  const int h = hq / a.G, g = hq - h * a.G;
+  const int nch = (int)cdiv(S, kOTok);
+  const int64_t cstr = (int64_t)a.G * kSD;
+  const float *pp = w.opart + ((int64_t)b * a.Hkv + h) * w.nch_o * cstr + g * kSD + dd;
+  float acc = 0.f;
+  for (int c0 = 0; c0 < nch; c0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = c0 + u < nch ? pp[(c0 + u) * cstr] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (c0 + u < nch) acc += v[u];
+  }
+  *o = (bf16)acc;
 }
 
 // ---------------------------------------------------------------- top-k
@@ -1099,13 +1222,14 @@ hipError_t launch_rank(const SelectArgs &a, const SelPtrs &w, hipStream_t s) {
 
 }  // namespace
 
-size_t select_workspace(int B, int Hq, int Hkv, int d, int s_max, int k_max) {
+size_t select_workspace(int B, int Hq, int Hkv, int d, int s_max, int k_max, bool with_out) {
   (void)k_max;
-  return sel_layout(B, Hq, Hkv, d, s_max).total;
+  return sel_layout(B, Hq, Hkv, d, s_max, with_out).total;
 }
 
 hipError_t launch_select(const SelectArgs &a, hipStream_t s) {
-  const SelLayout L = sel_layout(a.B, a.Hq, a.Hkv, a.d, a.s_max);
+  const bool with_out = a.o_rep != nullptr;
+  const SelLayout L = sel_layout(a.B, a.Hq, a.Hkv, a.d, a.s_max, with_out);
   SelPtrs w;
   w.qhi = reinterpret_cast<bf16 *>(a.ws + L.qhi);
   w.qlo = reinterpret_cast<bf16 *>(a.ws + L.qlo);
@@ -1118,15 +1242,29 @@ hipError_t launch_select(const SelectArgs &a, hipStream_t s) {
   w.multi = L.multi;
   w.hist = reinterpret_cast<uint32_t *>(a.ws + L.hist);
   w.ccount = reinterpret_cast<uint32_t *>(a.ws + L.ccount);
+  w.opart = reinterpret_cast<float *>(a.ws + L.opart);
+  w.nch_o = L.nch_o;
   hipError_t e;
+  if (a.k_max == 0) {   // no row selects: only the output rows (zeros)
+    if (with_out) hipLaunchKernelGGL(sel_out_merge_kernel, dim3(a.Hq, a.B), dim3(kSD), 0, s, a, w);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(sel_prep_kernel, dim3(a.Hq, a.B), dim3(kThreads), 0, s, a, w);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t scan_lds = (size_t)a.Hq * (2 * kSD * sizeof(bf16) + kZStr * sizeof(float));
   hipLaunchKernelGGL(sel_scan_kernel, dim3(L.nch_scan, a.B), dim3(kThreads), scan_lds, s, a, w);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(sel_score_kernel, dim3((unsigned)cdiv(a.s_max, kScoreTok), a.Hkv, a.B),
-                     dim3(kThreads), 0, s, a, w);
+  if (a.s_max > 0)   // (no prefix anywhere: the rank pass writes the -1 rows)
+    hipLaunchKernelGGL(sel_score_kernel, dim3((unsigned)cdiv(a.s_max, kScoreTok), a.Hkv, a.B),
+                       dim3(kThreads), 0, s, a, w);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (with_out) {
+    if (a.s_max > 0)
+      hipLaunchKernelGGL(sel_out_kernel, dim3((unsigned)L.nch_o, a.Hkv, a.B), dim3(kThreads), 0, s, a, w);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(sel_out_merge_kernel, dim3(a.Hq, a.B), dim3(kSD), 0, s, a, w);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   return launch_rank(a, w, s);
 }
 

@@ -24,7 +24,7 @@ def L():
 
 def test_exports_every_header_function(L):
     names = bd.header_functions()
-    assert len(names) == 23
+    assert len(names) == 25
     for n in names:
         assert hasattr(L, n), n
 
@@ -125,6 +125,47 @@ def test_select_workspace_too_small(L):
     assert need > 0
     assert _select(L, ws_bytes=need - 1) == bd.BD_ERR_WORKSPACE
     assert "need" in bd.last_error()
+
+
+def _select_attn(L, ws_bytes=None, **kw):
+    a = dict(dtype=bd.BD_BF16, B=2, Hq=32, Hkv=8, d=128, q=FAKE, qs=I3(32 * 4096, 4096, 128),
+             nq=32, mode=bd.BD_REP_MEAN, row=0, k=FAKE2, ks=I3(1 << 22, 1024, 128), v=FAKE2,
+             vs=I3(1 << 22, 1024, 128), kcap=4000, s_len=FAKE, s_max=4000, k_sel=FAKE, k_max=200,
+             scale=0.088, idx=FAKE, score=None, o=FAKE, ws=FAKE)
+    a.update(kw)
+    need = bd.select_attn_workspace_size(a["B"], a["Hq"], a["Hkv"], a["d"], a["s_max"], a["k_max"])
+    wsb = need if ws_bytes is None else ws_bytes
+    return L.bd_select_attn(a["dtype"], a["B"], a["Hq"], a["Hkv"], a["d"], a["q"], a["qs"], a["nq"],
+                            a["mode"], a["row"], a["k"], a["ks"], a["v"], a["vs"], a["kcap"],
+                            a["s_len"], a["s_max"], a["k_sel"], a["k_max"], a["scale"], a["idx"],
+                            a["score"], a["o"], a["ws"], wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=bd.BD_F32), bd.BD_ERR_UNSUPPORTED),
+    (dict(d=64), bd.BD_ERR_UNSUPPORTED),
+    (dict(Hq=30), bd.BD_ERR_INVALID_ARG),
+    (dict(o=None), bd.BD_ERR_INVALID_ARG),
+    (dict(v=None), bd.BD_ERR_INVALID_ARG),
+    (dict(vs=None), bd.BD_ERR_INVALID_ARG),
+    (dict(v=MISALIGNED), bd.BD_ERR_INVALID_ARG),
+    (dict(vs=I3(1 << 22, 1001, 128)), bd.BD_ERR_INVALID_ARG),   # row stride not a 16-byte multiple
+    (dict(idx=None), bd.BD_ERR_INVALID_ARG),
+    (dict(ws=None), bd.BD_ERR_WORKSPACE),
+])
+def test_select_attn_validation(L, kw, code):
+    assert _select_attn(L, **kw) == code
+
+
+def test_select_attn_workspace(L):
+    """The output pass's partials come on top of bd_select's workspace: one
+    G x d fp32 block per (row, KV head, 1024 prefix positions)."""
+    base = bd.select_workspace_size(2, 32, 8, 128, 4000, 200)
+    need = bd.select_attn_workspace_size(2, 32, 8, 128, 4000, 200)
+    assert need >= base + 2 * 8 * 4 * 4 * 128 * 4
+    assert _select_attn(L, ws_bytes=need - 1) == bd.BD_ERR_WORKSPACE
+    assert _select_attn(L, ws_bytes=base) == bd.BD_ERR_WORKSPACE
+    assert _select_attn(L, B=0) == bd.BD_OK
 
 
 def _select_multi(L, ws_bytes=None, **kw):
