@@ -468,6 +468,13 @@ def bench_configs(dev, reps: int = 10):
         f_sel = lambda: bd.select(Qsel, Kc, s_len, s_max, k_sel, k_max, wl.sm_scale, idx_out=idx, ws=ws)
         f_gat = lambda: bd.gather(Kc, Vc, idx, k_sel, pool_k, pool_v)
         ms_sel = time_calls(f_sel, reps)
+        # the same selection plus the representative query's attention
+        # output over the prefix (V read once more)
+        o_rep = torch.empty((B, wl.Hq, d), dtype=Kc.dtype, device=dev)
+        ws_o = bd.workspace(bd.select_attn_workspace_size(B, wl.Hq, Hkv, d, s_max, k_max), dev)
+        ms_sela = time_calls(lambda: bd.select_attn(Qsel, Kc, Vc, s_len, s_max, k_sel, k_max, wl.sm_scale,
+                                                    idx_out=idx, o_rep=o_rep, ws=ws_o), reps)
+        del ws_o
         ms_gat = time_calls(f_gat, reps)
         ms_selc, q_selc = cold(f_sel)
         ms_gatc, q_gatc = cold(f_gat)
@@ -519,6 +526,10 @@ def bench_configs(dev, reps: int = 10):
                      "select_frac_hbm": round(sel_bytes / (ms_sel * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                      "select_cold_us": q_selc, "select_cold_GB/s": _rate(sel_bytes, ms_selc, 1e9),
                      "select_cold_frac_hbm": round(sel_bytes / (ms_selc * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "select_attn": {"us": round(ms_sela * 1e3, 2),
+                                     "GB/s": _rate(sel_bytes + sum(int(wl.s_len[b]) for b in range(B))
+                                                   * kv_bytes(wl), ms_sela, 1e9),
+                                     "output_pass_us": round((ms_sela - ms_sel) * 1e3, 2)},
                      "gather_us": round(ms_gat * 1e3, 2), "gather_GB/s": _rate(gat_bytes, ms_gat, 1e9),
                      "gather_cold_us": q_gatc, "gather_cold_GB/s": _rate(gat_bytes, ms_gatc, 1e9),
                      "attn_us_per_step": round(ms_att * 1e3 / wl.T, 2),

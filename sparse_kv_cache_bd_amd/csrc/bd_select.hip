@@ -534,15 +534,17 @@ __global__ __launch_bounds__(kThreads) void sel_out_kernel(SelectArgs a, SelPtrs
   }
 }
 
-// Block = (query head, row), one thread per dimension: the chunk partials in
-// chunk order; rows without a prefix or a budget get zeros.
-__global__ __launch_bounds__(kSD) void sel_out_merge_kernel(SelectArgs a, SelPtrs w) {
-  const int hq = blockIdx.x, b = blockIdx.y, dd = threadIdx.x;
+// Block = (query head, row), 4 threads per dimension: thread (j, dd) adds
+// the partials of chunks j, j + 4, ... in order, then the four sums are
+// added in a fixed order; rows without a prefix or a budget get zeros.
+__global__ __launch_bounds__(4 * kSD) void sel_out_merge_kernel(SelectArgs a, SelPtrs w) {
+  const int hq = blockIdx.x, b = blockIdx.y;
+  const int dd = threadIdx.x & (kSD - 1), j = threadIdx.x / kSD;
   int S, kb;
   row_sizes(a, b, S, kb);
   bf16 *o = a.o_rep + ((int64_t)b * a.Hq + hq) * kSD + dd;
   if (S == 0 || kb == 0) {
-    *o = (bf16)0.f;
+    if (j == 0) *o = (bf16)0.f;
     return;
   }
   const int h = hq / a.G, g = hq - h * a.G;
@@ -550,15 +552,18 @@ __global__ __launch_bounds__(kSD) void sel_out_merge_kernel(SelectArgs a, SelPtr
   const int64_t cstr = (int64_t)a.G * kSD;
   const float *pp = w.opart + ((int64_t)b * a.Hkv + h) * w.nch_o * cstr + g * kSD + dd;
   float acc = 0.f;
-  for (int c0 = 0; c0 < nch; c0 += 8) {
+  for (int c0 = j; c0 < nch; c0 += 4 * 8) {
     float v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = c0 + u < nch ? pp[(c0 + u) * cstr] : 0.f;
+    for (int u = 0; u < 8; ++u) v[u] = c0 + 4 * u < nch ? pp[(c0 + 4 * u) * cstr] : 0.f;
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      if (c0 + u < nch) acc += v[u];
+      if (c0 + 4 * u < nch) acc += v[u];
   }
-  *o = (bf16)acc;
+  __shared__ float part[4][kSD];
+  part[j][dd] = acc;
+  __syncthreads();
+  if (j == 0) *o = (bf16)(((part[0][dd] + part[1][dd]) + part[2][dd]) + part[3][dd]);
 }
 
 // ---------------------------------------------------------------- top-k
@@ -1246,7 +1251,7 @@ hipError_t launch_select(const SelectArgs &a, hipStream_t s) {
   w.nch_o = L.nch_o;
   hipError_t e;
   if (a.k_max == 0) {   // no row selects: only the output rows (zeros)
-    if (with_out) hipLaunchKernelGGL(sel_out_merge_kernel, dim3(a.Hq, a.B), dim3(kSD), 0, s, a, w);
+    if (with_out) hipLaunchKernelGGL(sel_out_merge_kernel, dim3(a.Hq, a.B), dim3(4 * kSD), 0, s, a, w);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(sel_prep_kernel, dim3(a.Hq, a.B), dim3(kThreads), 0, s, a, w);
@@ -1262,7 +1267,7 @@ hipError_t launch_select(const SelectArgs &a, hipStream_t s) {
     if (a.s_max > 0)
       hipLaunchKernelGGL(sel_out_kernel, dim3((unsigned)L.nch_o, a.Hkv, a.B), dim3(kThreads), 0, s, a, w);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(sel_out_merge_kernel, dim3(a.Hq, a.B), dim3(kSD), 0, s, a, w);
+    hipLaunchKernelGGL(sel_out_merge_kernel, dim3(a.Hq, a.B), dim3(4 * kSD), 0, s, a, w);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return launch_rank(a, w, s);
