@@ -469,7 +469,8 @@ int bd_attn_block_table(int dtype, int B, int Hq, int Hkv, int d, int q, int bl,
  *   q_out     [B, q, Hq, d] bf16, strides q_strides.
  *   k_cache, v_cache   [B, c_cap, Hkv, d] bf16, shared strides c_strides.
  *
- * Built for dtype BD_BF16 with d == 128 and Dm a multiple of 64.
+ * Built for dtype BD_BF16 with d == 128 and Dm a multiple of 64; W and the
+ * span of x each under 2 GiB (BD_ERR_UNSUPPORTED otherwise).
  */
 int bd_qkv_rope_write(int dtype, int B, int q, int Dm, int Hq, int Hkv, int d,
                       const void *x, const int64_t x_strides[2], const void *w,

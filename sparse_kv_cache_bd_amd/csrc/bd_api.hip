@@ -530,6 +530,11 @@ int bd_qkv_rope_write(int dtype, int B, int q, int Dm, int Hq, int Hkv, int d, c
     return fail(BD_ERR_INVALID_ARG, "bd_qkv_rope_write: strides must be >= 0 and 16-byte multiples");
   if (!aligned16(x) || !aligned16(w) || !aligned16(q_out) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(BD_ERR_INVALID_ARG, "bd_qkv_rope_write: base pointers must be 16-byte aligned");
+  // the kernel addresses W and x with 32-bit byte offsets from their bases
+  const int64_t w_bytes = (int64_t)(Hq + 2 * Hkv) * d * Dm * 2;
+  const int64_t x_bytes = ((int64_t)(B - 1) * x_strides[0] + (int64_t)(q - 1) * x_strides[1] + Dm) * 2;
+  if (w_bytes >= ((int64_t)1 << 31) || x_bytes >= ((int64_t)1 << 31))
+    return fail(BD_ERR_UNSUPPORTED, "bd_qkv_rope_write: W and x must each span less than 2 GiB");
   ProduceArgs a;
   a.B = B; a.q = q; a.Dm = Dm; a.Hq = Hq; a.Hkv = Hkv; a.c_cap = c_cap;
   a.x = (const bf16 *)x; a.xs[0] = x_strides[0]; a.xs[1] = x_strides[1];

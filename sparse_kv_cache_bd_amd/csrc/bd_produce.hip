@@ -12,11 +12,12 @@
 // back to back): wave (head h, token quarter t) owns the head's 128 features
 // x 64 tokens, 8 accumulators, so each MFMA costs three quarters of an LDS
 // fragment read.  Tiles of 64 hidden elements of W and X are double-buffered
-// in LDS (128 KB); while a tile's 32 MFMAs per wave run, the next tile goes
-// from registers to the other buffer and the tile after it is loaded into
-// the registers, the three interleaved with the MFMAs by scheduling barriers.
-// One block barrier per tile, placed before the tile's last 8 MFMAs, which
-// then hide the next tile's first fragment reads.  Blocks are
+// in LDS (128 KB) and reach it by buffer-to-LDS transfers (no staging
+// registers, no LDS store instructions): while a tile's 32 MFMAs per wave
+// run, the next tile's transfers are in flight.  One block barrier per tile,
+// placed before the tile's last 8 MFMAs: after it the next tile's first
+// fragments are read and the transfers of the tile after it are issued into
+// the buffer just released, under those 8 MFMAs.  Blocks are
 // ordered so that the 32 running on one XCD (dispatch is round-robin over
 // the 8 XCDs) share 4 head pairs and 8 token tiles, which their L2 serves.
 //
@@ -144,31 +145,41 @@ __global__ __launch_bounds__(512, 1) void produce_kernel(ProduceArgs a, int n_pa
   __shared__ __attribute__((aligned(16))) bf16 X0[kPTok * kPStr];
   __shared__ __attribute__((aligned(16))) bf16 X1[kPTok * kPStr];
 
-  // staging: thread tid holds chunk kc of rows srow + 64u (u < 4) of both the
-  // W tile (the pair's 256 feature rows; a missing second head re-reads the
-  // last head, its results are not stored) and the X tile (tokens past the
-  // end re-read the last token, their results are not stored)
-  const int srow = tid >> 3, kc = tid & 7, kq = kc * 8;
-  const bf16 *wrow[2];
+  // staging by buffer-to-LDS transfers: wave w fills the 1 KB blocks
+  // gb = 8 (w % 4) + p (p < 8) of W (waves 0-3: the pair's 256 feature rows;
+  // a missing second head re-reads the last head) or of X (waves 4-7: tokens
+  // past the end re-read the last token), rows 8 gb .. 8 gb + 7; lane l
+  // writes chunk position l % 8 of row 8 gb + l / 8 and loads into it the
+  // global chunk (l % 8) ^ ((row / 2) % 8), the swizzle of lds_off
+  const bool isx = wave >= 4;
+  int voff[8];
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
-    wrow[h] = a.w + ((int64_t)min(2 * pair + h, nheads - 1) * kPD + srow) * a.Dm + kq;
-  const bf16 *xr[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int T = min(t0 + srow + 64 * u, n_tok - 1);
-    const int b = T / a.q, i = T - b * a.q;
-    xr[u] = a.x + (int64_t)b * a.xs[0] + (int64_t)i * a.xs[1] + kq;
+  for (int p = 0; p < 8; ++p) {
+    const int gb = 8 * (wave & 3) + p, row = 8 * gb + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7);
+    if (!isx) {
+      const int hd = min(2 * pair + (row >> 7), nheads - 1);
+      voff[p] = (int)((((int64_t)hd * kPD + (row & 127)) * a.Dm + c * 8) * 2);
+    } else {
+      const int T = min(t0 + row, n_tok - 1);
+      const int b = T / a.q, i = T - b * a.q;
+      voff[p] = (int)(((int64_t)b * a.xs[0] + (int64_t)i * a.xs[1] + c * 8) * 2);
+    }
   }
-  bf16x8 rg[8];   // units 0..3: W rows srow + 64u; 4..7: X rows srow + 64(u - 4)
+  const auto rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)(isx ? a.x : a.w), (short)0, 0x7fffffff, 0x00020000);
   const int nit = a.Dm / kPBK;
-  auto gload = [&](int u, int k0) {
-    if (u < 4) rg[u] = *reinterpret_cast<const bf16x8 *>(wrow[u >> 1] + (int64_t)(64 * (u & 1)) * a.Dm + k0);
-    else rg[u] = *reinterpret_cast<const bf16x8 *>(xr[u - 4] + k0);
-  };
-  auto lstore = [&](bf16 *Wn, bf16 *Xn, int u) {
-    if (u < 4) *reinterpret_cast<bf16x8 *>(&Wn[lds_off(srow + 64 * u, kc)]) = rg[u];
-    else *reinterpret_cast<bf16x8 *>(&Xn[lds_off(srow + 64 * (u - 4), kc)]) = rg[u];
+  auto dma = [&](bf16 *Wn, bf16 *Xn, int k0) __attribute__((always_inline)) {
+    bf16 *dst = isx ? Xn : Wn;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int gb = 8 * (wave & 3) + p;
+#if defined(__HIP_DEVICE_COMPILE__)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)&dst[gb * 512], 16,
+                                               voff[p], k0 * 2, 0, 0);
+#else
+      (void)dst, (void)gb, (void)k0;   // the builtin exists in the device pass only
+#endif
+    }
   };
 
   // acc[nb][mb]: token block nb (32 tokens) x feature block mb (32 features)
@@ -185,15 +196,13 @@ __global__ __launch_bounds__(512, 1) void produce_kernel(ProduceArgs a, int n_pa
     for (int mb = 0; mb < 4; ++mb)
       wf[mb] = *reinterpret_cast<const bf16x8 *>(&Wb[lds_off(hsel * kPD + mb * 32 + ln, ks * 2 + hh)]);
   };
-  // One tile from (Wb, Xb); the registers' tile goes to (Wn, Xn) and the tile
-  // at hidden offset k0 is loaded.  Steps 0-2 (16 elements each): 8 MFMAs,
-  // the next step's 6 fragment reads, and the 8 staging writes and global
-  // loads spread 3 / 3 / 2.  The block barrier then comes before step 3: the
-  // tile's last fragments are already in registers and (Wn, Xn) is complete,
-  // so the next tile's first fragments are read while step 3's MFMAs run.
-  // After the last tile that read is not used; the epilogue's LDS writes
-  // (each wave into its own 16 KB) may overlap it, which changes nothing a
-  // wave keeps.
+  // One tile from (Wb, Xb), whose successor is already in flight into
+  // (Wn, Xn).  Steps 0-2 (16 elements each): 8 MFMAs and the next step's 6
+  // fragment reads.  The block barrier (which waits for every wave's
+  // transfers into (Wn, Xn)) then comes before step 3: the tile's last
+  // fragments are in registers, so (Wb, Xb) is free; the next tile's first
+  // fragments are read and the transfers of the tile after it into (Wb, Xb)
+  // are issued while step 3's MFMAs run.
   bf16x8 xf[2][2], wf[2][4];
   auto mfma8 = [&](int b) {
 #pragma unroll
@@ -202,54 +211,35 @@ __global__ __launch_bounds__(512, 1) void produce_kernel(ProduceArgs a, int n_pa
       for (int nb = 0; nb < 2; ++nb)
         acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[b][mb], xf[b][nb], acc[nb][mb], 0, 0, 0);
   };
-  auto step = [&](const bf16 *Wb, const bf16 *Xb, bf16 *Wn, bf16 *Xn, int k0) {
+  auto step = [&](bf16 *Wb, bf16 *Xb, const bf16 *Wn, const bf16 *Xn, int t_refill) {
 #pragma unroll
     for (int ks = 0; ks < 3; ++ks) {
       frag(Wb, Xb, ks + 1, xf[(ks + 1) & 1], wf[(ks + 1) & 1]);
-      const int u0 = ks * 3, nl = ks < 2 ? 3 : 2;
-#pragma unroll
-      for (int j = 0; j < nl; ++j) {
-        lstore(Wn, Xn, u0 + j);
-        gload(u0 + j, k0);
-      }
       mfma8(ks & 1);
-      // masks: 0x008 MFMA, 0x020 global load, 0x100 LDS read, 0x200 LDS write
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        if (i < nl) {
-          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        }
       }
     }
-    // nothing moves across the barrier (the compiler would otherwise hoist
-    // step 3's MFMAs above it)
+    // this wave's transfers into (Wn, Xn) have landed (the transfers count
+    // on the vector memory counter), then every wave's
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
     frag(Wn, Xn, 0, xf[0], wf[0]);
+    if (t_refill < nit) dma(Wb, Xb, t_refill * kPBK);
     mfma8(1);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
   };
-  // loads past the last tile are clamped to it (their data is never used),
-  // so every wait count is static
-#pragma unroll
-  for (int u = 0; u < 8; ++u) gload(u, 0);
-#pragma unroll
-  for (int u = 0; u < 8; ++u) lstore(W0, X0, u);
-#pragma unroll
-  for (int u = 0; u < 8; ++u) gload(u, min(1, nit - 1) * kPBK);
+  dma(W0, X0, 0);
+  if (nit > 1) dma(W1, X1, kPBK);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   frag(W0, X0, 0, xf[0], wf[0]);
   for (int it = 0; it < nit; it += 2) {
-    step(W0, X0, W1, X1, min(it + 2, nit - 1) * kPBK);
-    if (it + 1 < nit) step(W1, X1, W0, X0, min(it + 3, nit - 1) * kPBK);   // odd tile count
+    step(W0, X0, W1, X1, it + 2);
+    if (it + 1 < nit) step(W1, X1, W0, X0, it + 3);   // odd tile count
   }
 
   // ---- epilogue: lane holds features mb*32 + g*8 + hh*4 + e (r = 4g + e) of

@@ -460,6 +460,8 @@ def _produce(L, **kw):
     (dict(cs=I3(1 << 20, 250, 128)), bd.BD_ERR_INVALID_ARG),   # row stride not 16 B
     (dict(B=0), bd.BD_OK),
     (dict(q=0, x=None), bd.BD_OK),
+    (dict(Hq=4096, Hkv=2048, Dm=1024), bd.BD_ERR_UNSUPPORTED),              # W spans 2 GiB
+    (dict(xs=(ctypes.c_int64 * 2)(1 << 30, 256)), bd.BD_ERR_UNSUPPORTED),  # x spans over 2 GiB
 ])
 def test_producer_validation(L, kw, code):
     assert _produce(L, **kw) == code

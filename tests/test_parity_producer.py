@@ -64,6 +64,8 @@ def _run(bd, X, W, rope_pos, dst_pos, Hq, Hkv, C, base=10000.0):
     (5, 64, 128, 16, 2, [5, 9, 33, 70000, 1]),  # G = 8
     (3, 40, 128, 1, 1, [2, 50, 7]),             # three heads: an odd head count
     (2, 128, 256, 4, 2, [1000003, 2500000]),   # stepped rotation at positions past 1e6
+    (2, 96, 64, 4, 2, [5, 77]),                 # one hidden tile (no loop iteration after the first)
+    (1, 64, 192, 2, 1, [0]),                    # three hidden tiles, one token quarter per wave row
 ])
 def test_producer_small(bd, B, q, Dm, Hq, Hkv, rope_pos):
     note(f"producer B={B} q={q} Dm={Dm} Hq={Hq} Hkv={Hkv}")
