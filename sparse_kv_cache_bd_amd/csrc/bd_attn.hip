@@ -490,13 +490,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
   // only waits for its own prefetches, at the LDS stores and the barrier
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  // the K transfers into a buffer complete before the barrier that ends the
-  // tile (the barrier's fence waits for this wave's transfers), so the next
-  // tile reads them after every wave's have landed
+  // the K / V transfers into a buffer complete before the barrier that ends
+  // the tile (an explicit wait on the vector memory counter, which counts
+  // them: the barrier's own fence covers only what the compiler tracks), so
+  // the next tile reads them after every wave's have landed
   auto step = [&](int tt, int buf, const bf16 *Kb, const bf16 *Vb, bf16 *Kn, bf16 *Vn)
       __attribute__((always_inline)) {
     if (tt + 1 < n_tiles) load(tt + 1, Kn, Vn);
     tile(tt, buf, Kb, Vb);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
   for (int tt = 0; tt < n_tiles; tt += 2) {
