@@ -131,3 +131,34 @@ def test_select_attn_configs(bd, name):
                  wl.sm_scale)
     ref = orc.rep_attention(orc.rep_query(wl.Qsel, "mean"), wl.Kc, wl.Vc, wl.s_len, wl.sm_scale)
     _check_out(o_rep, ref, [int(x) for x in wl.s_len], [int(x) for x in wl.k_sel], name)
+
+
+def test_select_attn_graph_replay(bd):
+    """Captured in a HIP graph and replayed three times, with eager calls on
+    other inputs in between: indices and outputs equal the eager call's (the
+    workspace's histograms are cleared by a kernel, not a memset)."""
+    note("select_attn graph replay")
+    S_list, k_list = [3000, 1200], [150, 60]
+    Q, K, V = (t.cuda() for t in _case(21, 2, S_list, 32, 8, peaky=True))
+    Q2, K2, V2 = (t.cuda() for t in _case(22, 2, S_list, 32, 8))
+    sl = torch.tensor(S_list, dtype=torch.int32).cuda()
+    ks = torch.tensor(k_list, dtype=torch.int32).cuda()
+    idx = torch.empty((2, 8, 150), dtype=torch.int32, device="cuda")
+    o_rep = torch.empty((2, 32, 128), dtype=torch.bfloat16, device="cuda")
+    ws = bd.workspace(bd.select_attn_workspace_size(2, 32, 8, 128, 3000, 150), "cuda")
+
+    def call():
+        bd.select_attn(Q, K, V, sl, 3000, ks, 150, 0.088, idx_out=idx, o_rep=o_rep, ws=ws)
+    call()
+    torch.cuda.synchronize()
+    want_idx, want_o = idx.clone(), o_rep.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(3):
+        bd.select_attn(Q2, K2, V2, sl, 3000, ks, 150, 0.088, idx_out=idx, o_rep=o_rep, ws=ws)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, want_idx), f"replay {rep}: indices"
+        assert torch.equal(o_rep, want_o), f"replay {rep}: o_rep"
