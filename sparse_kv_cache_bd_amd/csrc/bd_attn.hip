@@ -556,13 +556,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
 
 // Merge the split-KV partials: one thread per (column, 4 dims), chunks in a
 // fixed order, so the result does not depend on scheduling.  A block takes
-// CPB = 32 columns (one column group, 1024 threads): 32 consecutive threads
-// take its 32 columns of the same 4 dims, which in the partials'
-// [dims / 4][column][4] order are 256 contiguous bytes.  (Blocks of 8
-// columns, four times as many, measured 4.6 % slower on the packed
-// wavefronts: the launch is short and block dispatch counts.)
+// CPB columns (32: one column group, 1024 threads; 8 for the long chunk
+// lists): CPB consecutive threads take its CPB columns of the same 4 dims,
+// which in the partials' [dims / 4][column][4] order are 8 CPB contiguous
+// bytes.  (Blocks of 8 columns for the short lists, four times as many,
+// measured 4.6 % slower on the packed wavefronts: the launch is short and
+// block dispatch counts.)
 // U: partials requested per round of loads (8, or 32 for long chunk lists).
-template <int NW, int G, int U, bool BT, int CPB = 32>
+template <int NW, int G, int U, bool BT, int CPB>
 __global__ __launch_bounds__(CPB * kD / 4) void attn_combine_kernel(AttnArgs a) {
   using S = Shape<NW, G>;
   const int blocks_per_unit = S::NCOL / CPB;
@@ -1037,18 +1038,20 @@ static hipError_t launch_mfma(const AttnArgs &a, hipStream_t s) {
     hipLaunchKernelGGL((attn_mfma_kernel<NW, G, false, false>), dim3((unsigned)grid), dim3(S::NT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split <= 1) return e;
-  const int64_t cgrid = n_groups * a.nqt * (S::NCOL / 32);
-  // one round of loads covers up to 8 chunks; longer lists (pools of
-  // thousands of keys) take 32 per round, fewer dependent round trips
+  // one round of loads covers up to 8 chunks, in blocks of 32 columns; longer
+  // lists (pools of thousands of keys) take 32 per round, fewer dependent
+  // round trips, in blocks of 8 columns (their 32 partials in flight per
+  // thread need more registers than a 1024-thread block leaves)
+  const int64_t cgrid8 = n_groups * a.nqt * (S::NCOL / 8), cgrid32 = n_groups * a.nqt * (S::NCOL / 32);
   if (bt) {
     if (a.n_split > 8)
-      hipLaunchKernelGGL((attn_combine_kernel<NW, G, 32, true>), dim3((unsigned)cgrid), dim3(32 * kD / 4), 0, s, a);
+      hipLaunchKernelGGL((attn_combine_kernel<NW, G, 32, true, 8>), dim3((unsigned)cgrid8), dim3(8 * kD / 4), 0, s, a);
     else
-      hipLaunchKernelGGL((attn_combine_kernel<NW, G, 8, true>), dim3((unsigned)cgrid), dim3(32 * kD / 4), 0, s, a);
+      hipLaunchKernelGGL((attn_combine_kernel<NW, G, 8, true, 32>), dim3((unsigned)cgrid32), dim3(32 * kD / 4), 0, s, a);
   } else if (a.n_split > 8) {
-    hipLaunchKernelGGL((attn_combine_kernel<NW, G, 32, false>), dim3((unsigned)cgrid), dim3(32 * kD / 4), 0, s, a);
+    hipLaunchKernelGGL((attn_combine_kernel<NW, G, 32, false, 8>), dim3((unsigned)cgrid8), dim3(8 * kD / 4), 0, s, a);
   } else {
-    hipLaunchKernelGGL((attn_combine_kernel<NW, G, 8, false>), dim3((unsigned)cgrid), dim3(32 * kD / 4), 0, s, a);
+    hipLaunchKernelGGL((attn_combine_kernel<NW, G, 8, false, 32>), dim3((unsigned)cgrid32), dim3(32 * kD / 4), 0, s, a);
   }
   return hipGetLastError();
 }
