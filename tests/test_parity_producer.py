@@ -117,3 +117,31 @@ def test_producer_serving_mix_shape(bd):
         _check(Qo[b:b + 1], Q, f"q row {b}")
         _check(Kc[b:b + 1, t:].cpu(), K, f"k row {b}")
         _check(Vc[b:b + 1, t:].cpu(), V, f"v row {b}")
+
+
+def test_producer_strided_hidden_states(bd):
+    """Hidden states as a view into a larger buffer (row and token strides
+    that are not q * Dm and Dm): the tile transfers address x through its
+    strides, tokens of a ragged last tile re-read the last token."""
+    note("producer strided x")
+    B, q, Dm, Hq, Hkv = 3, 72, 192, 4, 2
+    rs = np.random.default_rng(31)
+    big = torch.from_numpy(rs.standard_normal((B, q + 9, Dm + 64)).astype(np.float32)).bfloat16()
+    X = big[:, 5:5 + q, 32:32 + Dm]                     # strides (81 * 256, 256, 1)
+    _, W = _case(32, B, q, Dm, Hq, Hkv)
+    rope_pos = [4, 1900, 70001]
+    dst = [0, 13, 40]
+    C = q + 64
+    Kc = torch.full((B, C, Hkv, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    Vc = torch.full((B, C, Hkv, 128), -7.0, dtype=torch.bfloat16, device="cuda")
+    Qo = torch.empty((B, q, Hq, 128), dtype=torch.bfloat16, device="cuda")
+    i32 = lambda v: torch.tensor(v, dtype=torch.int32).cuda()
+    Xg = big.cuda()[:, 5:5 + q, 32:32 + Dm]
+    assert not Xg.is_contiguous()
+    bd.qkv_rope_write(Xg, W.cuda(), i32(rope_pos), Hq, Hkv, Qo, Kc, Vc, i32(dst))
+    torch.cuda.synchronize()
+    Q, K, V = orc.qkv_rope(X.contiguous(), W, rope_pos, Hq, Hkv)
+    _check(Qo, Q, "q (strided x)")
+    for b in range(B):
+        _check(Kc.cpu()[b:b + 1, dst[b]:dst[b] + q], K[b:b + 1], f"k row {b} (strided x)")
+        _check(Vc.cpu()[b:b + 1, dst[b]:dst[b] + q], V[b:b + 1], f"v row {b} (strided x)")
